@@ -1,0 +1,692 @@
+// Host pack scheduler: prefix tree -> packs -> split items -> schedule blob.
+//
+// Follows the pack stage of the PAT review ("pack-forward-merge paradigm",
+// pack scheduler workflow of Fig 7, key implementation details of the pack
+// scheduler): queries sharing a prefix are grouped into one work item so each
+// shared KV block is fetched once; a profit model that weighs prefix length
+// against query count decides which shared nodes are packed; packing scheme 1
+// splits leaves off their parent's item, scheme 2 folds a specific leaf into
+// it; long KV ranges are split so unequal lengths leave no bubbles; each item
+// gets a kernel variant chosen by its row count (multi-tile kernel, runtime
+// tile selector).  Nothing here calls HIP, so plans can be built and checked
+// on a host without a GPU.
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "kvattn_plan.hpp"
+
+namespace kvattn {
+
+static thread_local std::string g_last_error;
+
+kvattn_status set_error(kvattn_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+void clear_error() { g_last_error.clear(); }
+
+namespace {
+
+struct Node {
+    int parent = -1;
+    int pos_begin = 0, pos_end = 0;     // logical block positions
+    int64_t tokens = 0;
+    std::vector<int> queries;           // ascending
+    std::vector<int> children;
+    bool packed = false;
+    int fold_child = -1;                // scheme 2: leaf folded into this node's item
+};
+
+struct Batch {
+    int B, mb;
+    const int32_t* bt;
+    const int32_t* sl;
+    std::vector<int> nb;                // blocks per query
+    int valid(int b, int j) const {
+        int n = nb[b];
+        return j < n - 1 ? kBlock : sl[b] - kBlock * (n - 1);
+    }
+    uint64_t key(int b, int j) const {
+        return (uint64_t(uint32_t(bt[size_t(b) * mb + j])) << 5) | uint64_t(valid(b, j));
+    }
+    int32_t id(int b, int j) const { return bt[size_t(b) * mb + j]; }
+};
+
+// Maximal tree: a node is a maximal run of positions over which one fixed set
+// of queries holds the same (physical block, token count) keys.
+void derive_tree(const Batch& bt, std::vector<Node>& nodes, std::vector<int>& leaf) {
+    std::vector<int> stack;
+    auto make_children = [&](std::vector<int>& qs, int pos, int parent) {
+        std::vector<std::pair<uint64_t, int>> kq;
+        kq.reserve(qs.size());
+        for (int q : qs) kq.emplace_back(bt.key(q, pos), q);
+        std::sort(kq.begin(), kq.end());
+        size_t i = 0;
+        std::vector<int> created;
+        while (i < kq.size()) {
+            size_t j = i;
+            while (j < kq.size() && kq[j].first == kq[i].first) ++j;
+            Node n;
+            n.parent = parent;
+            n.pos_begin = pos;
+            for (size_t t = i; t < j; ++t) n.queries.push_back(kq[t].second);
+            std::sort(n.queries.begin(), n.queries.end());
+            nodes.push_back(std::move(n));
+            created.push_back(int(nodes.size()) - 1);
+            i = j;
+        }
+        if (parent >= 0)
+            for (int c : created) nodes[parent].children.push_back(c);
+        for (auto it = created.rbegin(); it != created.rend(); ++it) stack.push_back(*it);
+    };
+    std::vector<int> all(bt.B);
+    std::iota(all.begin(), all.end(), 0);
+    make_children(all, 0, -1);
+    while (!stack.empty()) {
+        int n = stack.back();
+        stack.pop_back();
+        const std::vector<int> qs = nodes[n].queries;
+        int min_nb = bt.nb[qs[0]];
+        for (int q : qs) min_nb = std::min(min_nb, bt.nb[q]);
+        int p = nodes[n].pos_begin + 1;
+        while (p < min_nb) {
+            uint64_t k0 = bt.key(qs[0], p);
+            bool same = true;
+            for (size_t i = 1; i < qs.size() && same; ++i) same = bt.key(qs[i], p) == k0;
+            if (!same) break;
+            ++p;
+        }
+        nodes[n].pos_end = p;
+        nodes[n].tokens = int64_t(kBlock) * (p - nodes[n].pos_begin - 1) + bt.valid(qs[0], p - 1);
+        std::vector<int> rest;
+        for (int q : qs) {
+            if (bt.nb[q] == p)
+                leaf[q] = n;
+            else
+                rest.push_back(q);
+        }
+        if (!rest.empty()) make_children(rest, p, n);
+    }
+}
+
+// Check a caller-supplied tree against the block tables and adopt it.
+kvattn_status adopt_tree(const Batch& bt, const kvattn_prefix_tree& t, std::vector<Node>& nodes,
+                         std::vector<int>& leaf) {
+    const int N = t.num_nodes;
+    if (N < 1 || !t.parent || !t.block_begin || !t.block_end || !t.query_leaf)
+        return set_error(KVATTN_EINVAL, "prefix tree: num_nodes < 1 or NULL array");
+    nodes.assign(N, Node());
+    for (int n = 0; n < N; ++n) {
+        int p = t.parent[n], b0 = t.block_begin[n], b1 = t.block_end[n];
+        if (p < -1 || p >= N || p == n) return set_error(KVATTN_EINVAL, "prefix tree: bad parent of node " + std::to_string(n));
+        if (b0 < 0 || b1 <= b0 || b1 > bt.mb)
+            return set_error(KVATTN_EINVAL, "prefix tree: bad block range of node " + std::to_string(n));
+        if (p == -1 && b0 != 0) return set_error(KVATTN_EINVAL, "prefix tree: root must start at block 0");
+        if (p >= 0 && b0 != t.block_end[p])
+            return set_error(KVATTN_EINVAL, "prefix tree: node " + std::to_string(n) + " does not start where its parent ends");
+        nodes[n].parent = p;
+        nodes[n].pos_begin = b0;
+        nodes[n].pos_end = b1;
+    }
+    // depth bound rules out cycles
+    for (int n = 0; n < N; ++n) {
+        int x = n, steps = 0;
+        while (x != -1) {
+            x = nodes[x].parent;
+            if (++steps > N) return set_error(KVATTN_EINVAL, "prefix tree: cycle");
+        }
+    }
+    for (int b = 0; b < bt.B; ++b) {
+        int lf = t.query_leaf[b];
+        if (lf < 0 || lf >= N) return set_error(KVATTN_EINVAL, "prefix tree: bad leaf of query " + std::to_string(b));
+        if (nodes[lf].pos_end != bt.nb[b])
+            return set_error(KVATTN_EINVAL, "prefix tree: leaf of query " + std::to_string(b) + " does not end at its last block");
+        leaf[b] = lf;
+        for (int x = lf; x != -1; x = nodes[x].parent) nodes[x].queries.push_back(b);
+    }
+    for (int n = 0; n < N; ++n) {
+        Node& nd = nodes[n];
+        std::sort(nd.queries.begin(), nd.queries.end());
+        if (nd.parent >= 0) nodes[nd.parent].children.push_back(n);
+        if (nd.queries.empty()) continue;
+        for (int j = nd.pos_begin; j < nd.pos_end; ++j) {
+            uint64_t k0 = bt.key(nd.queries[0], j);
+            for (int q : nd.queries)
+                if (bt.key(q, j) != k0)
+                    return set_error(KVATTN_EINVAL, "prefix tree: queries of node " + std::to_string(n) +
+                                                        " differ at block position " + std::to_string(j));
+        }
+        nd.tokens = int64_t(kBlock) * (nd.pos_end - nd.pos_begin - 1) + bt.valid(nd.queries[0], nd.pos_end - 1);
+    }
+    return KVATTN_OK;
+}
+
+// A run of KV positions read by a fixed set of queries.
+struct Unit {
+    std::vector<int> queries;
+    int ref_query;              // block table row that supplies the ids
+    int pos_begin, pos_end;
+    int64_t tokens;
+    int fold_query = -1;        // scheme 2: this query also reads the leaf range below
+    int fold_pos_end = 0;
+    int64_t fold_tokens = 0;
+};
+
+struct Proto {                  // item before ordering
+    Item it;
+    double cost;
+    std::vector<Entry> entries;
+    std::vector<int32_t> blocks;
+};
+
+int next_pow2(int x) {
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+int64_t ceil16(int64_t x) { return (x + kBlock - 1) / kBlock * kBlock; }
+
+// Item size caps: a chunk plus a folded leaf stays within kMaxItemBlocks blocks.
+constexpr int64_t kFoldCapTokens = 256;
+constexpr int64_t kChunkCapTokens = int64_t(kMaxItemBlocks) * kBlock - kFoldCapTokens;
+
+}  // namespace
+
+kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, const int32_t* seq_lens,
+                         const kvattn_prefix_tree* tree, const kvattn_plan_options& o, kvattn_plan_s& P) {
+    const auto t0 = std::chrono::steady_clock::now();
+    const int B = s.num_queries, Hq = s.num_q_heads, Hkv = s.num_kv_heads, D = s.head_dim;
+    const int G = Hq / Hkv;
+    Batch bt{B, s.max_blocks_per_seq, block_tables, seq_lens, std::vector<int>(B)};
+    for (int b = 0; b < B; ++b) {
+        int T = seq_lens[b];
+        if (T < 1 || int64_t(T) > int64_t(s.max_blocks_per_seq) * kBlock)
+            return set_error(KVATTN_EINVAL, "seq_lens[" + std::to_string(b) + "] = " + std::to_string(T) +
+                                                " outside [1, max_blocks_per_seq * 16]");
+        bt.nb[b] = (T + kBlock - 1) / kBlock;
+        for (int j = 0; j < bt.nb[b]; ++j) {
+            int32_t id = bt.id(b, j);
+            if (id < 0 || id >= s.num_physical_blocks)
+                return set_error(KVATTN_EINVAL, "block_tables[" + std::to_string(b) + "][" + std::to_string(j) +
+                                                    "] = " + std::to_string(id) + " outside [0, num_physical_blocks)");
+        }
+    }
+
+    // ---- prefix tree ---------------------------------------------------------
+    std::vector<Node> nodes;
+    std::vector<int> leaf(B, -1);
+    if (tree) {
+        kvattn_status st = adopt_tree(bt, *tree, nodes, leaf);
+        if (st != KVATTN_OK) return st;
+    } else {
+        derive_tree(bt, nodes, leaf);
+    }
+
+    // ---- pack decision (profit model) -----------------------------------------
+    const int64_t bpt = int64_t(2) * Hkv * D * 2;          // K+V bytes per token, all KV heads
+    const int64_t partial_row_bytes = int64_t(D + 2) * 4;   // one (m, l, acc) triple
+    const int num_cus = o.num_cus > 0 ? o.num_cus : 256;
+    int packed_nodes = 0;
+    for (Node& n : nodes) {
+        const int64_t k = int64_t(n.queries.size());
+        if (k < 2 || o.pack_mode == KVATTN_PACK_QUERY) continue;
+        if (o.pack_mode == KVATTN_PACK_FULL) {
+            n.packed = true;
+        } else {
+            // bytes saved by reading the node once instead of k times, against the
+            // partial triples the pack adds (written by forward, read by merge) for
+            // every (query, q head) and every ~2K-token chunk of the node.
+            const double saved = double(k - 1) * double(n.tokens) * double(bpt);
+            const double chunks = 1.0 + double(n.tokens) / 2048.0;
+            const double extra = 2.0 * double(k) * Hq * double(partial_row_bytes) * chunks;
+            n.packed = saved > extra;
+        }
+        packed_nodes += n.packed;
+    }
+
+    // ---- scheme 2: fold one short singleton leaf into its packed parent ------
+    int folded = 0;
+    if (o.scheme != 1) {
+        // a folded leaf rides on the parent's last chunk; the cap keeps an item
+        // within kMaxItemBlocks together with the chunk cap below
+        const int64_t fold_max = o.scheme == 2 ? kFoldCapTokens : 128;
+        for (size_t ni = 0; ni < nodes.size(); ++ni) {
+            Node& n = nodes[ni];
+            if (!n.packed) continue;
+            int best = -1;
+            for (int c : n.children) {
+                const Node& cn = nodes[c];
+                if (cn.queries.size() != 1 || !cn.children.empty() || cn.tokens > fold_max) continue;
+                if (leaf[cn.queries[0]] != c) continue;
+                if (best < 0 || cn.tokens < nodes[best].tokens ||
+                    (cn.tokens == nodes[best].tokens && cn.queries[0] < nodes[best].queries[0]))
+                    best = c;
+            }
+            if (best >= 0) {
+                n.fold_child = best;
+                ++folded;
+            }
+        }
+    }
+
+    // ---- units: packed nodes, then each query's private runs -------------------
+    std::vector<Unit> units;
+    std::vector<char> folded_leaf(nodes.size(), 0);
+    for (size_t ni = 0; ni < nodes.size(); ++ni) {
+        const Node& n = nodes[ni];
+        if (!n.packed) continue;
+        Unit u;
+        u.queries = n.queries;
+        u.ref_query = n.queries[0];
+        u.pos_begin = n.pos_begin;
+        u.pos_end = n.pos_end;
+        u.tokens = n.tokens;
+        if (n.fold_child >= 0) {
+            const Node& c = nodes[n.fold_child];
+            u.fold_query = c.queries[0];
+            u.fold_pos_end = c.pos_end;
+            u.fold_tokens = c.tokens;
+            folded_leaf[n.fold_child] = 1;
+        }
+        units.push_back(std::move(u));
+    }
+    {
+        std::vector<int> path;
+        for (int b = 0; b < B; ++b) {
+            path.clear();
+            for (int x = leaf[b]; x != -1; x = nodes[x].parent) path.push_back(x);
+            std::reverse(path.begin(), path.end());
+            int run_begin = -1, run_end = -1;
+            auto flush = [&]() {
+                if (run_begin < 0) return;
+                Unit u;
+                u.queries = {b};
+                u.ref_query = b;
+                u.pos_begin = run_begin;
+                u.pos_end = run_end;
+                u.tokens = int64_t(kBlock) * (run_end - run_begin - 1) + bt.valid(b, run_end - 1);
+                units.push_back(std::move(u));
+                run_begin = -1;
+            };
+            for (int x : path) {
+                const Node& n = nodes[x];
+                if (n.packed || folded_leaf[x]) {
+                    flush();
+                    continue;
+                }
+                if (run_begin < 0) run_begin = n.pos_begin;
+                run_end = n.pos_end;
+            }
+            flush();
+        }
+    }
+
+    // ---- row groups, kernel variant, split length --------------------------------
+    struct Group {
+        int unit;
+        std::vector<int> queries;
+        int kind, tile, rows;
+        double w;                // cost per token relative to a bandwidth-bound token
+    };
+    std::vector<Group> groups;
+    for (size_t ui = 0; ui < units.size(); ++ui) {
+        const Unit& u = units[ui];
+        const int R = int(u.queries.size()) * G;
+        int kind;
+        if (o.force_variant == KVATTN_VARIANT_VALU) {
+            if (G > kValuMaxRows) return set_error(KVATTN_EUNSUPPORTED, "VALU forward holds at most 8 rows per KV head");
+            kind = KVATTN_VARIANT_VALU;
+        } else if (o.force_variant == KVATTN_VARIANT_MFMA) {
+            kind = KVATTN_VARIANT_MFMA;
+        } else {
+            kind = (R <= kValuMaxRows) ? KVATTN_VARIANT_VALU : KVATTN_VARIANT_MFMA;
+        }
+        const int max_rows = kind == KVATTN_VARIANT_VALU ? kValuMaxRows : kMfmaRowsPerWave * kMfmaMaxWaves;
+        const int qpg = std::max(1, max_rows / G);
+        const int n = int(u.queries.size());
+        const int ng = (n + qpg - 1) / qpg;
+        for (int gi = 0; gi < ng; ++gi) {
+            Group g;
+            g.unit = int(ui);
+            const int lo = int(int64_t(n) * gi / ng), hi = int(int64_t(n) * (gi + 1) / ng);
+            g.queries.assign(u.queries.begin() + lo, u.queries.begin() + hi);
+            g.kind = kind;
+            g.rows = int(g.queries.size()) * G;
+            if (kind == KVATTN_VARIANT_VALU) {
+                g.tile = next_pow2(g.rows);
+                g.w = 1.0;
+            } else {
+                g.tile = next_pow2((g.rows + kMfmaRowsPerWave - 1) / kMfmaRowsPerWave);
+                g.w = std::max(1.0, g.rows / 192.0);
+            }
+            groups.push_back(std::move(g));
+        }
+    }
+    double work = 0.0;
+    for (const Group& g : groups) work += double(units[g.unit].tokens) * g.w * Hkv;
+    int64_t C;
+    if (o.split_tokens > 0) {
+        C = std::min<int64_t>(ceil16(o.split_tokens), kChunkCapTokens);
+    } else {
+        C = ceil16(int64_t(std::ceil(work / (double(num_cus) * 8.0))));
+        C = std::min<int64_t>(std::max<int64_t>(C, 64), kChunkCapTokens);
+    }
+
+    // ---- items ----------------------------------------------------------------------
+    std::vector<Proto> protos;
+    for (const Group& g : groups) {
+        const Unit& u = units[g.unit];
+        int64_t chunk;
+        if (o.split_tokens > 0) {
+            chunk = C;
+        } else {
+            chunk = ceil16(std::max<int64_t>(32, int64_t(double(C) / g.w)));
+            chunk = std::min<int64_t>(chunk, g.kind == KVATTN_VARIANT_VALU ? 4096 : kChunkCapTokens);
+        }
+        const int64_t nch = (u.tokens + chunk - 1) / chunk;
+        const int64_t len = ceil16((u.tokens + nch - 1) / nch);
+        const bool has_fold = u.fold_query >= 0 &&
+                              std::find(g.queries.begin(), g.queries.end(), u.fold_query) != g.queries.end();
+        for (int64_t c = 0; c < nch; ++c) {
+            const int64_t tok0 = c * len;
+            if (tok0 >= u.tokens) break;
+            const int64_t ntok = std::min(len, u.tokens - tok0);
+            const bool last = tok0 + ntok == u.tokens;
+            Proto p;
+            p.it.kind = g.kind;
+            p.it.tile = g.tile;
+            p.it.pos_begin = u.pos_begin + int(tok0 / kBlock);
+            const int nblk = int((ntok + kBlock - 1) / kBlock);
+            for (int j = 0; j < nblk; ++j) p.blocks.push_back(bt.id(u.ref_query, p.it.pos_begin + j));
+            int64_t item_tokens = ntok;
+            for (int q : g.queries) {
+                Entry e{q, -1, int32_t(ntok), 0};
+                if (has_fold && last && q == u.fold_query) e.limit = int32_t(ntok + u.fold_tokens);
+                p.entries.push_back(e);
+            }
+            if (has_fold && last) {
+                for (int j = u.pos_end; j < u.fold_pos_end; ++j) p.blocks.push_back(bt.id(u.fold_query, j));
+                item_tokens = ntok + u.fold_tokens;
+            }
+            if ((item_tokens + kBlock - 1) / kBlock > kMaxItemBlocks)
+                return set_error(KVATTN_EINVAL, "internal: item exceeds the per-item block cap");
+            p.it.n_tokens = int32_t(item_tokens);
+            p.it.n_q = int32_t(g.queries.size());
+            p.it.n_rows = g.rows;
+            p.cost = double(item_tokens) * g.w;
+            protos.push_back(std::move(p));
+        }
+    }
+
+    // ---- order: launch group (MFMA by waves, then VALU by rows), longest first ----
+    std::vector<int> order(protos.size());
+    std::iota(order.begin(), order.end(), 0);
+    auto group_key = [&](const Proto& p) { return (p.it.kind == KVATTN_VARIANT_MFMA ? 0 : 1000) + p.it.tile; };
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+        int ka = group_key(protos[a]), kb = group_key(protos[b]);
+        if (ka != kb) return ka < kb;
+        return protos[a].cost > protos[b].cost;
+    });
+
+    // ---- destinations and merge map ----------------------------------------------------
+    std::vector<int> count(B, 0);
+    for (const Proto& p : protos)
+        for (const Entry& e : p.entries) count[e.query]++;
+    P.items.clear();
+    P.entries.clear();
+    P.block_ids.clear();
+    std::vector<std::vector<int32_t>> dests(B);
+    int32_t slots = 0;
+    for (int idx : order) {
+        Proto& p = protos[idx];
+        p.it.q_begin = int32_t(P.entries.size());
+        p.it.blk_begin = int32_t(P.block_ids.size());
+        for (Entry e : p.entries) {
+            if (count[e.query] > 1) {
+                e.dest = slots;
+                slots += Hq;
+                dests[e.query].push_back(e.dest);
+            }
+            P.entries.push_back(e);
+        }
+        P.block_ids.insert(P.block_ids.end(), p.blocks.begin(), p.blocks.end());
+        P.items.push_back(p.it);
+    }
+    P.n_slots = slots;
+    P.merge_query.clear();
+    P.merge_dest.clear();
+    P.merge_ptr.assign(1, 0);
+    int direct_rows = 0;
+    for (int b = 0; b < B; ++b) {
+        if (count[b] == 1) {
+            direct_rows += Hq;
+            continue;
+        }
+        P.merge_query.push_back(b);
+        P.merge_dest.insert(P.merge_dest.end(), dests[b].begin(), dests[b].end());
+        P.merge_ptr.push_back(int32_t(P.merge_dest.size()));
+    }
+
+    // ---- launches ---------------------------------------------------------------------------
+    P.forward_launches.clear();
+    P.merge_launches.clear();
+    for (size_t i = 0; i < P.items.size();) {
+        size_t j = i;
+        while (j < P.items.size() && P.items[j].kind == P.items[i].kind && P.items[j].tile == P.items[i].tile) ++j;
+        Launch L;
+        L.kind = P.items[i].kind == KVATTN_VARIANT_MFMA ? 1 : 0;
+        L.tile = P.items[i].tile;
+        L.item_begin = int(i);
+        L.item_count = int(j - i);
+        P.forward_launches.push_back(L);
+        i = j;
+    }
+    if (!P.merge_query.empty()) P.merge_launches.push_back(Launch{2, 0, 0, int(P.merge_query.size())});
+
+    // ---- blob ------------------------------------------------------------------------------------
+    BlobHeader& h = P.header;
+    std::memset(&h, 0, sizeof(h));
+    h.magic = kBlobMagic;
+    h.version = kBlobVersion;
+    h.n_items = int32_t(P.items.size());
+    h.n_entries = int32_t(P.entries.size());
+    h.n_block_ids = int32_t(P.block_ids.size());
+    h.n_merge_q = int32_t(P.merge_query.size());
+    h.n_slots = slots;
+    h.head_dim = D;
+    uint64_t off = align256(sizeof(BlobHeader));
+    h.off_items = off;        off = align256(off + P.items.size() * sizeof(Item));
+    h.off_entries = off;      off = align256(off + P.entries.size() * sizeof(Entry));
+    h.off_block_ids = off;    off = align256(off + P.block_ids.size() * 4);
+    h.off_merge_query = off;  off = align256(off + P.merge_query.size() * 4);
+    h.off_merge_ptr = off;    off = align256(off + P.merge_ptr.size() * 4);
+    h.off_merge_dest = off;   off = align256(off + P.merge_dest.size() * 4);
+    h.off_zero = off;         off = align256(off + 256);
+    h.blob_bytes = off;
+    h.off_part_ml = off;      off = align256(off + uint64_t(slots) * 8);
+    h.off_part_acc = off;     off = align256(off + uint64_t(slots) * D * 4);
+    h.total_bytes = off;
+    P.blob.assign(h.blob_bytes, 0);
+    std::memcpy(P.blob.data(), &h, sizeof(h));
+    auto put = [&](uint64_t at, const void* src, size_t n) {
+        if (n) std::memcpy(P.blob.data() + at, src, n);
+    };
+    put(h.off_items, P.items.data(), P.items.size() * sizeof(Item));
+    put(h.off_entries, P.entries.data(), P.entries.size() * sizeof(Entry));
+    put(h.off_block_ids, P.block_ids.data(), P.block_ids.size() * 4);
+    put(h.off_merge_query, P.merge_query.data(), P.merge_query.size() * 4);
+    put(h.off_merge_ptr, P.merge_ptr.data(), P.merge_ptr.size() * 4);
+    put(h.off_merge_dest, P.merge_dest.data(), P.merge_dest.size() * 4);
+
+    // ---- statistics ------------------------------------------------------------------------------
+    kvattn_stats& st = P.stats;
+    std::memset(&st, 0, sizeof(st));
+    {
+        std::vector<int32_t> maxv(size_t(s.num_physical_blocks), 0);
+        int64_t qc = 0;
+        for (int b = 0; b < B; ++b) {
+            qc += seq_lens[b];
+            for (int j = 0; j < bt.nb[b]; ++j) {
+                int32_t id = bt.id(b, j);
+                maxv[id] = std::max(maxv[id], int32_t(bt.valid(b, j)));
+            }
+        }
+        int64_t uniq = 0;
+        for (int32_t v : maxv) uniq += v;
+        st.unique_kv_bytes = uniq * bpt;
+        st.query_centric_kv_bytes = qc * bpt;
+    }
+    int64_t planned = 0;
+    for (const Item& it : P.items) {
+        planned += it.n_tokens;
+        if (it.kind == KVATTN_VARIANT_VALU)
+            st.num_items_valu++;
+        else
+            st.num_items_mfma++;
+    }
+    st.planned_kv_bytes = planned * bpt;
+    st.partial_bytes = int64_t(slots) * partial_row_bytes * 2;
+    st.num_nodes = int32_t(nodes.size());
+    st.num_packed_nodes = packed_nodes;
+    st.num_items = int32_t(P.items.size());
+    st.num_folded_leaves = folded;
+    st.num_partial_slots = slots;
+    st.num_merge_rows = int32_t(P.merge_query.size()) * Hq;
+    st.num_direct_rows = direct_rows;
+    st.num_launches = int32_t(P.forward_launches.size() + P.merge_launches.size());
+    st.split_tokens = int32_t(C);
+    st.blob_bytes = h.blob_bytes;
+    st.workspace_bytes = h.total_bytes;
+    st.plan_seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+    return KVATTN_OK;
+}
+
+}  // namespace kvattn
+
+// ============================================================================
+// C ABI: host-only entry points
+// ============================================================================
+extern "C" {
+
+void kvattn_plan_options_default(kvattn_plan_options* o) {
+    if (!o) return;
+    o->scale = 0.f;
+    o->pack_mode = KVATTN_PACK_AUTO;
+    o->scheme = 0;
+    o->force_variant = KVATTN_VARIANT_AUTO;
+    o->split_tokens = 0;
+    o->num_cus = 0;
+}
+
+kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables, const int32_t* seq_lens,
+                          const kvattn_prefix_tree* tree, const kvattn_plan_options* opts, kvattn_plan_t* out) {
+    using namespace kvattn;
+    clear_error();
+    if (!out) return set_error(KVATTN_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!shape || !block_tables || !seq_lens) return set_error(KVATTN_EINVAL, "shape, block_tables or seq_lens is NULL");
+    const kvattn_shape& s = *shape;
+    if (s.num_queries < 1 || s.num_q_heads < 1 || s.num_kv_heads < 1 || s.head_dim < 1 || s.max_blocks_per_seq < 1 ||
+        s.num_physical_blocks < 1)
+        return set_error(KVATTN_EINVAL, "shape fields must be >= 1");
+    if (s.num_q_heads % s.num_kv_heads != 0) return set_error(KVATTN_EINVAL, "num_q_heads % num_kv_heads != 0");
+    if (s.block_size != kBlock) return set_error(KVATTN_EUNSUPPORTED, "block_size must be 16");
+    if (s.head_dim != 64 && s.head_dim != 128) return set_error(KVATTN_EUNSUPPORTED, "head_dim must be 64 or 128");
+    if (s.num_q_heads / s.num_kv_heads > kMaxGroup)
+        return set_error(KVATTN_EUNSUPPORTED, "more than 64 q heads per KV head");
+    kvattn_plan_options o;
+    kvattn_plan_options_default(&o);
+    if (opts) o = *opts;
+    if (o.pack_mode < 0 || o.pack_mode > 2 || o.scheme < 0 || o.scheme > 2 || o.force_variant < -1 ||
+        o.force_variant > 1 || o.split_tokens < 0 || o.num_cus < 0 || !(o.scale >= 0.f) || std::isinf(o.scale))
+        return set_error(KVATTN_EINVAL, "bad option value");
+    kvattn_plan_s* P = new (std::nothrow) kvattn_plan_s();
+    if (!P) return set_error(KVATTN_ENOMEM, "plan allocation failed");
+    P->shape = s;
+    P->opts = o;
+    P->scale = o.scale > 0.f ? o.scale : float(1.0 / std::sqrt(double(s.head_dim)));
+    kvattn_status st;
+    try {
+        st = build_plan(s, block_tables, seq_lens, tree, o, *P);
+    } catch (const std::bad_alloc&) {
+        st = set_error(KVATTN_ENOMEM, "host allocation failed while planning");
+    }
+    if (st != KVATTN_OK) {
+        delete P;
+        return st;
+    }
+    if (std::getenv("KVATTN_LOG")) {
+        const kvattn_stats& x = P->stats;
+        std::fprintf(stderr,
+                     "kvattn_plan: nodes %d packed %d folded %d items %d (valu %d mfma %d) split %d slots %d "
+                     "merge_rows %d unique %.3f MB planned %.3f MB partial %.3f MB plan %.3f ms\n",
+                     x.num_nodes, x.num_packed_nodes, x.num_folded_leaves, x.num_items, x.num_items_valu,
+                     x.num_items_mfma, x.split_tokens, x.num_partial_slots, x.num_merge_rows,
+                     x.unique_kv_bytes / 1e6, x.planned_kv_bytes / 1e6, x.partial_bytes / 1e6, x.plan_seconds * 1e3);
+    }
+    *out = P;
+    return KVATTN_OK;
+}
+
+kvattn_status kvattn_plan_device_bytes(kvattn_plan_t plan, size_t* bytes) {
+    using namespace kvattn;
+    clear_error();
+    if (!plan || !bytes) return set_error(KVATTN_EINVAL, "plan or bytes is NULL");
+    *bytes = size_t(plan->header.total_bytes);
+    return KVATTN_OK;
+}
+
+kvattn_status kvattn_plan_stats(kvattn_plan_t plan, kvattn_stats* stats) {
+    using namespace kvattn;
+    clear_error();
+    if (!plan || !stats) return set_error(KVATTN_EINVAL, "plan or stats is NULL");
+    *stats = plan->stats;
+    return KVATTN_OK;
+}
+
+kvattn_status kvattn_plan_export(kvattn_plan_t plan, kvattn_export* out) {
+    using namespace kvattn;
+    clear_error();
+    if (!plan || !out) return set_error(KVATTN_EINVAL, "plan or out is NULL");
+    out->num_items = int32_t(plan->items.size());
+    out->items = reinterpret_cast<const kvattn_item_info*>(plan->items.data());
+    out->num_entries = int32_t(plan->entries.size());
+    out->entries = reinterpret_cast<const kvattn_item_query*>(plan->entries.data());
+    out->num_block_ids = int32_t(plan->block_ids.size());
+    out->block_ids = plan->block_ids.data();
+    out->num_merge_queries = int32_t(plan->merge_query.size());
+    out->merge_query = plan->merge_query.data();
+    out->merge_ptr = plan->merge_ptr.data();
+    out->merge_dest = plan->merge_dest.data();
+    out->num_partial_slots = plan->n_slots;
+    out->head_dim = plan->shape.head_dim;
+    return KVATTN_OK;
+}
+
+void kvattn_plan_destroy(kvattn_plan_t plan) { delete plan; }
+
+const char* kvattn_status_string(kvattn_status s) {
+    switch (s) {
+        case KVATTN_OK: return "KVATTN_OK";
+        case KVATTN_EINVAL: return "KVATTN_EINVAL";
+        case KVATTN_EUNSUPPORTED: return "KVATTN_EUNSUPPORTED";
+        case KVATTN_ENOMEM: return "KVATTN_ENOMEM";
+        case KVATTN_EWORKSPACE: return "KVATTN_EWORKSPACE";
+        case KVATTN_EHIP: return "KVATTN_EHIP";
+        case KVATTN_ESTATE: return "KVATTN_ESTATE";
+    }
+    return "KVATTN_UNKNOWN";
+}
+
+const char* kvattn_last_error(void) { return kvattn::g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,30 @@
+// Host-side plan object and error helpers (no HIP dependency).
+#pragma once
+
+#include <string>
+#include <vector>
+
+#include "kvattn_internal.h"
+
+struct kvattn_plan_s {
+    kvattn_shape shape{};
+    kvattn_plan_options opts{};
+    float scale = 0.f;                      // effective softmax scale
+    std::vector<kvattn::Item> items;
+    std::vector<kvattn::Entry> entries;
+    std::vector<int32_t> block_ids;
+    std::vector<int32_t> merge_query, merge_ptr, merge_dest;
+    int32_t n_slots = 0;
+    std::vector<kvattn::Launch> forward_launches;
+    std::vector<kvattn::Launch> merge_launches;
+    std::vector<unsigned char> blob;        // serialised schedule: header + arrays + zero region
+    kvattn::BlobHeader header{};
+    kvattn_stats stats{};
+    void* dev_ws = nullptr;                 // bound device workspace (caller-owned)
+    size_t dev_bytes = 0;
+};
+
+namespace kvattn {
+kvattn_status set_error(kvattn_status s, const std::string& msg);
+void clear_error();
+}  // namespace kvattn

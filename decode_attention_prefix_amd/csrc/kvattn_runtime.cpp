@@ -1,0 +1,131 @@
+// Device-side entry points of the C ABI: bind a workspace, launch the forward
+// and merge kernels.  The library never allocates device memory; the caller
+// provides every device buffer (the workspace included).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "kvattn_plan.hpp"
+
+namespace kvattn {
+namespace {
+
+DevPlan resolve(const kvattn_plan_s& P) {
+    auto* base = static_cast<unsigned char*>(P.dev_ws);
+    const BlobHeader& h = P.header;
+    DevPlan d;
+    d.items = reinterpret_cast<const Item*>(base + h.off_items);
+    d.entries = reinterpret_cast<const Entry*>(base + h.off_entries);
+    d.block_ids = reinterpret_cast<const int32_t*>(base + h.off_block_ids);
+    d.merge_query = reinterpret_cast<const int32_t*>(base + h.off_merge_query);
+    d.merge_ptr = reinterpret_cast<const int32_t*>(base + h.off_merge_ptr);
+    d.merge_dest = reinterpret_cast<const int32_t*>(base + h.off_merge_dest);
+    d.zero = reinterpret_cast<const uint16_t*>(base + h.off_zero);
+    d.part_ml = reinterpret_cast<float*>(base + h.off_part_ml);
+    d.part_acc = reinterpret_cast<float*>(base + h.off_part_acc);
+    return d;
+}
+
+Dims dims(const kvattn_plan_s& P) {
+    Dims d;
+    d.num_q_heads = P.shape.num_q_heads;
+    d.num_kv_heads = P.shape.num_kv_heads;
+    d.head_dim = P.shape.head_dim;
+    d.group = P.shape.num_q_heads / P.shape.num_kv_heads;
+    d.scale_log2 = float(double(P.scale) * 1.4426950408889634);
+    return d;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kvattn_status check_bound(kvattn_plan_t plan) {
+    if (!plan) return set_error(KVATTN_EINVAL, "plan is NULL");
+    if (!plan->dev_ws) return set_error(KVATTN_ESTATE, "no device workspace bound: call kvattn_plan_upload first");
+    return KVATTN_OK;
+}
+
+kvattn_status run_forward(const void* q, const void* k, const void* v, kvattn_plan_t plan, float* out,
+                          void* stream) {
+    if (!q || !k || !v || !out) return set_error(KVATTN_EINVAL, "q, k_cache, v_cache or out is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return set_error(KVATTN_EINVAL, "q, k_cache, v_cache and out must be 16-byte aligned");
+    const DevPlan dp = resolve(*plan);
+    const Dims d = dims(*plan);
+    for (const Launch& L : plan->forward_launches) {
+        int rc;
+        if (L.kind == 1)
+            rc = launch_forward_mfma(dp, d, L.tile, L.item_begin, L.item_count, static_cast<const uint16_t*>(q),
+                                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), out, stream);
+        else
+            rc = launch_forward_valu(dp, d, L.tile, L.item_begin, L.item_count, static_cast<const uint16_t*>(q),
+                                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), out, stream);
+        if (rc != 0)
+            return set_error(KVATTN_EHIP, std::string("forward launch failed: ") + hipGetErrorString(hipError_t(rc)));
+    }
+    return KVATTN_OK;
+}
+
+kvattn_status run_merge(kvattn_plan_t plan, float* out, void* stream) {
+    if (!out) return set_error(KVATTN_EINVAL, "out is NULL");
+    const DevPlan dp = resolve(*plan);
+    const Dims d = dims(*plan);
+    for (const Launch& L : plan->merge_launches) {
+        int rc = launch_merge(dp, d, L.item_begin, L.item_count, out, stream);
+        if (rc != 0)
+            return set_error(KVATTN_EHIP, std::string("merge launch failed: ") + hipGetErrorString(hipError_t(rc)));
+    }
+    return KVATTN_OK;
+}
+
+}  // namespace
+}  // namespace kvattn
+
+extern "C" {
+
+kvattn_status kvattn_plan_upload(kvattn_plan_t plan, void* dev_workspace, size_t bytes, void* stream) {
+    using namespace kvattn;
+    clear_error();
+    if (!plan || !dev_workspace) return set_error(KVATTN_EINVAL, "plan or dev_workspace is NULL");
+    if ((reinterpret_cast<uintptr_t>(dev_workspace) & 255u) != 0)
+        return set_error(KVATTN_EWORKSPACE, "dev_workspace must be 256-byte aligned");
+    if (bytes < plan->header.total_bytes)
+        return set_error(KVATTN_EWORKSPACE, "workspace holds " + std::to_string(bytes) + " bytes, plan needs " +
+                                                std::to_string(plan->header.total_bytes));
+    hipError_t e = hipMemcpyAsync(dev_workspace, plan->blob.data(), plan->blob.size(), hipMemcpyHostToDevice,
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return set_error(KVATTN_EHIP, std::string("upload copy failed: ") + hipGetErrorString(e));
+    plan->dev_ws = dev_workspace;
+    plan->dev_bytes = bytes;
+    return KVATTN_OK;
+}
+
+kvattn_status kvattn_forward(const void* q, const void* k_cache, const void* v_cache, kvattn_plan_t plan, float* out,
+                             void* stream) {
+    using namespace kvattn;
+    clear_error();
+    kvattn_status s = check_bound(plan);
+    if (s != KVATTN_OK) return s;
+    return run_forward(q, k_cache, v_cache, plan, out, stream);
+}
+
+kvattn_status kvattn_merge(kvattn_plan_t plan, float* out, void* stream) {
+    using namespace kvattn;
+    clear_error();
+    kvattn_status s = check_bound(plan);
+    if (s != KVATTN_OK) return s;
+    return run_merge(plan, out, stream);
+}
+
+kvattn_status kvattn_decode(const void* q, const void* k_cache, const void* v_cache, kvattn_plan_t plan, float* out,
+                            void* stream) {
+    using namespace kvattn;
+    clear_error();
+    kvattn_status s = check_bound(plan);
+    if (s != KVATTN_OK) return s;
+    s = run_forward(q, k_cache, v_cache, plan, out, stream);
+    if (s != KVATTN_OK) return s;
+    return run_merge(plan, out, stream);
+}
+
+}  // extern "C"

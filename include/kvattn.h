@@ -1,0 +1,258 @@
+/*
+ * kvattn -- prefix-aware paged decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * Computes, for a batch of single-token decode queries, out = softmax(q K^T / sqrt(d)) V
+ * over a paged bf16 KV cache whose blocks are shared by requests along a
+ * prefix tree (PAT review, "core formula" section: decode attention with Q a
+ * single token and K, V the accumulated cache).  Execution follows the
+ * pack-forward-merge scheme of the PAT review ("pack-forward-merge paradigm"):
+ *   pack    -- host: group the queries that share a run of KV blocks so the run
+ *              is fetched from HBM once (memory-centric prefix-aware packing,
+ *              Fig 5(d) caption; profit-model heuristic packing; tree-structure
+ *              block table, Fig 7 caption);
+ *   forward -- device: split-KV multi-tile kernels, tile variant chosen per
+ *              work item at plan time (multi-tile kernel, runtime tile
+ *              selector, long-KV splitting);
+ *   merge   -- device: combine the per-item partial (m, l, acc) triples of each
+ *              query row by the online-softmax rule (online-softmax merge).
+ *
+ * Conventions for every entry point:
+ *   - Plain C ABI; no exception crosses it.  Every call returns a kvattn_status;
+ *     on failure kvattn_last_error() gives a thread-local detail string.
+ *   - Host pointers are read during the call only, except where stated.
+ *   - Device pointers are HIP device memory owned by the caller; the library
+ *     never allocates device memory (no hipMalloc, no hipFree).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Device work is enqueued asynchronously on `stream`; faults inside a
+ *     kernel surface at the caller's next synchronisation.
+ *
+ * Layouts (all row-major, C order):
+ *   block_tables int32 [num_queries][max_blocks_per_seq]  physical block of each
+ *                logical 16-token block; entries at j >= ceil(seq_len/16) are ignored
+ *   seq_lens     int32 [num_queries]  tokens each query attends over, the current
+ *                token included (short-term-memory concept page, autoregressive
+ *                KV-cache step: K_t, V_t are appended before attending)
+ *   q            bf16  [num_queries][num_q_heads][head_dim]
+ *   k_cache, v_cache bf16 [num_physical_blocks][num_kv_heads][block_size][head_dim]
+ *                (paged cache: concept page, PagedAttention section).  Token t of
+ *                query b is slot t % 16 of block block_tables[b][t / 16].  Slots a
+ *                block does not hold are never read into the result (they may be NaN).
+ *   out          fp32  [num_queries][num_q_heads][head_dim]
+ *   GQA: query head h reads KV head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef KVATTN_H
+#define KVATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVATTN_OK = 0,
+    KVATTN_EINVAL = 1,        /* bad argument: NULL, shape, block id, length, tree     */
+    KVATTN_EUNSUPPORTED = 2,  /* valid but not built: head_dim not 64/128, block_size != 16,
+                                 more than 64 q heads per KV head                        */
+    KVATTN_ENOMEM = 3,        /* host allocation failed                                  */
+    KVATTN_EWORKSPACE = 4,    /* device workspace too small, misaligned or not bound    */
+    KVATTN_EHIP = 5,          /* a HIP runtime call (copy, launch) failed               */
+    KVATTN_ESTATE = 6         /* call order: decode before upload                       */
+} kvattn_status;
+
+typedef struct kvattn_plan_s* kvattn_plan_t; /* opaque; host memory owned by the library */
+
+typedef struct {
+    int32_t num_queries;          /* B  >= 1                                  */
+    int32_t num_q_heads;          /* Hq >= 1                                  */
+    int32_t num_kv_heads;         /* Hkv >= 1, Hq % Hkv == 0                  */
+    int32_t head_dim;             /* D: 64 or 128                            */
+    int32_t block_size;           /* tokens per KV block: 16                 */
+    int32_t max_blocks_per_seq;   /* row stride of block_tables              */
+    int32_t num_physical_blocks;  /* blocks in each of k_cache, v_cache      */
+} kvattn_shape;
+
+/*
+ * Optional explicit prefix tree (PAT review, Fig 7(b) caption: the pack
+ * scheduler works on a tree-structured block table).  Node n covers logical
+ * block positions [block_begin[n], block_end[n]) of every query whose path
+ * passes through it; a root has parent -1 and block_begin 0; a child starts
+ * where its parent ends; query b's path ends at node query_leaf[b] with
+ * block_end == ceil(seq_len[b] / 16).  All queries passing through a node must
+ * hold the same physical blocks with the same token counts over its range.
+ * kvattn_plan checks all of this and returns KVATTN_EINVAL otherwise.  Pass
+ * NULL to let the planner derive the (maximal) tree from the block tables.
+ * Arrays are read during the kvattn_plan call only.
+ */
+typedef struct {
+    int32_t num_nodes;
+    const int32_t* parent;        /* [num_nodes]                        */
+    const int32_t* block_begin;   /* [num_nodes]                        */
+    const int32_t* block_end;     /* [num_nodes]                        */
+    const int32_t* query_leaf;    /* [num_queries]                      */
+} kvattn_prefix_tree;
+
+enum { KVATTN_PACK_AUTO = 0, KVATTN_PACK_QUERY = 1, KVATTN_PACK_FULL = 2 };
+enum { KVATTN_VARIANT_AUTO = -1, KVATTN_VARIANT_VALU = 0, KVATTN_VARIANT_MFMA = 1 };
+
+/*
+ * Plan options.  kvattn_plan_options_default() fills the defaults.
+ *   scale          softmax scale; 0 selects 1/sqrt(head_dim) (core formula).
+ *   pack_mode      AUTO: pack a shared node when the profit model says the
+ *                  HBM bytes saved outweigh the partial-result traffic and lost
+ *                  parallelism (profit-model heuristic packing, which weighs
+ *                  prefix length against query count); QUERY: one query per work
+ *                  item, shared blocks re-read (query-centric packing, Fig 5(b));
+ *                  FULL: pack every node shared by >= 2 queries (memory-centric
+ *                  packing, Fig 5(d)).
+ *   scheme         0 auto, 1 = packing scheme 1 only (leaves always split off their
+ *                  parent, Fig 7(c)), 2 = also allow scheme 2 (one short leaf folded
+ *                  into its parent's item, Fig 7(d)).
+ *   force_variant  -1 auto; KVATTN_VARIANT_VALU / _MFMA force one forward kernel
+ *                  family for every item (for tests).  VALU handles at most 8 rows
+ *                  per KV head; wider packs are split into several items.
+ *   split_tokens   0 auto; otherwise the KV chunk length of split items, rounded
+ *                  up to a multiple of 16 (long-KV splitting).
+ *   num_cus        compute units the split model balances over; 0 means 256.
+ */
+typedef struct {
+    float scale;
+    int32_t pack_mode;
+    int32_t scheme;
+    int32_t force_variant;
+    int32_t split_tokens;
+    int32_t num_cus;
+} kvattn_plan_options;
+
+/* Statistics of a plan (bytes are per decode call, all KV heads). */
+typedef struct {
+    int64_t unique_kv_bytes;         /* distinct (physical block) tokens x 2 x Hkv x D x 2 B     */
+    int64_t planned_kv_bytes;        /* KV bytes the forward items read (>= unique)              */
+    int64_t query_centric_kv_bytes;  /* sum over queries of seq_len x 2 x Hkv x D x 2 B          */
+    int64_t partial_bytes;           /* partial triples written by forward and read by merge     */
+    int32_t num_nodes;               /* prefix-tree nodes                                       */
+    int32_t num_packed_nodes;        /* nodes read once for all their queries                   */
+    int32_t num_items;               /* forward work items (each runs for every KV head)        */
+    int32_t num_items_valu;
+    int32_t num_items_mfma;
+    int32_t num_folded_leaves;       /* leaves folded into a parent item (scheme 2)            */
+    int32_t num_partial_slots;       /* (query, q head) partial triples                         */
+    int32_t num_merge_rows;          /* (query, q head) rows the merge kernel combines          */
+    int32_t num_direct_rows;         /* rows written by exactly one forward item                */
+    int32_t num_launches;            /* kernel launches per kvattn_decode                       */
+    int32_t split_tokens;            /* chunk length the split model chose                      */
+    int32_t reserved;
+    double plan_seconds;             /* host wall time of kvattn_plan                            */
+    uint64_t blob_bytes;             /* schedule bytes uploaded by kvattn_plan_upload            */
+    uint64_t workspace_bytes;        /* = kvattn_plan_device_bytes                               */
+} kvattn_stats;
+
+/* One forward work item, as exported for inspection and coverage checks. */
+typedef struct {
+    int32_t kind;        /* KVATTN_VARIANT_VALU or _MFMA                                      */
+    int32_t tile;        /* VALU: rows per KV head (1,2,4,8); MFMA: waves per workgroup      */
+    int32_t pos_begin;   /* first logical block position of the item's KV range               */
+    int32_t n_tokens;    /* tokens in the item's KV range                                     */
+    int32_t q_begin;     /* first entry in entries[]                                          */
+    int32_t n_q;         /* queries in the item                                               */
+    int32_t blk_begin;   /* first entry in block_ids[]; the range has ceil(n_tokens/16) blocks */
+    int32_t n_rows;      /* n_q x (Hq / Hkv) query rows per KV head                           */
+} kvattn_item_info;
+
+typedef struct {
+    int32_t query;       /* b                                                                  */
+    int32_t dest;        /* -1: the item writes out[b] directly; else partial slot of q head h
+                            is dest + h                                                          */
+    int32_t limit;       /* query b attends to tokens [0, limit) of the item's range            */
+    int32_t pad;
+} kvattn_item_query;
+
+/* Host views of a plan's schedule; pointers stay valid until kvattn_plan_destroy. */
+typedef struct {
+    int32_t num_items;
+    const kvattn_item_info* items;
+    int32_t num_entries;
+    const kvattn_item_query* entries;
+    int32_t num_block_ids;
+    const int32_t* block_ids;
+    int32_t num_merge_queries;
+    const int32_t* merge_query;   /* [num_merge_queries] b                                 */
+    const int32_t* merge_ptr;     /* [num_merge_queries + 1] CSR offsets into merge_dest  */
+    const int32_t* merge_dest;    /* partial slot bases of the query's items              */
+    int32_t num_partial_slots;
+    int32_t head_dim;
+} kvattn_export;
+
+/* Fill *opts with the defaults (AUTO packing, scheme auto, auto variant and split). */
+void kvattn_plan_options_default(kvattn_plan_options* opts);
+
+/*
+ * Build a decode plan on the host (no HIP call; usable without a GPU).
+ * Steps: derive or check the prefix tree, decide packs with the profit model,
+ * split long KV ranges, pick a kernel variant per item, order items longest
+ * first, build the merge map, serialise the schedule.
+ *   shape, block_tables, seq_lens: required; layouts above.
+ *   tree: optional (NULL derives it); opts: optional (NULL = defaults).
+ *   *out receives a plan owned by the caller until kvattn_plan_destroy.
+ * Errors: EINVAL (NULL pointer, B/H/D <= 0, Hq % Hkv, seq_len outside
+ * [1, max_blocks*16], block id outside [0, num_physical_blocks), bad tree or
+ * option), EUNSUPPORTED (head_dim not 64/128, block_size != 16, Hq/Hkv > 64),
+ * ENOMEM.  Reentrant; plans are independent.
+ */
+kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables, const int32_t* seq_lens,
+                          const kvattn_prefix_tree* tree, const kvattn_plan_options* opts, kvattn_plan_t* out);
+
+/* Device workspace bytes the plan needs: schedule blob + partial triples (256-B aligned). */
+kvattn_status kvattn_plan_device_bytes(kvattn_plan_t plan, size_t* bytes);
+
+/*
+ * Copy the plan's schedule into the caller's device workspace (one async
+ * host-to-device copy on `stream`) and bind the workspace to the plan.
+ * dev_workspace must be 256-byte aligned and at least kvattn_plan_device_bytes.
+ * The plan's host blob is read until the copy completes: keep the plan alive
+ * until `stream` has passed this point.  Binding again replaces the binding.
+ * Errors: EINVAL (NULL), EWORKSPACE (too small / misaligned), EHIP.
+ */
+kvattn_status kvattn_plan_upload(kvattn_plan_t plan, void* dev_workspace, size_t bytes, void* stream);
+
+/*
+ * One decode-attention call: forward kernels over every planned item, then
+ * the merge kernel over rows that have several partial triples.  q, k_cache,
+ * v_cache, out: device pointers, layouts above, matching the plan's shape.
+ * The bound workspace holds the partial triples, so at most one decode per
+ * workspace may be in flight.  One plan serves any number of calls (e.g. every
+ * layer of a decode step) with different q / caches of the same shape.
+ * Errors: EINVAL (NULL), ESTATE (no workspace bound), EHIP (launch failed).
+ */
+kvattn_status kvattn_decode(const void* q, const void* k_cache, const void* v_cache, kvattn_plan_t plan,
+                            float* out, void* stream);
+
+/* The forward stage of kvattn_decode alone (PAT review, forward stage). */
+kvattn_status kvattn_forward(const void* q, const void* k_cache, const void* v_cache, kvattn_plan_t plan,
+                             float* out, void* stream);
+
+/* The merge stage of kvattn_decode alone (PAT review, merge stage); reads the
+ * partial triples the last kvattn_forward on this workspace wrote. */
+kvattn_status kvattn_merge(kvattn_plan_t plan, float* out, void* stream);
+
+/* Plan statistics (host only). */
+kvattn_status kvattn_plan_stats(kvattn_plan_t plan, kvattn_stats* stats);
+
+/* Host views of the schedule, for coverage checks and inspection. */
+kvattn_status kvattn_plan_export(kvattn_plan_t plan, kvattn_export* out);
+
+/* Free a plan (NULL is a no-op).  Does not touch the bound device workspace. */
+void kvattn_plan_destroy(kvattn_plan_t plan);
+
+/* Static name of a status code. */
+const char* kvattn_status_string(kvattn_status status);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* kvattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVATTN_H */

@@ -1,0 +1,286 @@
+"""Host planner: coverage invariant (bit-exact), byte model, determinism, validation.
+
+The coverage checker below is written from the definition, independently of
+the planner: for every query b and every token t < seq_len[b], exactly one
+(item, entry) pair covers t, and that item reads the physical block
+block_tables[b][t // 16] at the position holding t.  Every item runs for every
+KV head, so this holds per KV head too.  A query covered by one entry is
+written directly; otherwise all its entries carry disjoint partial slots and
+the merge map lists exactly those slots.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+
+K = pytest.importorskip("decode_attention_prefix_amd.kvattn")
+
+
+def check_coverage(wl_bt, seq_lens, Hq, Hkv, ex):
+    B = len(seq_lens)
+    G = Hq // Hkv
+    it, en, ids = ex["items"], ex["entries"], ex["block_ids"]
+    cover = [np.zeros(int(T), dtype=np.int32) for T in seq_lens]
+    per_query = [[] for _ in range(B)]
+    for i in range(len(it["kind"])):
+        n_tok, pb = int(it["n_tokens"][i]), int(it["pos_begin"][i])
+        q0, nq = int(it["q_begin"][i]), int(it["n_q"][i])
+        assert it["n_rows"][i] == nq * G
+        assert it["kind"][i] in (K.KVATTN_VARIANT_VALU, K.KVATTN_VARIANT_MFMA)
+        if it["kind"][i] == K.KVATTN_VARIANT_VALU:
+            assert it["n_rows"][i] <= it["tile"][i] <= 8
+        else:
+            assert it["n_rows"][i] <= 32 * it["tile"][i] and it["tile"][i] in (1, 2, 4, 8)
+        nblk = (n_tok + 15) // 16
+        assert nblk <= 512
+        blk = ids[int(it["blk_begin"][i]): int(it["blk_begin"][i]) + nblk]
+        assert blk.size == nblk
+        assert any(int(en["limit"][q0 + k]) == n_tok for k in range(nq))
+        for k in range(nq):
+            b, dest, lim = int(en["query"][q0 + k]), int(en["dest"][q0 + k]), int(en["limit"][q0 + k])
+            assert 1 <= lim <= n_tok
+            t0 = 16 * pb
+            assert t0 + lim <= seq_lens[b]
+            # a range ends on a block boundary or at the query's last token
+            assert lim % 16 == 0 or t0 + lim == seq_lens[b]
+            cover[b][t0:t0 + lim] += 1
+            nb = (lim + 15) // 16
+            assert np.array_equal(blk[:nb], wl_bt[b, pb:pb + nb]), "item reads another block than the query's"
+            per_query[b].append(dest)
+    for b in range(B):
+        assert np.all(cover[b] == 1), "query %d covered %s times" % (b, np.unique(cover[b]))
+    # destinations and merge map
+    slots_used = {}
+    mq = {int(b): i for i, b in enumerate(ex["merge_query"])}
+    for b in range(B):
+        d = per_query[b]
+        if len(d) == 1:
+            assert d[0] == -1 and b not in mq
+        else:
+            assert all(x >= 0 for x in d) and b in mq
+            i = mq[b]
+            listed = ex["merge_dest"][ex["merge_ptr"][i]:ex["merge_ptr"][i + 1]]
+            assert sorted(listed.tolist()) == sorted(d)
+            for x in d:
+                for h in range(Hq):
+                    assert (x + h) not in slots_used
+                    slots_used[x + h] = b
+    assert len(slots_used) == ex["num_partial_slots"]
+
+
+def plan_of(wl, **opts):
+    return K.kvattn_plan(wl.shape_tuple(), wl.block_tables, wl.seq_lens, options=K.make_options(**opts))
+
+
+@pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("mode", [K.KVATTN_PACK_AUTO, K.KVATTN_PACK_QUERY, K.KVATTN_PACK_FULL])
+def test_coverage_full_size_configs(c, mode):
+    wl = W.CONFIGS[c]()
+    p = plan_of(wl, pack_mode=mode)
+    check_coverage(wl.block_tables, wl.seq_lens, wl.num_q_heads, wl.num_kv_heads, K.kvattn_plan_export(p))
+    s = K.kvattn_plan_stats(p)
+    assert s["unique_kv_bytes"] == wl.unique_kv_bytes
+    assert s["query_centric_kv_bytes"] == wl.query_centric_kv_bytes
+    if mode == K.KVATTN_PACK_QUERY:
+        assert s["planned_kv_bytes"] == wl.query_centric_kv_bytes
+    elif c != 3:
+        # every physical block read by exactly one item
+        assert s["planned_kv_bytes"] == wl.unique_kv_bytes
+    else:
+        # the 1024-row root is read by four 256-row groups
+        root = 4096 * wl.bytes_per_token
+        assert s["planned_kv_bytes"] == wl.unique_kv_bytes + 3 * root
+
+
+@pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("variant", [K.KVATTN_VARIANT_VALU, K.KVATTN_VARIANT_MFMA])
+@pytest.mark.parametrize("scheme", [1, 2])
+def test_coverage_forced_variants_and_schemes(c, variant, scheme):
+    wl = W.small(c)
+    if variant == K.KVATTN_VARIANT_VALU and wl.group > 8:
+        with pytest.raises(K.KvattnError):
+            plan_of(wl, force_variant=variant)
+        return
+    for split in (0, 16, 48):
+        p = plan_of(wl, force_variant=variant, scheme=scheme, split_tokens=split)
+        check_coverage(wl.block_tables, wl.seq_lens, wl.num_q_heads, wl.num_kv_heads, K.kvattn_plan_export(p))
+        s = K.kvattn_plan_stats(p)
+        if scheme == 1:
+            assert s["num_folded_leaves"] == 0
+
+
+def test_scheme2_folds_one_leaf_per_packed_parent():
+    wl = W.config1()
+    p = plan_of(wl, pack_mode=K.KVATTN_PACK_FULL, scheme=2, split_tokens=4096)
+    s = K.kvattn_plan_stats(p)
+    assert s["num_packed_nodes"] == 1 and s["num_folded_leaves"] == 1
+    ex = K.kvattn_plan_export(p)
+    limits = ex["entries"]["limit"]
+    # the folded query attends past the shared prefix inside the packed item
+    assert limits.max() > 256 and (limits == 256).any()
+    # the folded query has one entry and is written directly
+    assert (ex["entries"]["dest"] == -1).sum() == 1
+
+
+def test_plan_is_deterministic():
+    wl = W.config3()
+    a = K.kvattn_plan_export(plan_of(wl))
+    b = K.kvattn_plan_export(plan_of(wl))
+    for key in ("block_ids", "merge_query", "merge_ptr", "merge_dest"):
+        assert np.array_equal(a[key], b[key])
+    for key in a["items"]:
+        assert np.array_equal(a["items"][key], b["items"][key])
+    for key in a["entries"]:
+        assert np.array_equal(a["entries"][key], b["entries"][key])
+
+
+def test_packing_reads_shared_prefix_once():
+    wl = W.config2()
+    s = K.kvattn_plan_stats(plan_of(wl))
+    assert s["num_packed_nodes"] == 1 and s["num_items_mfma"] > 0
+    assert s["planned_kv_bytes"] == s["unique_kv_bytes"] < s["query_centric_kv_bytes"] / 4
+
+
+def test_profit_model_skips_tiny_shared_node():
+    # two queries share one 16-token block, then go their own ways for long tails:
+    # re-reading 16 tokens costs less than an extra partial triple per query and head
+    segs = [[("p", 16), (("own", b), 3000)] for b in range(2)]
+    wl = W.from_segments("tiny_share", segs, 32, 8, 128, 1, 2)
+    s = K.kvattn_plan_stats(plan_of(wl))
+    assert s["num_packed_nodes"] == 0
+    s2 = K.kvattn_plan_stats(plan_of(wl, pack_mode=K.KVATTN_PACK_FULL))
+    assert s2["num_packed_nodes"] == 1
+
+
+def random_tree_workload(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 24))
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    n_roots = int(rng.integers(1, 4))
+    segs = []
+    for b in range(B):
+        r = int(rng.integers(0, n_roots))
+        s = [(("root", r), 16 * int(1 + (r * 7) % 5))]
+        if rng.random() < 0.6:
+            c = int(rng.integers(0, 3))
+            s.append((("child", r, c), 16 * int(1 + c)))
+        if rng.random() < 0.8:
+            s.append((("leaf", b), int(rng.integers(1, 90))))
+        segs.append(s)
+    # a query without its own leaf ends on its shared node; make sure the last
+    # segment of every query may be partial only if private
+    fixed = []
+    for s in segs:
+        fixed.append(s)
+    return W.from_segments("rand%d" % seed, fixed, G * Hkv, Hkv, D, seed, seed + 1, extra_blocks=3)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_coverage_random_trees(seed):
+    wl = random_tree_workload(seed)
+    for mode in (0, 1, 2):
+        for scheme in (0, 1, 2):
+            for split in (0, 16, 32):
+                variant = -1 if seed % 3 else K.KVATTN_VARIANT_MFMA
+                p = plan_of(wl, pack_mode=mode, scheme=scheme, split_tokens=split, force_variant=variant)
+                check_coverage(wl.block_tables, wl.seq_lens, wl.num_q_heads, wl.num_kv_heads,
+                               K.kvattn_plan_export(p))
+
+
+def tree_from_segments(wl):
+    """Explicit prefix tree built from the generator's segment keys (one node per segment key)."""
+    node_of = {}
+    parent, begin, end = [], [], []
+    leaf = []
+    for segs in wl.segments:
+        par, pos = -1, 0
+        for i, (key, n) in enumerate(segs):
+            nb = (n + 15) // 16
+            k = (key, par)
+            if k not in node_of:
+                node_of[k] = len(parent)
+                parent.append(par)
+                begin.append(pos)
+                end.append(pos + nb)
+            par = node_of[k]
+            pos += nb
+        leaf.append(par)
+    return {"parent": np.array(parent), "block_begin": np.array(begin), "block_end": np.array(end),
+            "query_leaf": np.array(leaf)}
+
+
+@pytest.mark.parametrize("c", [1, 2, 3])
+def test_explicit_tree_is_checked_and_used(c):
+    wl = W.small(c)
+    tree = tree_from_segments(wl)
+    p = K.kvattn_plan(wl.shape_tuple(), wl.block_tables, wl.seq_lens, tree=tree)
+    check_coverage(wl.block_tables, wl.seq_lens, wl.num_q_heads, wl.num_kv_heads, K.kvattn_plan_export(p))
+    derived = K.kvattn_plan_stats(plan_of(wl))
+    given = K.kvattn_plan_stats(p)
+    assert given["planned_kv_bytes"] == derived["planned_kv_bytes"]
+    bad = {k: v.copy() for k, v in tree.items()}
+    bad["block_end"][0] += 1          # root claims one block more than the queries share
+    with pytest.raises(K.KvattnError) as e:
+        K.kvattn_plan(wl.shape_tuple(), wl.block_tables, wl.seq_lens, tree=bad)
+    assert e.value.status == K.KVATTN_EINVAL
+    bad = {k: v.copy() for k, v in tree.items()}
+    bad["parent"][0] = 0
+    with pytest.raises(K.KvattnError):
+        K.kvattn_plan(wl.shape_tuple(), wl.block_tables, wl.seq_lens, tree=bad)
+
+
+def test_validation_errors():
+    wl = W.small(2)
+    shp = list(wl.shape_tuple())
+
+    def expect(status, shape=None, bt=None, sl=None, **opts):
+        with pytest.raises(K.KvattnError) as e:
+            K.kvattn_plan(tuple(shape or shp), wl.block_tables if bt is None else bt,
+                          wl.seq_lens if sl is None else sl, options=K.make_options(**opts) if opts else None)
+        assert e.value.status == status, str(e.value)
+        assert K.kvattn_last_error() != ""
+
+    sl = wl.seq_lens.copy()
+    sl[0] = 0
+    expect(K.KVATTN_EINVAL, sl=sl)
+    sl = wl.seq_lens.copy()
+    sl[1] = 16 * wl.max_blocks + 1
+    expect(K.KVATTN_EINVAL, sl=sl)
+    bt = wl.block_tables.copy()
+    bt[0, 0] = wl.num_blocks
+    expect(K.KVATTN_EINVAL, bt=bt)
+    bt = wl.block_tables.copy()
+    bt[0, 0] = -5
+    expect(K.KVATTN_EINVAL, bt=bt)
+    s = list(shp)
+    s[2] = 7
+    expect(K.KVATTN_EINVAL, shape=s)
+    s = list(shp)
+    s[3] = 96
+    expect(K.KVATTN_EUNSUPPORTED, shape=s)
+    s = list(shp)
+    s[4] = 32
+    expect(K.KVATTN_EUNSUPPORTED, shape=s)
+    expect(K.KVATTN_EINVAL, pack_mode=7)
+    expect(K.KVATTN_EINVAL, split_tokens=-1)
+    # unused block-table entries are never read, whatever they hold
+    bt = wl.block_tables.copy()
+    bt[bt < 0] = 10 ** 9
+    K.kvattn_plan(tuple(shp), bt, wl.seq_lens)
+
+
+def test_device_calls_report_state_errors_without_gpu():
+    wl = W.small(1)
+    p = plan_of(wl)
+    with pytest.raises(K.KvattnError) as e:
+        K.kvattn_decode(16, 16, 16, p, 16, stream=0)
+    assert e.value.status == K.KVATTN_ESTATE
+    with pytest.raises(K.KvattnError) as e:
+        K.kvattn_plan_upload(p, 256 * 3, 10, stream=0)
+    assert e.value.status == K.KVATTN_EWORKSPACE
+    with pytest.raises(K.KvattnError) as e:
+        K.kvattn_plan_upload(p, 257, 1 << 30, stream=0)
+    assert e.value.status == K.KVATTN_EWORKSPACE
+    assert K.kvattn_plan_device_bytes(p) >= K.kvattn_plan_stats(p)["blob_bytes"]
