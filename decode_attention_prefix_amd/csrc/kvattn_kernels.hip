@@ -1,18 +1,21 @@
 // gfx950 (MI355X) kernels of the forward and merge stages.
 //
 // Forward (PAT review, forward stage: multi-tile kernels picked per work item,
-// long KV split into chunks): each work item reads one run of paged KV blocks
-// for one KV head and attends the item's query rows over it, producing either
-// the final output row or a partial triple (m, l, acc) with m in log2 units.
-//   * fwd_valu  -- at most 8 rows per KV head (a single query's GQA group, or a
+// long KV split into chunks, several kernels kept busy at once to cut
+// bubbles): one persistent launch whose workgroups pull tasks from per-XCD
+// queues.  A task is one item (a run of paged KV blocks and the query rows
+// attending to it) on one KV head (MFMA path) or four KV heads (VALU path); it
+// yields either final output rows or partial triples (m, l, acc), m in log2
+// units.
+//   * VALU path -- at most 8 rows per KV head (a single query's GQA group, or a
 //                  few queries of a small pack).  Bandwidth bound: q K^T with
 //                  v_dot2_f32_bf16, p V with fp32 FMAs, 16-byte coalesced loads
-//                  straight into registers, 8-lane DPP reductions, online softmax.
-//   * fwd_mfma  -- packed groups (up to 256 rows per KV head): S^T = K Q^T and
+//                  straight into registers, 8-lane DPP reductions.
+//   * MFMA path -- packed groups (up to 128 rows per KV head): S^T = K Q^T and
 //                  O^T = V^T P^T on v_mfma_f32_16x16x32_bf16, K/V tiles staged
 //                  in LDS by direct global->LDS DMA, three stages deep.
 // Merge (PAT review, merge stage: online-softmax combination of the per-
-// workgroup partial results of a query): fwd rows with several partials.
+// workgroup partial results of a query): one workgroup per query, all heads.
 //
 // Scores are kept in log2 units (q.k * scale * log2 e) so every exponential is
 // a single v_exp_f32.  The running max is refreshed lazily: a row is rescaled
@@ -64,6 +67,59 @@ constexpr int waitcnt_vm() {
     return (N & 0xF) | ((N >> 4) << 14) | 0x0F70;
 }
 
+// Direct global -> LDS copy of 16 bytes per lane: lane i writes LDS bytes
+// [lds + 16 i, lds + 16 i + 16) (lds is wave-uniform, passed in M0).  Issued from
+// inline assembly so that the compiler does not guard later LDS reads with waits
+// on these loads: the pipeline orders them itself (s_waitcnt vmcnt + s_barrier).
+// M0 is saved and restored around the copy.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(g)
+        : "memory");
+}
+
+// Schedule arrays are read-only for a whole launch: reading them through the
+// constant address space lets uniform reads become scalar (SMEM) loads, which
+// do not count against vmcnt and so never stall the in-flight KV loads.
+#define KV_CONST __attribute__((address_space(4)))
+template <typename T>
+__device__ __forceinline__ const KV_CONST T* cptr(const T* x) {
+    return (const KV_CONST T*)(x);
+}
+
+// Schedule records read field by field through the constant address space;
+// items come out as wave-uniform values (SGPRs).
+__device__ __forceinline__ Item load_item(const Item* base, int i) {
+    const KV_CONST int32_t* f = cptr(reinterpret_cast<const int32_t*>(base + i));
+    Item u;
+    u.kind = __builtin_amdgcn_readfirstlane(f[0]);
+    u.tile = __builtin_amdgcn_readfirstlane(f[1]);
+    u.pos_begin = __builtin_amdgcn_readfirstlane(f[2]);
+    u.n_tokens = __builtin_amdgcn_readfirstlane(f[3]);
+    u.q_begin = __builtin_amdgcn_readfirstlane(f[4]);
+    u.n_q = __builtin_amdgcn_readfirstlane(f[5]);
+    u.blk_begin = __builtin_amdgcn_readfirstlane(f[6]);
+    u.n_rows = __builtin_amdgcn_readfirstlane(f[7]);
+    return u;
+}
+
+__device__ __forceinline__ Entry load_entry(const Entry* base, int i) {
+    const KV_CONST int32_t* f = cptr(reinterpret_cast<const int32_t*>(base + i));
+    Entry e;
+    e.query = f[0];
+    e.dest = f[1];
+    e.limit = f[2];
+    e.pad = 0;
+    return e;
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     bf16x2 v;
     v.x = (__bf16)a;
@@ -72,27 +128,20 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 }
 
 // ============================================================================
-// VALU forward: one wave per (item, KV head); a workgroup holds 4 KV heads.
+// VALU task: one wave per KV head; a workgroup covers 4 consecutive KV heads.
 // Lane = 8 * t + c: token slots t and t + 8 of each 16-token block, and the
 // head-dim chunk set of c (elements [8c, 8c+8) and, for D = 128, [64+8c, 64+8c+8)),
 // so every load instruction reads whole 128-byte rows of a block.
 // ============================================================================
 template <int D, int R>
-__global__ __launch_bounds__(256) void fwd_valu_kernel(DevPlan p, Dims dm, int item_begin,
-                                                       const uint16_t* __restrict__ q,
-                                                       const uint16_t* __restrict__ kc,
-                                                       const uint16_t* __restrict__ vc, float* __restrict__ out) {
+__device__ __forceinline__ void valu_task(const DevPlan& p, const Dims& dm, const Item& it, int g,
+                                          const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+                                          const uint16_t* __restrict__ vc, float* __restrict__ out) {
     constexpr int NPC = D / 64;      // 16-byte pieces per token per lane
     constexpr int NE = 8 * NPC;      // elements per token per lane
     constexpr int NWD = NE / 2;      // bf16 pairs per token per lane
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
     const int Hkv = dm.num_kv_heads;
-    const int n_hg = (Hkv + 3) >> 2;
-    const int item_id = item_begin + int(blockIdx.x) / n_hg;
-    const int g = (int(blockIdx.x) % n_hg) * 4 + wave;
-    if (g >= Hkv) return;
-    const Item it = p.items[item_id];
     const int G = dm.group;
     const int t = lane >> 3, c = lane & 7;
 
@@ -101,7 +150,7 @@ __global__ __launch_bounds__(256) void fwd_valu_kernel(DevPlan p, Dims dm, int i
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         if (r < it.n_rows) {
-            const Entry e = p.entries[it.q_begin + r / G];
+            const Entry e = load_entry(p.entries, it.q_begin + r / G);
             const int h = g * G + r % G;
             const uint16_t* qrow = q + (size_t(e.query) * dm.num_q_heads + h) * D;
 #pragma unroll
@@ -133,11 +182,13 @@ __global__ __launch_bounds__(256) void fwd_valu_kernel(DevPlan p, Dims dm, int i
     const int nblk = (n_tok + 15) >> 4;
     const size_t head_elems = size_t(16) * D;
     const size_t blk_elems = size_t(Hkv) * head_elems;
-    const int32_t* __restrict__ bids = p.block_ids + it.blk_begin;
+    const KV_CONST int32_t* bids = cptr(p.block_ids) + it.blk_begin;
     const float sl2 = dm.scale_log2;
 
+    // Blocks past the end of the range are loaded from the zero page and masked,
+    // so the ring below needs no branches (and the compiler keeps its loads in flight).
     auto load_block = [&](int k, uint4 (&kb)[2][NPC], uint4 (&vb)[2][NPC]) {
-        const int blk = bids[k];
+        const int blk = bids[k < nblk ? k : nblk - 1];
         const uint16_t* kbase = kc + size_t(blk) * blk_elems + size_t(g) * head_elems;
         const uint16_t* vbase = vc + size_t(blk) * blk_elems + size_t(g) * head_elems;
 #pragma unroll
@@ -219,19 +270,23 @@ __global__ __launch_bounds__(256) void fwd_valu_kernel(DevPlan p, Dims dm, int i
     // three-deep register ring: blocks k+1 and k+2 are in flight while k is processed
     uint4 k0[2][NPC], v0[2][NPC], k1[2][NPC], v1[2][NPC], k2[2][NPC], v2[2][NPC];
     load_block(0, k0, v0);
-    if (nblk > 1) load_block(1, k1, v1);
-    if (nblk > 2) load_block(2, k2, v2);
+    load_block(1, k1, v1);
+    load_block(2, k2, v2);
+    // scheduling barriers keep each refill after the compute that frees its registers,
+    // so two blocks stay in flight and register pressure stays bounded
     for (int k = 0; k < nblk; k += 3) {
         process(k, k0, v0);
-        if (k + 3 < nblk) load_block(k + 3, k0, v0);
-        if (k + 1 < nblk) {
-            process(k + 1, k1, v1);
-            if (k + 4 < nblk) load_block(k + 4, k1, v1);
-        }
-        if (k + 2 < nblk) {
-            process(k + 2, k2, v2);
-            if (k + 5 < nblk) load_block(k + 5, k2, v2);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_block(k + 3, k0, v0);
+        __builtin_amdgcn_sched_barrier(0);
+        process(k + 1, k1, v1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_block(k + 4, k1, v1);
+        __builtin_amdgcn_sched_barrier(0);
+        process(k + 2, k2, v2);
+        __builtin_amdgcn_sched_barrier(0);
+        load_block(k + 5, k2, v2);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- combine the 8 token lanes of each chunk set (lanes c, c+8, ..., c+56) ----
@@ -280,8 +335,8 @@ __global__ __launch_bounds__(256) void fwd_valu_kernel(DevPlan p, Dims dm, int i
     const int d0 = (ebase < 8) ? 8 * c + ebase : 64 + 8 * c + (ebase - 8);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        if (r >= it.n_rows) break;
-        const Entry e = p.entries[it.q_begin + r / G];
+        if (r >= it.n_rows) continue;
+        const Entry e = load_entry(p.entries, it.q_begin + r / G);
         const int h = g * G + r % G;
         if (e.dest < 0) {
             float* o = out + (size_t(e.query) * dm.num_q_heads + h) * D + d0;
@@ -305,8 +360,8 @@ __global__ __launch_bounds__(256) void fwd_valu_kernel(DevPlan p, Dims dm, int i
 }
 
 // ============================================================================
-// MFMA forward: one workgroup of NW waves per (item, KV head); wave w owns rows
-// [32w, 32w + 32) as two 16-row tiles.  Per 32-token tile:
+// MFMA task: the workgroup's 4 waves share one KV head's tiles; wave w owns
+// rows [16 t w, 16 t (w + 1)) as t = 1 or 2 sixteen-row tiles.  Per 32-token tile:
 //   S^T[16 tok x 16 rows] = K[16 x 32 d] . Q^T[32 d x 16 rows]   (4 k-steps at D = 128)
 //   O^T[16 d x 16 rows]  += V^T[16 d x 32 tok] . P^T[32 tok x 16 rows]
 // The head-dim index of O^T row m in output tile j is 8m + j (D = 128) or 4m + j
@@ -316,12 +371,12 @@ __global__ __launch_bounds__(256) void fwd_valu_kernel(DevPlan p, Dims dm, int i
 // K and V tiles live in LDS in rows of D/8 16-byte chunks, chunk index XOR
 // (token mod D/8) to keep the 16 row-strided reads of an operand conflict free.
 // ============================================================================
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void fwd_mfma_kernel(DevPlan p, Dims dm, int item_begin,
-                                                           const uint16_t* __restrict__ q,
-                                                           const uint16_t* __restrict__ kc,
-                                                           const uint16_t* __restrict__ vc,
-                                                           float* __restrict__ out) {
+template <int D, int TPW>
+__device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, const Item& it, int g,
+                                          const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+                                          const uint16_t* __restrict__ vc, float* __restrict__ out,
+                                          uint16_t* s_kv, int32_t* s_blk) {
+    constexpr int NW = kWaves;
     constexpr int TT = kMfmaTileTokens;    // 32 tokens per stage
     constexpr int CPR = D / 8;             // 16-byte chunks per token row
     constexpr int TCH = TT * CPR;          // chunks per K (or V) tile
@@ -329,36 +384,32 @@ __global__ __launch_bounds__(64 * NW) void fwd_mfma_kernel(DevPlan p, Dims dm, i
     constexpr int NDT = D / 16;            // output tiles
     constexpr int NT = 64 * NW;            // threads
     constexpr int LPT = TCH >= NT ? TCH / NT : 1;   // DMA chunks per thread per tensor and tile
-    constexpr int MAXBLK = kMaxItemBlocks;
+    constexpr int NS = kMfmaStages;        // LDS stages: NS - 1 tiles in flight
+    constexpr int STAGE = 2 * TT * D;      // elements per stage (K tile then V tile)
     static_assert(TCH % NT == 0 || NT % TCH == 0, "tile chunks must split evenly over the workgroup");
 
-    __shared__ __attribute__((aligned(16))) uint16_t s_k0[TT * D], s_k1[TT * D], s_k2[TT * D];
-    __shared__ __attribute__((aligned(16))) uint16_t s_v0[TT * D], s_v1[TT * D], s_v2[TT * D];
-    __shared__ int32_t s_blk[MAXBLK];
-
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
     const int Hkv = dm.num_kv_heads;
-    const int item_id = item_begin + int(blockIdx.x) / Hkv;
-    const int g = int(blockIdx.x) % Hkv;
-    const Item it = p.items[item_id];
     const int G = dm.group;
     const int n_tok = it.n_tokens;
     const int nblk = (n_tok + 15) >> 4;
     const int ntiles = (n_tok + TT - 1) / TT;
+    const int row0 = wave * 16 * TPW;       // TPW sixteen-row tiles per wave
 
     for (int i = tid; i < nblk; i += NT) s_blk[i] = p.block_ids[it.blk_begin + i];
 
-    // ---- Q operands (B of S^T = K Q^T): lane -> row lr of the tile, d = 32s + 8lg .. +7
-    bf16x8 qop[2][KS];
-    int lim[2];
-    int nrt = 0;
+    // ---- Q operands (B of S^T = K Q^T): lane -> row lr of the tile, d = 32s + 8lg .. +7.
+    // Rows past the item's rows get q = 0: they are computed but never stored.
+    bf16x8 qop[TPW][KS];
+    int lim[TPW];
+    const bool active = row0 < it.n_rows;   // wave-uniform
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const int r = wave * 32 + rt * 16 + lr;
+    for (int rt = 0; rt < TPW; ++rt) {
+        const int r = row0 + rt * 16 + lr;
         if (r < it.n_rows) {
-            const Entry e = p.entries[it.q_begin + r / G];
+            const Entry e = load_entry(p.entries, it.q_begin + r / G);
             const int h = g * G + r % G;
             const uint16_t* qrow = q + (size_t(e.query) * dm.num_q_heads + h) * D;
 #pragma unroll
@@ -369,92 +420,112 @@ __global__ __launch_bounds__(64 * NW) void fwd_mfma_kernel(DevPlan p, Dims dm, i
             for (int s = 0; s < KS; ++s) qop[rt][s] = bf16x8{};
             lim[rt] = 0;
         }
-        if (wave * 32 + rt * 16 < it.n_rows) nrt = rt + 1;
     }
-    __syncthreads();   // s_blk ready; all scalar and vector setup loads done
+    // tokens every row of the item attends to: tiles below this need no mask
+    int lim_all = n_tok;
+    for (int e = 0; e < it.n_q; ++e) lim_all = min(lim_all, load_entry(p.entries, it.q_begin + e).limit);
+    // Complete every setup load here: the tile loop below must see no older
+    // vector-memory operation, or waits on it would also drain the tile DMA.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
+    __syncthreads();   // block table staged; every wave's setup loads are done
 
+    // ---- loop-invariant DMA geometry: chunk u of this thread is token tok_u, row offset off_u
     const size_t head_elems = size_t(16) * D;
     const size_t blk_elems = size_t(Hkv) * head_elems;
-    const size_t goff = size_t(g) * head_elems;
-
-    auto issue_tile = [&](int i, uint16_t* sk, uint16_t* sv) {
+    const uint16_t* kh = kc + size_t(g) * head_elems;
+    const uint16_t* vh = vc + size_t(g) * head_elems;
+    // chunk u of this thread is token tok0 + u * (NT / CPR): the same row offset in
+    // every u, since NT / CPR is a multiple of 16 (or LPT is 1)
+    static_assert(LPT == 1 || (NT / CPR) % 16 == 0, "DMA chunk stride");
+    const int tok0 = tid / CPR;
+    const int off0 = (tok0 & 15) * D + ((tid % CPR) ^ (tok0 & (CPR - 1))) * 8;
+    const uint32_t lds_base = uint32_t(uintptr_t(s_kv));
+    auto issue_tile = [&](int i) {
+        const uint32_t st = lds_base + uint32_t((i % NS) * STAGE * 2);
+        const int kb = 2 * i;
+        const int blk0 = __builtin_amdgcn_readfirstlane(s_blk[kb]);
+        const int blk1 = __builtin_amdgcn_readfirstlane(kb + 1 < nblk ? s_blk[kb + 1] : blk0);
+        const size_t o0 = size_t(blk0) * blk_elems, o1 = size_t(blk1) * blk_elems;
 #pragma unroll
         for (int u = 0; u < LPT; ++u) {
-            if (u * NT + wave * 64 >= TCH) break;       // wave-uniform: waves past the tile issue nothing
-            const int pos = u * NT + tid;               // physical chunk in the tile
-            const int tok = pos / CPR, pc = pos % CPR;
-            const int lc = pc ^ (tok & (CPR - 1));       // logical chunk held at pos
-            const int gt = i * TT + tok;
-            const uint16_t* ks = p.zero;
-            const uint16_t* vs = p.zero;
-            if (gt < n_tok) {
-                const size_t off = size_t(s_blk[gt >> 4]) * blk_elems + goff + size_t(gt & 15) * D + lc * 8;
-                ks = kc + off;
-                vs = vc + off;
-            }
-            __builtin_amdgcn_global_load_lds(ks, (__attribute__((address_space(3))) void*)(sk + (u * NT + wave * 64) * 8),
-                                             16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vs, (__attribute__((address_space(3))) void*)(sv + (u * NT + wave * 64) * 8),
-                                             16, 0, 0);
+            if (u * NT + wave * 64 >= TCH) continue;    // wave-uniform: waves past the tile issue nothing
+            const int tok = tok0 + u * (NT / CPR);
+            const bool ok = i * TT + tok < n_tok;
+            const size_t o = (tok < 16 ? o0 : o1) + off0;
+            const uint32_t dst = st + uint32_t((u * NT + wave * 64) * 16);
+            dma16(ok ? static_cast<const void*>(kh + o) : static_cast<const void*>(p.zero), dst);
+            dma16(ok ? static_cast<const void*>(vh + o) : static_cast<const void*>(p.zero), dst + TT * D * 2);
         }
     };
 
-    float mref[2] = {kNegSentinel, kNegSentinel};
-    float lsum[2] = {0.f, 0.f};
-    f32x4 acc[2][NDT];
+    float mref[TPW], lsum[TPW];
+    f32x4 acc[TPW][NDT];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < TPW; ++rt) {
+        mref[rt] = kNegSentinel;
+        lsum[rt] = 0.f;
 #pragma unroll
         for (int j = 0; j < NDT; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     const float sl2 = dm.scale_log2;
 
-    auto compute = [&](int i, const uint16_t* sk, const uint16_t* sv) {
-        if (nrt == 0) return;
-        // K operands: token 16*half + lr, logical chunk 4s + lg
-        bf16x8 kop[2][KS];
+    // per-lane LDS element offsets of the K (A of QK) and V (to be transposed)
+    // operands for token half 0; half 1 adds 16 rows (the XOR swizzle only sees
+    // token mod 16, which both halves share)
+    constexpr int HALF = 16 * CPR * 8;
+    int koff[KS], voff[4];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) koff[s] = (lr * CPR + ((4 * s + lg) ^ (lr & (CPR - 1)))) * 8;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int tok = 4 * lg + u;
+        if constexpr (D == 128)
+            voff[u] = TT * D + (tok * CPR + (lr ^ (tok & (CPR - 1)))) * 8;
+        else
+            voff[u] = TT * D + (tok * CPR + ((lr >> 1) ^ (tok & (CPR - 1)))) * 8 + (lr & 1) * 4;
+    }
+
+    auto compute = [&](int i, const uint16_t* sb) {
+        if (!active) return;
+        // ---- S^T tiles (unscaled q.k)
+        f32x4 sc[TPW][2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            const int tok = 16 * half + lr;
+            bf16x8 kop[KS];
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int pc = (4 * s + lg) ^ (tok & (CPR - 1));
-                kop[half][s] = *reinterpret_cast<const bf16x8*>(sk + (tok * CPR + pc) * 8);
-            }
-        }
-        f32x4 sc[2][2];
+            for (int s = 0; s < KS; ++s) kop[s] = *reinterpret_cast<const bf16x8*>(sb + koff[s] + half * HALF);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            if (rt >= nrt) break;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
+            for (int rt = 0; rt < TPW; ++rt) {
                 f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < KS; ++s) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[half][s], qop[rt][s], a, 0, 0, 0);
+                for (int s = 0; s < KS; ++s) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[s], qop[rt][s], a, 0, 0, 0);
                 sc[rt][half] = a;
             }
         }
-        // scale, mask, lazy max
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- mask (tail tiles only): token 16 half + 4 lg + e beyond the row's limit
+        if ((i + 1) * TT > lim_all) {
+#pragma unroll
+            for (int rt = 0; rt < TPW; ++rt)
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (i * TT + 16 * half + 4 * lg + e >= lim[rt]) sc[rt][half][e] = -INFINITY;
+        }
+        // ---- lazy running max in log2 units
         bool need = false;
-        float tmax[2];
+        float tmax[TPW];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            tmax[rt] = -INFINITY;
-            if (rt >= nrt) break;
-#pragma unroll
-            for (int half = 0; half < 2; ++half)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int tok = i * TT + 16 * half + 4 * lg + e;
-                    const float v = tok < lim[rt] ? sc[rt][half][e] * sl2 : -INFINITY;
-                    sc[rt][half][e] = v;
-                    tmax[rt] = fmaxf(tmax[rt], v);
-                }
+        for (int rt = 0; rt < TPW; ++rt) {
+            const float m4a = fmaxf(fmaxf(sc[rt][0][0], sc[rt][0][1]), fmaxf(sc[rt][0][2], sc[rt][0][3]));
+            const float m4b = fmaxf(fmaxf(sc[rt][1][0], sc[rt][1][1]), fmaxf(sc[rt][1][2], sc[rt][1][3]));
+            tmax[rt] = fmaxf(m4a, m4b) * sl2;
             need |= tmax[rt] > mref[rt] + kRescaleLog2;
         }
         if (__any(need)) {
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                if (rt >= nrt) break;
+            for (int rt = 0; rt < TPW; ++rt) {
                 float rm = tmax[rt];
                 rm = fmaxf(rm, __shfl_xor(rm, 16));
                 rm = fmaxf(rm, __shfl_xor(rm, 32));
@@ -466,104 +537,86 @@ __global__ __launch_bounds__(64 * NW) void fwd_mfma_kernel(DevPlan p, Dims dm, i
                 mref[rt] = mn;
             }
         }
-        // V^T operands: tokens tau(lg, u) = 4lg + u (u < 4) or 16 + 4lg + (u - 4)
-        bf16x8 vt[8];
-        if constexpr (D == 128) {
-            uint4 raw[8];
+        // ---- P^T operands (bf16 hi + lo): token tau(lg, u) = 4lg + u (u < 4) or 16 + 4lg + (u - 4)
+        bf16x8 phi[TPW], plo[TPW];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int tok = (u < 4) ? 4 * lg + u : 16 + 4 * lg + (u - 4);
-                const int pc = lr ^ (tok & (CPR - 1));
-                raw[u] = *reinterpret_cast<const uint4*>(sv + (tok * CPR + pc) * 8);
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                uint32_t w[4];
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const uint32_t a = (&raw[2 * x].x)[j >> 1], b = (&raw[2 * x + 1].x)[j >> 1];
-                    w[x] = __builtin_amdgcn_perm(b, a, (j & 1) ? 0x07060302u : 0x05040100u);
-                }
-                vt[j] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-            }
-        } else {
-            uint2 raw[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int tok = (u < 4) ? 4 * lg + u : 16 + 4 * lg + (u - 4);
-                const int pc = (lr >> 1) ^ (tok & (CPR - 1));
-                raw[u] = *reinterpret_cast<const uint2*>(sv + (tok * CPR + pc) * 8 + (lr & 1) * 4);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t w[4];
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const uint32_t a = (&raw[2 * x].x)[j >> 1], b = (&raw[2 * x + 1].x)[j >> 1];
-                    w[x] = __builtin_amdgcn_perm(b, a, (j & 1) ? 0x07060302u : 0x05040100u);
-                }
-                vt[j] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-            }
-        }
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            if (rt >= nrt) break;
+        for (int rt = 0; rt < TPW; ++rt) {
             float pv[8];
-            float ps = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                pv[e] = fast_exp2(sc[rt][0][e] - mref[rt]);
-                pv[4 + e] = fast_exp2(sc[rt][1][e] - mref[rt]);
+                pv[e] = fast_exp2(fmaf(sc[rt][0][e], sl2, -mref[rt]));
+                pv[4 + e] = fast_exp2(fmaf(sc[rt][1][e], sl2, -mref[rt]));
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ps += pv[e];
-            lsum[rt] += ps;
+            lsum[rt] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 hi[x] = pack_bf16(pv[2 * x], pv[2 * x + 1]);
                 lo[x] = pack_bf16(pv[2 * x] - bf_lo(hi[x]), pv[2 * x + 1] - bf_hi(hi[x]));
             }
-            const bf16x8 phi = __builtin_bit_cast(bf16x8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
-            const bf16x8 plo = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+            phi[rt] = __builtin_bit_cast(bf16x8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+            plo[rt] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- V^T operands, built one output tile at a time from an 8 x 8 (8 x 4) register block
+        constexpr int RAWW = D == 128 ? 4 : 2;   // dwords per lane per token
+        uint32_t raw[8][RAWW];
 #pragma unroll
-            for (int j = 0; j < NDT; ++j) {
-                acc[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[j], phi, acc[rt][j], 0, 0, 0);
-                acc[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[j], plo, acc[rt][j], 0, 0, 0);
+        for (int u = 0; u < 8; ++u) {
+            const uint16_t* src = sb + voff[u & 3] + (u >> 2) * HALF;
+            if constexpr (D == 128) {
+                const uint4 r4 = *reinterpret_cast<const uint4*>(src);
+                raw[u][0] = r4.x; raw[u][1] = r4.y; raw[u][2] = r4.z; raw[u][3] = r4.w;
+            } else {
+                const uint2 r2 = *reinterpret_cast<const uint2*>(src);
+                raw[u][0] = r2.x; raw[u][1] = r2.y;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NDT; ++j) {
+            uint32_t w[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                w[x] = __builtin_amdgcn_perm(raw[2 * x + 1][j >> 1], raw[2 * x][j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
+            const bf16x8 vt = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+#pragma unroll
+            for (int rt = 0; rt < TPW; ++rt) {
+                acc[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, phi[rt], acc[rt][j], 0, 0, 0);
+                acc[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, plo[rt], acc[rt][j], 0, 0, 0);
             }
         }
     };
 
-    // ---- three-stage pipeline: tiles i+1 and i+2 stream in while i is computed ----
-    issue_tile(0, s_k0, s_v0);
-    if (ntiles > 1) issue_tile(1, s_k1, s_v1);
+    // ---- NS-stage pipeline: tiles i+1 .. i+NS-1 stream in while tile i is computed ----
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+        if (i < ntiles) issue_tile(i);
     for (int i = 0; i < ntiles; ++i) {
-        // this thread's DMA for tile i is complete once at most the 2*LPT loads of
-        // tile i+1 remain outstanding
-        if (i + 1 < ntiles) {
+        // this thread's DMA for tile i is complete once at most the loads of the
+        // (up to NS - 2) younger tiles remain outstanding
+        const int younger = min(ntiles - 1 - i, NS - 2);
+        if (younger >= 2) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm<4 * LPT>());
+        } else if (younger == 1) {
             __builtin_amdgcn_s_waitcnt(waitcnt_vm<2 * LPT>());
         } else {
             __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
         }
         __builtin_amdgcn_s_barrier();   // every wave's DMA for tile i landed; tile i-1 is consumed
-        const int st = i % 3;
-        if (i + 2 < ntiles) {
-            const int sn = (i + 2) % 3;
-            issue_tile(i + 2, sn == 0 ? s_k0 : (sn == 1 ? s_k1 : s_k2), sn == 0 ? s_v0 : (sn == 1 ? s_v1 : s_v2));
-        }
-        compute(i, st == 0 ? s_k0 : (st == 1 ? s_k1 : s_k2), st == 0 ? s_v0 : (st == 1 ? s_v1 : s_v2));
+        if (i + NS - 1 < ntiles) issue_tile(i + NS - 1);
+        compute(i, s_kv + (i % NS) * STAGE);
     }
 
     // ---- epilogue: lane holds row lr of each tile, head dims of output tile j, row m = 4lg + e
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        if (rt >= nrt) break;
+    for (int rt = 0; rt < TPW; ++rt) {
+        if (!active) continue;
         float lt = lsum[rt];
         lt += __shfl_xor(lt, 16);
         lt += __shfl_xor(lt, 32);
-        const int r = wave * 32 + rt * 16 + lr;
+        const int r = row0 + rt * 16 + lr;
         if (r >= it.n_rows) continue;
-        const Entry e = p.entries[it.q_begin + r / G];
+        const Entry e = load_entry(p.entries, it.q_begin + r / G);
         const int h = g * G + r % G;
         float* dst;
         float scale;
@@ -600,102 +653,195 @@ __global__ __launch_bounds__(64 * NW) void fwd_mfma_kernel(DevPlan p, Dims dm, i
 }
 
 // ============================================================================
-// Merge: one wave per (query, q head) with >= 2 partial triples.
-//   M = max_i m_i, w_i = 2^(m_i - M), out = sum_i w_i acc_i / sum_i w_i l_i
+// Persistent forward kernels: each workgroup drains its own XCD's queue
+// (blockIdx mod 8; workgroups are dispatched round-robin over the XCDs), then
+// steals from the others.  The last workgroup to finish clears the queue
+// cursors, so the next launch -- or a graph replay -- starts from zero without
+// a memset.  VALU and MFMA tasks share one launch and one set of queues, so
+// the MFMA work of packed groups runs side by side with the bandwidth-bound
+// private tails (the goal of the PAT review's multi-stream forward: no
+// execution bubbles), without cross-stream synchronisation.
 // ============================================================================
-template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(DevPlan p, Dims dm, int q_begin, int q_count,
-                                                    float* __restrict__ out) {
-    constexpr int PER = D / 64;
-    const int Hq = dm.num_q_heads;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int row = int(blockIdx.x) * 4 + wave;
-    if (row >= q_count * Hq) return;
-    const int mq = q_begin + row / Hq;
-    const int h = row % Hq;
-    const int b = p.merge_query[mq];
-    const int i0 = p.merge_ptr[mq], i1 = p.merge_ptr[mq + 1];
-    float M = -INFINITY;
-    for (int i = i0; i < i1; ++i) M = fmaxf(M, p.part_ml[(size_t(p.merge_dest[i]) + h) * 2]);
-    float L = 0.f;
-    float a[PER];
-#pragma unroll
-    for (int x = 0; x < PER; ++x) a[x] = 0.f;
-    for (int i = i0; i < i1; ++i) {
-        const size_t slot = size_t(p.merge_dest[i]) + h;
-        const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + slot * 2);
-        const float w = fast_exp2(ml.x - M);
-        L += w * ml.y;
-        const float* src = p.part_acc + slot * D + lane * PER;
-        if constexpr (PER == 2) {
-            const float2 v = *reinterpret_cast<const float2*>(src);
-            a[0] = fmaf(w, v.x, a[0]);
-            a[1] = fmaf(w, v.y, a[1]);
-        } else {
-            a[0] = fmaf(w, src[0], a[0]);
+template <typename Body>
+__device__ __forceinline__ void drain_queues(const DevPlan& p, int32_t* s_task, Body&& body) {
+    const int own = int(blockIdx.x) % kQueues;
+    for (int k = 0; k < kQueues; ++k) {
+        const int qi = (own + k) % kQueues;
+        const int base = cptr(p.queue_ptr)[qi];
+        const int n = cptr(p.queue_ptr)[qi + 1] - base;
+        if (n <= 0) continue;
+        while (true) {
+            if (threadIdx.x == 0) *s_task = atomicAdd(p.counters + qi, 1);
+            __syncthreads();
+            const int t = __builtin_amdgcn_readfirstlane(*s_task);
+            __syncthreads();   // every thread has read s_task; the previous task's LDS is free
+            if (t >= n) break;
+            const KV_CONST int32_t* tk = cptr(reinterpret_cast<const int32_t*>(p.tasks + base + t));
+            const int item = __builtin_amdgcn_readfirstlane(tk[0]);
+            const int head = __builtin_amdgcn_readfirstlane(tk[1]);
+            body(load_item(p.items, item), head);
         }
     }
-    const float inv = 1.f / L;
-    float* o = out + (size_t(b) * Hq + h) * D + lane * PER;
-    if constexpr (PER == 2) {
-        *reinterpret_cast<float2*>(o) = make_float2(a[0] * inv, a[1] * inv);
-    } else {
-        o[0] = a[0] * inv;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        if (atomicAdd(p.counters + kQueues, 1) == int(gridDim.x) - 1) {
+            for (int qi = 0; qi < kQueues; ++qi) atomicExch(p.counters + qi, 0);
+            atomicExch(p.counters + kQueues, 0);
+        }
     }
 }
 
-template <int D, int R>
-int launch_valu_t(const DevPlan& p, const Dims& d, int item_begin, int item_count, const uint16_t* q,
-                  const uint16_t* k, const uint16_t* v, float* out, hipStream_t s) {
-    const int n_hg = (d.num_kv_heads + 3) / 4;
-    hipLaunchKernelGGL((fwd_valu_kernel<D, R>), dim3(item_count * n_hg), dim3(256), 0, s, p, d, item_begin, q, k, v,
-                       out);
-    return int(hipGetLastError());
+template <int D, int R, int TPW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fwd_kernel(
+    DevPlan p, Dims dm, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, float* __restrict__ out) {
+    constexpr int TT = kMfmaTileTokens;
+    __shared__ __attribute__((aligned(16))) uint16_t s_kv[kMfmaStages * 2 * TT * D];
+    __shared__ int32_t s_blk[kMaxItemBlocks];
+    __shared__ int32_t s_task;
+    drain_queues(p, &s_task, [&](const Item& it, int head) {
+        if (it.kind == KVATTN_VARIANT_MFMA) {
+            mfma_task<D, TPW>(p, dm, it, head, q, kc, vc, out, s_kv, s_blk);
+        } else {
+            const int g = head + (threadIdx.x >> 6);
+            if (g < dm.num_kv_heads) valu_task<D, R>(p, dm, it, g, q, kc, vc, out);
+        }
+    });
 }
 
-template <int D, int NW>
-int launch_mfma_t(const DevPlan& p, const Dims& d, int item_begin, int item_count, const uint16_t* q,
-                  const uint16_t* k, const uint16_t* v, float* out, hipStream_t s) {
-    hipLaunchKernelGGL((fwd_mfma_kernel<D, NW>), dim3(item_count * d.num_kv_heads), dim3(64 * NW), 0, s, p, d,
-                       item_begin, q, k, v, out);
+// ============================================================================
+// Merge: one workgroup per query with several partial triples, all q heads at
+// once.  The slots of one item entry are consecutive (slot = dest + h), so each
+// partial's accumulators for every head form one contiguous [Hq][D] block.
+//   M_h = max_i m_ih, w_ih = 2^(m_ih - M_h) / sum_i 2^(m_ih - M_h) l_ih,
+//   out[h] = sum_i w_ih acc_ih
+// ============================================================================
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(DevPlan p, Dims dm, float* __restrict__ out) {
+    constexpr int COLS = 1024;              // floats of [Hq][D] per workgroup (blockIdx.y selects the block)
+    constexpr int HB = COLS / D;            // heads per workgroup
+    constexpr int MAXW = 4096;              // weights staged per batch of partials
+    __shared__ float s_m[HB];
+    __shared__ float s_inv[HB];
+    __shared__ float s_w[MAXW];
+    const int Hq = dm.num_q_heads;
+    const int h_lo = int(blockIdx.y) * HB;
+    const int nh = min(HB, Hq - h_lo);
+    const int mq = blockIdx.x;
+    const KV_CONST int32_t* mptr = cptr(p.merge_ptr);
+    const KV_CONST int32_t* mdst = cptr(p.merge_dest);
+    const int b = cptr(p.merge_query)[mq];
+    const int i0 = mptr[mq], i1 = mptr[mq + 1];
+    const int tid = threadIdx.x;
+    // per head: M = max m_i, 1 / sum_i 2^(m_i - M) l_i  (one wave per head)
+    for (int hh = tid >> 6; hh < nh; hh += 4) {
+        const int h = h_lo + hh;
+        float M = -INFINITY;
+        for (int i = i0 + (tid & 63); i < i1; i += 64) M = fmaxf(M, p.part_ml[(size_t(mdst[i]) + h) * 2]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+        float L = 0.f;
+        for (int i = i0 + (tid & 63); i < i1; i += 64) {
+            const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + (size_t(mdst[i]) + h) * 2);
+            L += fast_exp2(ml.x - M) * ml.y;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+        if ((tid & 63) == 0) {
+            s_m[hh] = M;
+            s_inv[hh] = 1.f / L;
+        }
+    }
+    const int n4 = nh * D / 4;              // float4 of this workgroup's block (<= 256)
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int per = MAXW / nh;
+    const int hq = (4 * tid) / D;           // head of this thread's float4
+    for (int ib = i0; ib < i1; ib += per) {
+        const int nb = min(per, i1 - ib);
+        __syncthreads();
+        for (int x = tid; x < nb * nh; x += 256) {
+            const int i = x / nh, hh = x % nh;
+            const float m = p.part_ml[(size_t(mdst[ib + i]) + h_lo + hh) * 2];
+            s_w[x] = fast_exp2(m - s_m[hh]) * s_inv[hh];
+        }
+        __syncthreads();
+        if (tid < n4) {
+            int i = 0;
+            for (; i + 4 <= nb; i += 4) {
+                float4 v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    v[u] = reinterpret_cast<const float4*>(p.part_acc + (size_t(mdst[ib + i + u]) + h_lo) * D)[tid];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float w = s_w[(i + u) * nh + hq];
+                    acc.x = fmaf(w, v[u].x, acc.x);
+                    acc.y = fmaf(w, v[u].y, acc.y);
+                    acc.z = fmaf(w, v[u].z, acc.z);
+                    acc.w = fmaf(w, v[u].w, acc.w);
+                }
+            }
+            for (; i < nb; ++i) {
+                const float4 v = reinterpret_cast<const float4*>(p.part_acc + (size_t(mdst[ib + i]) + h_lo) * D)[tid];
+                const float w = s_w[i * nh + hq];
+                acc.x = fmaf(w, v.x, acc.x);
+                acc.y = fmaf(w, v.y, acc.y);
+                acc.z = fmaf(w, v.z, acc.z);
+                acc.w = fmaf(w, v.w, acc.w);
+            }
+        }
+    }
+    if (tid < n4) reinterpret_cast<float4*>(out + (size_t(b) * Hq + h_lo) * D)[tid] = acc;
+}
+
+// Grid of a persistent launch: the workgroups the device holds at once
+// (occupancy API x CUs), or fewer when there are fewer tasks.
+template <typename K>
+int persistent_grid(K kernel, int* cache, int n_tasks) {
+    if (*cache == 0) {
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return -1;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess) return -1;
+        *cache = cus * (per_cu > 0 ? per_cu : 1);
+    }
+    return n_tasks < *cache ? n_tasks : *cache;
+}
+
+template <int D, int R, int TPW>
+int launch_fwd_t(const DevPlan& p, const Dims& d, int n_tasks, const uint16_t* q, const uint16_t* k,
+                 const uint16_t* v, float* out, hipStream_t s) {
+    static int slots = 0;
+    const int grid = persistent_grid(fwd_kernel<D, R, TPW>, &slots, n_tasks);
+    if (grid < 0) return int(hipErrorInvalidDevice);
+    hipLaunchKernelGGL((fwd_kernel<D, R, TPW>), dim3(grid), dim3(256), 0, s, p, d, q, k, v, out);
     return int(hipGetLastError());
 }
 
 }  // namespace
 
-int launch_forward_valu(const DevPlan& p, const Dims& d, int rows, int item_begin, int item_count,
-                        const uint16_t* q, const uint16_t* k, const uint16_t* v, float* out, void* stream) {
+int launch_forward(const DevPlan& p, const Dims& d, int valu_rows, int mfma_tiles, int n_tasks,
+                   const uint16_t* q, const uint16_t* k, const uint16_t* v, float* out, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (item_count <= 0) return 0;
-#define KV_VALU(DD, RR) \
-    if (d.head_dim == DD && rows == RR) return launch_valu_t<DD, RR>(p, d, item_begin, item_count, q, k, v, out, s);
-    KV_VALU(128, 1) KV_VALU(128, 2) KV_VALU(128, 4) KV_VALU(128, 8)
-    KV_VALU(64, 1) KV_VALU(64, 2) KV_VALU(64, 4) KV_VALU(64, 8)
-#undef KV_VALU
+    if (n_tasks <= 0) return 0;
+#define KV_FWD(DD, RR, TP)                                           \
+    if (d.head_dim == DD && valu_rows == RR && mfma_tiles == TP) \
+        return launch_fwd_t<DD, RR, TP>(p, d, n_tasks, q, k, v, out, s);
+    KV_FWD(128, 1, 1) KV_FWD(128, 2, 1) KV_FWD(128, 4, 1) KV_FWD(128, 8, 1)
+    KV_FWD(128, 1, 2) KV_FWD(128, 2, 2) KV_FWD(128, 4, 2) KV_FWD(128, 8, 2)
+    KV_FWD(64, 1, 1) KV_FWD(64, 2, 1) KV_FWD(64, 4, 1) KV_FWD(64, 8, 1)
+    KV_FWD(64, 1, 2) KV_FWD(64, 2, 2) KV_FWD(64, 4, 2) KV_FWD(64, 8, 2)
+#undef KV_FWD
     return int(hipErrorInvalidValue);
 }
 
-int launch_forward_mfma(const DevPlan& p, const Dims& d, int waves, int item_begin, int item_count,
-                        const uint16_t* q, const uint16_t* k, const uint16_t* v, float* out, void* stream) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (item_count <= 0) return 0;
-#define KV_MFMA(DD, WW) \
-    if (d.head_dim == DD && waves == WW) return launch_mfma_t<DD, WW>(p, d, item_begin, item_count, q, k, v, out, s);
-    KV_MFMA(128, 1) KV_MFMA(128, 2) KV_MFMA(128, 4) KV_MFMA(128, 8)
-    KV_MFMA(64, 1) KV_MFMA(64, 2) KV_MFMA(64, 4) KV_MFMA(64, 8)
-#undef KV_MFMA
-    return int(hipErrorInvalidValue);
-}
-
-int launch_merge(const DevPlan& p, const Dims& d, int q_begin, int q_count, float* out, void* stream) {
+int launch_merge(const DevPlan& p, const Dims& d, int q_count, float* out, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (q_count <= 0) return 0;
-    const int rows = q_count * d.num_q_heads;
-    const dim3 grid((rows + 3) / 4);
     if (d.head_dim == 128)
-        hipLaunchKernelGGL((merge_kernel<128>), grid, dim3(256), 0, s, p, d, q_begin, q_count, out);
+        hipLaunchKernelGGL((merge_kernel<128>), dim3(q_count, (d.num_q_heads + 7) / 8), dim3(256), 0, s, p, d, out);
     else if (d.head_dim == 64)
-        hipLaunchKernelGGL((merge_kernel<64>), grid, dim3(256), 0, s, p, d, q_begin, q_count, out);
+        hipLaunchKernelGGL((merge_kernel<64>), dim3(q_count, (d.num_q_heads + 15) / 16), dim3(256), 0, s, p, d, out);
     else
         return int(hipErrorInvalidValue);
     return int(hipGetLastError());

@@ -330,12 +330,15 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         }
     }
 
-    // ---- row groups, kernel variant, split length --------------------------------
+    // ---- row groups and kernel variant (runtime tile selector) -------------------
+    // VALU: at most 8 rows per KV head; MFMA: at most 128 rows (4 waves x 32),
+    // 16 rows per wave when the group fits 64 rows.  Wider packs are split into
+    // row groups that read the same KV range (in the same XCD's L2).
     struct Group {
         int unit;
         std::vector<int> queries;
         int kind, tile, rows;
-        double w;                // cost per token relative to a bandwidth-bound token
+        double w;                // cost per token and KV head relative to streaming it from HBM
     };
     std::vector<Group> groups;
     for (size_t ui = 0; ui < units.size(); ++ui) {
@@ -350,7 +353,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         } else {
             kind = (R <= kValuMaxRows) ? KVATTN_VARIANT_VALU : KVATTN_VARIANT_MFMA;
         }
-        const int max_rows = kind == KVATTN_VARIANT_VALU ? kValuMaxRows : kMfmaRowsPerWave * kMfmaMaxWaves;
+        const int max_rows = kind == KVATTN_VARIANT_VALU ? kValuMaxRows : kMfmaMaxRows;
         const int qpg = std::max(1, max_rows / G);
         const int n = int(u.queries.size());
         const int ng = (n + qpg - 1) / qpg;
@@ -365,19 +368,29 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
                 g.tile = next_pow2(g.rows);
                 g.w = 1.0;
             } else {
-                g.tile = next_pow2((g.rows + kMfmaRowsPerWave - 1) / kMfmaRowsPerWave);
-                g.w = std::max(1.0, g.rows / 192.0);
+                g.tile = g.rows <= 64 ? 1 : 2;
+                // MFMA task time relative to streaming the same tokens at one workgroup's
+                // share of a CU's bandwidth: grows with the rows of the group
+                g.w = std::max(1.0, g.rows / 64.0);
             }
             groups.push_back(std::move(g));
         }
     }
-    double work = 0.0;
+
+    // ---- split length (long-KV splitting) -------------------------------------------
+    // A task is one item on one KV head (MFMA) or four KV heads (VALU).  The
+    // chunk length aims at ~1.5 waves of tasks over the persistent workgroups,
+    // but never so short that partial triples cost more than ~25 % of the
+    // chunk's KV bytes.
+    const int heads_per_valu_task = std::min(Hkv, kWaves);
+    const int slots = num_cus * 2;
+    double work = 0.0;           // token x KV-head units, weighted
     for (const Group& g : groups) work += double(units[g.unit].tokens) * g.w * Hkv;
     int64_t C;
     if (o.split_tokens > 0) {
         C = std::min<int64_t>(ceil16(o.split_tokens), kChunkCapTokens);
     } else {
-        C = ceil16(int64_t(std::ceil(work / (double(num_cus) * 8.0))));
+        C = ceil16(int64_t(std::ceil(work / (double(slots) * 1.5))));
         C = std::min<int64_t>(std::max<int64_t>(C, 64), kChunkCapTokens);
     }
 
@@ -389,7 +402,11 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         if (o.split_tokens > 0) {
             chunk = C;
         } else {
-            chunk = ceil16(std::max<int64_t>(32, int64_t(double(C) / g.w)));
+            const int hpt = g.kind == KVATTN_VARIANT_VALU ? heads_per_valu_task : 1;
+            chunk = ceil16(int64_t(double(C) / (g.w * hpt)));
+            // partial triples (write + read) per chunk stay under ~25 % of the chunk's KV bytes
+            const int64_t floor_tok = ceil16(int64_t(4.0 * g.rows * partial_row_bytes * 2 / (2.0 * D * 2)));
+            chunk = std::max<int64_t>(chunk, std::max<int64_t>(64, floor_tok));
             chunk = std::min<int64_t>(chunk, g.kind == KVATTN_VARIANT_VALU ? 4096 : kChunkCapTokens);
         }
         const int64_t nch = (u.tokens + chunk - 1) / chunk;
@@ -422,18 +439,36 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             p.it.n_tokens = int32_t(item_tokens);
             p.it.n_q = int32_t(g.queries.size());
             p.it.n_rows = g.rows;
-            p.cost = double(item_tokens) * g.w;
+            // per-task cost: tokens x heads of the task x weight (+ a fixed start-up cost)
+            const int hpt = g.kind == KVATTN_VARIANT_VALU ? heads_per_valu_task : 1;
+            p.cost = double(item_tokens) * g.w * hpt + 32.0 * hpt;
             protos.push_back(std::move(p));
         }
     }
 
-    // ---- order: launch group (MFMA by waves, then VALU by rows), longest first ----
+    // ---- forward launches ----------------------------------------------------------------
+    // One launch runs VALU and MFMA tasks side by side.  Launch i takes the
+    // i-th largest VALU row template and the i-th largest MFMA tiling, so a
+    // plan needs max(#templates, #tilings) launches -- normally one.
+    std::vector<int> vt, mt;
+    for (const Proto& p : protos) {
+        std::vector<int>& v = p.it.kind == KVATTN_VARIANT_MFMA ? mt : vt;
+        if (std::find(v.begin(), v.end(), p.it.tile) == v.end()) v.push_back(p.it.tile);
+    }
+    std::sort(vt.begin(), vt.end(), std::greater<int>());
+    std::sort(mt.begin(), mt.end(), std::greater<int>());
+    const int n_launch = int(std::max(vt.size(), mt.size()));
+    auto launch_of = [&](const Proto& p) {
+        const std::vector<int>& v = p.it.kind == KVATTN_VARIANT_MFMA ? mt : vt;
+        return int(std::find(v.begin(), v.end(), p.it.tile) - v.begin());
+    };
+
+    // ---- item order: by launch, then longest first (stable) -------------------------------
     std::vector<int> order(protos.size());
     std::iota(order.begin(), order.end(), 0);
-    auto group_key = [&](const Proto& p) { return (p.it.kind == KVATTN_VARIANT_MFMA ? 0 : 1000) + p.it.tile; };
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
-        int ka = group_key(protos[a]), kb = group_key(protos[b]);
-        if (ka != kb) return ka < kb;
+        const int la = launch_of(protos[a]), lb = launch_of(protos[b]);
+        if (la != lb) return la < lb;
         return protos[a].cost > protos[b].cost;
     });
 
@@ -445,23 +480,27 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     P.entries.clear();
     P.block_ids.clear();
     std::vector<std::vector<int32_t>> dests(B);
-    int32_t slots = 0;
+    std::vector<double> item_cost;
+    std::vector<int> item_launch;
+    int32_t slots_used = 0;
     for (int idx : order) {
         Proto& p = protos[idx];
         p.it.q_begin = int32_t(P.entries.size());
         p.it.blk_begin = int32_t(P.block_ids.size());
         for (Entry e : p.entries) {
             if (count[e.query] > 1) {
-                e.dest = slots;
-                slots += Hq;
+                e.dest = slots_used;
+                slots_used += Hq;
                 dests[e.query].push_back(e.dest);
             }
             P.entries.push_back(e);
         }
         P.block_ids.insert(P.block_ids.end(), p.blocks.begin(), p.blocks.end());
         P.items.push_back(p.it);
+        item_cost.push_back(p.cost);
+        item_launch.push_back(launch_of(p));
     }
-    P.n_slots = slots;
+    P.n_slots = slots_used;
     P.merge_query.clear();
     P.merge_dest.clear();
     P.merge_ptr.assign(1, 0);
@@ -476,21 +515,59 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         P.merge_ptr.push_back(int32_t(P.merge_dest.size()));
     }
 
-    // ---- launches ---------------------------------------------------------------------------
+    // ---- tasks and per-XCD queues --------------------------------------------------------------
+    // MFMA tasks of KV head g go to queue g mod 8, so the row groups and chunks
+    // that read one KV head's shared range meet in one XCD's L2; VALU tasks go
+    // to the least-loaded queue, longest first.  Each queue is drained longest
+    // first; idle workgroups steal from the other queues.
+    P.tasks.clear();
+    P.queue_ptr.assign(size_t(n_launch) * (kQueues + 1), 0);
     P.forward_launches.clear();
-    P.merge_launches.clear();
-    for (size_t i = 0; i < P.items.size();) {
-        size_t j = i;
-        while (j < P.items.size() && P.items[j].kind == P.items[i].kind && P.items[j].tile == P.items[i].tile) ++j;
-        Launch L;
-        L.kind = P.items[i].kind == KVATTN_VARIANT_MFMA ? 1 : 0;
-        L.tile = P.items[i].tile;
-        L.item_begin = int(i);
-        L.item_count = int(j - i);
-        P.forward_launches.push_back(L);
-        i = j;
+    for (int L = 0; L < n_launch; ++L) {
+        struct QT {
+            Task t;
+            double cost;
+        };
+        std::vector<std::vector<QT>> q(kQueues);
+        std::vector<double> load(kQueues, 0.0);
+        std::vector<QT> valu;
+        for (size_t i = 0; i < P.items.size(); ++i) {
+            if (item_launch[i] != L) continue;
+            const Item& it = P.items[i];
+            if (it.kind == KVATTN_VARIANT_MFMA) {
+                for (int g = 0; g < Hkv; ++g) {
+                    const double c = item_cost[i];
+                    q[g % kQueues].push_back({{int32_t(i), g}, c});
+                    load[g % kQueues] += c;
+                }
+            } else {
+                for (int g = 0; g < Hkv; g += kWaves) valu.push_back({{int32_t(i), g}, item_cost[i]});
+            }
+        }
+        std::stable_sort(valu.begin(), valu.end(), [](const QT& a, const QT& b) { return a.cost > b.cost; });
+        for (const QT& t : valu) {
+            int best = int(std::min_element(load.begin(), load.end()) - load.begin());
+            q[best].push_back(t);
+            load[best] += t.cost;
+        }
+        int n_tasks = 0;
+        const int base = int(P.tasks.size());
+        for (int k = 0; k < kQueues; ++k) {
+            std::stable_sort(q[k].begin(), q[k].end(), [](const QT& a, const QT& b) { return a.cost > b.cost; });
+            P.queue_ptr[size_t(L) * (kQueues + 1) + k] = int32_t(P.tasks.size()) - base;
+            for (const QT& t : q[k]) P.tasks.push_back(t.t);
+            n_tasks += int(q[k].size());
+        }
+        P.queue_ptr[size_t(L) * (kQueues + 1) + kQueues] = int32_t(P.tasks.size()) - base;
+        Launch Lr;
+        // a kind without tasks in this launch takes the smallest instantiation
+        Lr.valu_rows = L < int(vt.size()) ? vt[size_t(L)] : 1;
+        Lr.mfma_tiles = L < int(mt.size()) ? mt[size_t(L)] : 1;
+        Lr.index = L;
+        Lr.n_tasks = n_tasks;
+        Lr.task_base = base;
+        P.forward_launches.push_back(Lr);
     }
-    if (!P.merge_query.empty()) P.merge_launches.push_back(Launch{2, 0, 0, int(P.merge_query.size())});
 
     // ---- blob ------------------------------------------------------------------------------------
     BlobHeader& h = P.header;
@@ -501,19 +578,24 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     h.n_entries = int32_t(P.entries.size());
     h.n_block_ids = int32_t(P.block_ids.size());
     h.n_merge_q = int32_t(P.merge_query.size());
-    h.n_slots = slots;
+    h.n_slots = slots_used;
     h.head_dim = D;
+    h.n_tasks = int32_t(P.tasks.size());
+    h.n_launches = n_launch;
     uint64_t off = align256(sizeof(BlobHeader));
     h.off_items = off;        off = align256(off + P.items.size() * sizeof(Item));
     h.off_entries = off;      off = align256(off + P.entries.size() * sizeof(Entry));
     h.off_block_ids = off;    off = align256(off + P.block_ids.size() * 4);
+    h.off_tasks = off;        off = align256(off + P.tasks.size() * sizeof(Task));
+    h.off_queue_ptr = off;    off = align256(off + P.queue_ptr.size() * 4);
+    h.off_counters = off;     off = align256(off + uint64_t(n_launch) * kCounters * 4);
     h.off_merge_query = off;  off = align256(off + P.merge_query.size() * 4);
     h.off_merge_ptr = off;    off = align256(off + P.merge_ptr.size() * 4);
     h.off_merge_dest = off;   off = align256(off + P.merge_dest.size() * 4);
     h.off_zero = off;         off = align256(off + 256);
     h.blob_bytes = off;
-    h.off_part_ml = off;      off = align256(off + uint64_t(slots) * 8);
-    h.off_part_acc = off;     off = align256(off + uint64_t(slots) * D * 4);
+    h.off_part_ml = off;      off = align256(off + uint64_t(slots_used) * 8);
+    h.off_part_acc = off;     off = align256(off + uint64_t(slots_used) * D * 4);
     h.total_bytes = off;
     P.blob.assign(h.blob_bytes, 0);
     std::memcpy(P.blob.data(), &h, sizeof(h));
@@ -523,6 +605,8 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     put(h.off_items, P.items.data(), P.items.size() * sizeof(Item));
     put(h.off_entries, P.entries.data(), P.entries.size() * sizeof(Entry));
     put(h.off_block_ids, P.block_ids.data(), P.block_ids.size() * 4);
+    put(h.off_tasks, P.tasks.data(), P.tasks.size() * sizeof(Task));
+    put(h.off_queue_ptr, P.queue_ptr.data(), P.queue_ptr.size() * 4);
     put(h.off_merge_query, P.merge_query.data(), P.merge_query.size() * 4);
     put(h.off_merge_ptr, P.merge_ptr.data(), P.merge_ptr.size() * 4);
     put(h.off_merge_dest, P.merge_dest.data(), P.merge_dest.size() * 4);
@@ -554,15 +638,15 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             st.num_items_mfma++;
     }
     st.planned_kv_bytes = planned * bpt;
-    st.partial_bytes = int64_t(slots) * partial_row_bytes * 2;
+    st.partial_bytes = int64_t(slots_used) * partial_row_bytes * 2;
     st.num_nodes = int32_t(nodes.size());
     st.num_packed_nodes = packed_nodes;
     st.num_items = int32_t(P.items.size());
     st.num_folded_leaves = folded;
-    st.num_partial_slots = slots;
+    st.num_partial_slots = slots_used;
     st.num_merge_rows = int32_t(P.merge_query.size()) * Hq;
     st.num_direct_rows = direct_rows;
-    st.num_launches = int32_t(P.forward_launches.size() + P.merge_launches.size());
+    st.num_launches = int32_t(P.forward_launches.size() + (P.merge_query.empty() ? 0 : 1));
     st.split_tokens = int32_t(C);
     st.blob_bytes = h.blob_bytes;
     st.workspace_bytes = h.total_bytes;
@@ -669,6 +753,8 @@ kvattn_status kvattn_plan_export(kvattn_plan_t plan, kvattn_export* out) {
     out->merge_dest = plan->merge_dest.data();
     out->num_partial_slots = plan->n_slots;
     out->head_dim = plan->shape.head_dim;
+    out->num_tasks = int32_t(plan->tasks.size());
+    out->tasks = reinterpret_cast<const int32_t*>(plan->tasks.data());
     return KVATTN_OK;
 }
 

@@ -15,8 +15,9 @@ struct kvattn_plan_s {
     std::vector<int32_t> block_ids;
     std::vector<int32_t> merge_query, merge_ptr, merge_dest;
     int32_t n_slots = 0;
+    std::vector<kvattn::Task> tasks;
+    std::vector<int32_t> queue_ptr;         // [launch][kQueues + 1]
     std::vector<kvattn::Launch> forward_launches;
-    std::vector<kvattn::Launch> merge_launches;
     std::vector<unsigned char> blob;        // serialised schedule: header + arrays + zero region
     kvattn::BlobHeader header{};
     kvattn_stats stats{};

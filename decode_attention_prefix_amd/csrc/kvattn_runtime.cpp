@@ -11,13 +11,21 @@
 namespace kvattn {
 namespace {
 
-DevPlan resolve(const kvattn_plan_s& P) {
+DevPlan resolve(const kvattn_plan_s& P, int launch) {
     auto* base = static_cast<unsigned char*>(P.dev_ws);
     const BlobHeader& h = P.header;
     DevPlan d;
     d.items = reinterpret_cast<const Item*>(base + h.off_items);
     d.entries = reinterpret_cast<const Entry*>(base + h.off_entries);
     d.block_ids = reinterpret_cast<const int32_t*>(base + h.off_block_ids);
+    d.tasks = reinterpret_cast<const Task*>(base + h.off_tasks);
+    d.queue_ptr = reinterpret_cast<const int32_t*>(base + h.off_queue_ptr);
+    d.counters = reinterpret_cast<int32_t*>(base + h.off_counters);
+    if (launch >= 0) {
+        d.tasks += P.forward_launches[size_t(launch)].task_base;
+        d.queue_ptr += size_t(launch) * (kQueues + 1);
+        d.counters += size_t(launch) * kCounters;
+    }
     d.merge_query = reinterpret_cast<const int32_t*>(base + h.off_merge_query);
     d.merge_ptr = reinterpret_cast<const int32_t*>(base + h.off_merge_ptr);
     d.merge_dest = reinterpret_cast<const int32_t*>(base + h.off_merge_dest);
@@ -50,16 +58,13 @@ kvattn_status run_forward(const void* q, const void* k, const void* v, kvattn_pl
     if (!q || !k || !v || !out) return set_error(KVATTN_EINVAL, "q, k_cache, v_cache or out is NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return set_error(KVATTN_EINVAL, "q, k_cache, v_cache and out must be 16-byte aligned");
-    const DevPlan dp = resolve(*plan);
     const Dims d = dims(*plan);
+    // Each launch drains its queues of MFMA and VALU tasks; launches (normally
+    // one) follow each other on `stream`.
     for (const Launch& L : plan->forward_launches) {
-        int rc;
-        if (L.kind == 1)
-            rc = launch_forward_mfma(dp, d, L.tile, L.item_begin, L.item_count, static_cast<const uint16_t*>(q),
-                                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), out, stream);
-        else
-            rc = launch_forward_valu(dp, d, L.tile, L.item_begin, L.item_count, static_cast<const uint16_t*>(q),
-                                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), out, stream);
+        const DevPlan dp = resolve(*plan, L.index);
+        const int rc = launch_forward(dp, d, L.valu_rows, L.mfma_tiles, L.n_tasks, static_cast<const uint16_t*>(q),
+                                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), out, stream);
         if (rc != 0)
             return set_error(KVATTN_EHIP, std::string("forward launch failed: ") + hipGetErrorString(hipError_t(rc)));
     }
@@ -68,13 +73,10 @@ kvattn_status run_forward(const void* q, const void* k, const void* v, kvattn_pl
 
 kvattn_status run_merge(kvattn_plan_t plan, float* out, void* stream) {
     if (!out) return set_error(KVATTN_EINVAL, "out is NULL");
-    const DevPlan dp = resolve(*plan);
+    const DevPlan dp = resolve(*plan, -1);
     const Dims d = dims(*plan);
-    for (const Launch& L : plan->merge_launches) {
-        int rc = launch_merge(dp, d, L.item_begin, L.item_count, out, stream);
-        if (rc != 0)
-            return set_error(KVATTN_EHIP, std::string("merge launch failed: ") + hipGetErrorString(hipError_t(rc)));
-    }
+    const int rc = launch_merge(dp, d, int(plan->merge_query.size()), out, stream);
+    if (rc != 0) return set_error(KVATTN_EHIP, std::string("merge launch failed: ") + hipGetErrorString(hipError_t(rc)));
     return KVATTN_OK;
 }
 

@@ -66,7 +66,7 @@ class kvattn_export(ctypes.Structure):
     _fields_ = [("num_items", i32), ("items", ctypes.POINTER(kvattn_item_info)), ("num_entries", i32),
                 ("entries", ctypes.POINTER(kvattn_item_query)), ("num_block_ids", i32), ("block_ids", P32),
                 ("num_merge_queries", i32), ("merge_query", P32), ("merge_ptr", P32), ("merge_dest", P32),
-                ("num_partial_slots", i32), ("head_dim", i32)]
+                ("num_partial_slots", i32), ("head_dim", i32), ("num_tasks", i32), ("tasks", P32)]
 
 
 def _load():
@@ -242,6 +242,7 @@ def kvattn_plan_export(plan: Plan) -> dict:
         "merge_dest": arr(e.merge_dest, int(arr(e.merge_ptr, e.num_merge_queries + 1, 1)[-1, 0]), 1).reshape(-1),
         "num_partial_slots": e.num_partial_slots,
         "head_dim": e.head_dim,
+        "tasks": arr(e.tasks, e.num_tasks, 2),
     }
 
 

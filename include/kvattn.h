@@ -151,7 +151,7 @@ typedef struct {
 /* One forward work item, as exported for inspection and coverage checks. */
 typedef struct {
     int32_t kind;        /* KVATTN_VARIANT_VALU or _MFMA                                      */
-    int32_t tile;        /* VALU: rows per KV head (1,2,4,8); MFMA: waves per workgroup      */
+    int32_t tile;        /* VALU: rows per KV head (1,2,4,8); MFMA: 16-row tiles per wave (1,2) */
     int32_t pos_begin;   /* first logical block position of the item's KV range               */
     int32_t n_tokens;    /* tokens in the item's KV range                                     */
     int32_t q_begin;     /* first entry in entries[]                                          */
@@ -182,6 +182,9 @@ typedef struct {
     const int32_t* merge_dest;    /* partial slot bases of the query's items              */
     int32_t num_partial_slots;
     int32_t head_dim;
+    int32_t num_tasks;
+    const int32_t* tasks;         /* [num_tasks][2]: (item, first KV head); an MFMA item runs one
+                                     task per KV head, a VALU item one per 4 consecutive KV heads */
 } kvattn_export;
 
 /* Fill *opts with the defaults (AUTO packing, scheme auto, auto variant and split). */

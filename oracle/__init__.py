@@ -43,6 +43,8 @@ def _oracle():
         lib.kvattn_oracle_partial.restype = ctypes.c_int
         lib.kvattn_oracle_merge.argtypes = [i32, i32, p, p, p, p]
         lib.kvattn_oracle_merge.restype = ctypes.c_int
+        lib.kvattn_oracle_threads.argtypes = []
+        lib.kvattn_oracle_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -118,3 +120,8 @@ def merge(ms, ls, accs):
     if rc != 0:
         raise ValueError("oracle rejected its inputs")
     return out
+
+
+def threads() -> int:
+    """OpenMP threads the oracle uses on this host."""
+    return int(_oracle().kvattn_oracle_threads())

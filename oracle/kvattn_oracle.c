@@ -28,6 +28,7 @@
  * a hand-derived golden case).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -154,3 +155,6 @@ int kvattn_oracle_merge(int32_t n, int32_t D, const double* m, const double* l, 
     for (int32_t k = 0; k < D; ++k) out[k] /= L;
     return 0;
 }
+
+/* OpenMP threads the oracle's parallel loops use. */
+int kvattn_oracle_threads(void) { return omp_get_max_threads(); }

@@ -38,7 +38,7 @@ _oracle_cache = {}
 
 
 def oracle_out(wl, scale=0.0):
-    key = (wl.name, scale, wl.seed_values)
+    key = (wl.name, wl.shape_tuple(), scale, wl.seed_values)
     if key not in _oracle_cache:
         _oracle_cache[key] = oracle.decode_workload(wl, scale=scale)
     return _oracle_cache[key]
@@ -48,13 +48,14 @@ _dev_cache = {}
 
 
 def device_inputs(wl):
-    if wl.name not in _dev_cache:
+    key = (wl.name, wl.shape_tuple(), wl.seed_values)
+    if key not in _dev_cache:
         _dev_cache.clear()
         q = torch.from_numpy(wl.q.view(np.int16)).cuda()
         k = torch.from_numpy(wl.k_pool.view(np.int16)).cuda()
         v = torch.from_numpy(wl.v_pool.view(np.int16)).cuda()
-        _dev_cache[wl.name] = (q, k, v)
-    return _dev_cache[wl.name]
+        _dev_cache[key] = (q, k, v)
+    return _dev_cache[key]
 
 
 def gpu_decode(wl, **opts):
@@ -116,7 +117,8 @@ def edge_workload(lengths, shared, Hq, Hkv, D, seed):
         else:
             s.append((("own", b), T))
         segs.append(s)
-    return W.from_segments("edge%d" % seed, segs, Hq, Hkv, D, seed, 500 + seed, extra_blocks=2).materialize()
+    name = "edge_s%d_sh%d_h%d_%d_d%d" % (seed, shared, Hq, Hkv, D)
+    return W.from_segments(name, segs, Hq, Hkv, D, seed, 500 + seed, extra_blocks=2).materialize()
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -187,6 +189,7 @@ def test_forward_then_merge_equals_decode():
 def sampled_rows(wl, n, seed):
     rng = np.random.default_rng(seed)
     B, Hq = wl.num_queries, wl.num_q_heads
+    n = min(n, B * Hq)
     rows = set()
     # longest and shortest queries, every head of query 0, plus random rows
     order = np.argsort(wl.seq_lens)
@@ -211,3 +214,28 @@ def test_parity_full_size_sampled(c):
     assert_close(g, ref, "full config %d" % c)
     _dev_cache.clear()
     del wl
+
+
+def test_graph_replay_matches_eager():
+    """A captured decode replays correctly several times, with eager work and syncs in between."""
+    k = K()
+    wl = small(2)
+    dec = k.Decoder(wl.shape_tuple(), wl.block_tables, wl.seq_lens)
+    q, kc, vc = device_inputs(wl)
+    shape = (wl.num_queries, wl.num_q_heads, wl.head_dim)
+    eager = torch.zeros(shape, dtype=torch.float32, device="cuda")
+    k.kvattn_decode(q, kc, vc, dec.plan, eager)
+    torch.cuda.synchronize()
+    out = torch.zeros(shape, dtype=torch.float32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        k.kvattn_decode(q, kc, vc, dec.plan, out)
+    for rep in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), "replay %d differs" % rep
+        other = torch.zeros_like(eager)
+        k.kvattn_decode(q, kc, vc, dec.plan, other)   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other, eager)

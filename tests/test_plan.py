@@ -30,7 +30,7 @@ def check_coverage(wl_bt, seq_lens, Hq, Hkv, ex):
         if it["kind"][i] == K.KVATTN_VARIANT_VALU:
             assert it["n_rows"][i] <= it["tile"][i] <= 8
         else:
-            assert it["n_rows"][i] <= 32 * it["tile"][i] and it["tile"][i] in (1, 2, 4, 8)
+            assert it["tile"][i] in (1, 2) and it["n_rows"][i] <= 64 * it["tile"][i]
         nblk = (n_tok + 15) // 16
         assert nblk <= 512
         blk = ids[int(it["blk_begin"][i]): int(it["blk_begin"][i]) + nblk]
@@ -66,6 +66,14 @@ def check_coverage(wl_bt, seq_lens, Hq, Hkv, ex):
                     assert (x + h) not in slots_used
                     slots_used[x + h] = b
     assert len(slots_used) == ex["num_partial_slots"]
+    # every item runs on every KV head exactly once: one task per head (MFMA) or per 4 heads (VALU)
+    seen = {}
+    for item, head in ex["tasks"]:
+        seen.setdefault(int(item), []).append(int(head))
+    for i in range(len(it["kind"])):
+        heads = sorted(seen.get(i, []))
+        step = 1 if it["kind"][i] == K.KVATTN_VARIANT_MFMA else 4
+        assert heads == list(range(0, Hkv, step)), (i, heads)
 
 
 def plan_of(wl, **opts):
@@ -83,13 +91,19 @@ def test_coverage_full_size_configs(c, mode):
     assert s["query_centric_kv_bytes"] == wl.query_centric_kv_bytes
     if mode == K.KVATTN_PACK_QUERY:
         assert s["planned_kv_bytes"] == wl.query_centric_kv_bytes
-    elif c != 3:
-        # every physical block read by exactly one item
-        assert s["planned_kv_bytes"] == wl.unique_kv_bytes
     else:
-        # the 1024-row root is read by four 256-row groups
-        root = 4096 * wl.bytes_per_token
-        assert s["planned_kv_bytes"] == wl.unique_kv_bytes + 3 * root
+        # every shared segment is read once per group of at most 128 rows (q heads of the
+        # queries sharing it); nothing else is read twice
+        users = {}
+        for segs in wl.segments:
+            for key, n in segs:
+                users.setdefault(key, [0, n])[0] += 1
+        extra = 0
+        for key, (k, n) in users.items():
+            if k >= 2:
+                groups = -(-k * wl.group // 128)
+                extra += (groups - 1) * n * wl.bytes_per_token
+        assert s["planned_kv_bytes"] == wl.unique_kv_bytes + extra
 
 
 @pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
@@ -138,7 +152,9 @@ def test_packing_reads_shared_prefix_once():
     wl = W.config2()
     s = K.kvattn_plan_stats(plan_of(wl))
     assert s["num_packed_nodes"] == 1 and s["num_items_mfma"] > 0
-    assert s["planned_kv_bytes"] == s["unique_kv_bytes"] < s["query_centric_kv_bytes"] / 4
+    # 64 queries x 4 q heads = 256 rows: two 128-row groups read the 2048-token prefix
+    assert s["planned_kv_bytes"] == s["unique_kv_bytes"] + 2048 * wl.bytes_per_token
+    assert s["planned_kv_bytes"] < s["query_centric_kv_bytes"] / 3.9
 
 
 def test_profit_model_skips_tiny_shared_node():
