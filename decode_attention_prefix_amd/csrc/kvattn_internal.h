@@ -6,9 +6,11 @@
 // shared block once for all of them (PAT review, memory-centric prefix-aware
 // packing, Fig 5(d) caption).  An item runs for every KV head: as one task per
 // KV head (MFMA items) or one task per group of four KV heads (VALU items).
-// Tasks wait in per-XCD work queues, longest first, and persistent workgroups
-// pull them.  MFMA and VALU tasks share one launch, so the MFMA work of packed
-// groups overlaps the bandwidth-bound streaming of private tails.
+// Each persistent workgroup runs one static task list built by the planner
+// (longest first over the workgroups): its MFMA tasks, then its VALU tasks as
+// continuous per-wave streams.  MFMA and VALU tasks share one launch, so the
+// MFMA work of packed groups overlaps the bandwidth-bound streaming of
+// private tails.
 #pragma once
 
 #include <cstddef>
@@ -19,17 +21,19 @@
 namespace kvattn {
 
 constexpr int kBlock = 16;              // tokens per KV block
-constexpr int kValuMaxRows = 8;         // rows per KV head the VALU path holds
+constexpr int kValuMaxRows = 8;         // rows per KV head the VALU path holds (D = 64)
+// At D = 128 eight rows do not fit the VALU path's register budget next to
+// its load ring; wider groups go to the MFMA path there.
+constexpr int valu_max_rows(int D) { return D == 128 ? 4 : kValuMaxRows; }
 constexpr int kWaves = 4;               // waves per forward workgroup (both paths)
 constexpr int kMfmaMaxRows = 128;       // rows per MFMA item: 4 waves x 32 rows
 constexpr int kMfmaTileTokens = 32;     // KV tokens per LDS stage
 constexpr int kMfmaStages = 4;          // LDS stages of the MFMA pipeline (3 tiles in flight)
 constexpr int kMaxItemBlocks = 512;     // KV blocks per item (8192 tokens)
 constexpr int kMaxGroup = 64;           // q heads per KV head supported
-constexpr int kQueues = 8;              // work queues, one per XCD of an MI355X
-constexpr int kCounters = 16;           // per launch: kQueues cursors, one finished count, spare
+constexpr int kXcds = 8;                // XCDs of an MI355X (L2 domains)
 constexpr uint32_t kBlobMagic = 0x4B564154u;  // "KVAT"
-constexpr uint32_t kBlobVersion = 2;
+constexpr uint32_t kBlobVersion = 5;
 
 // Device view of one item; identical layout to kvattn_item_info.
 struct Item {
@@ -53,47 +57,69 @@ struct Entry {
 static_assert(sizeof(Entry) == sizeof(kvattn_item_query), "entry layout");
 
 // A forward task: one item for KV head `head` (MFMA) or for KV heads
-// [head, head + 4) (VALU).
+// [head, head + 4) (VALU).  Host-side schedule; the device reads descriptors.
 struct Task {
     int32_t item;
     int32_t head;
 };
 
+// Task descriptor (device, int32 words, 16-byte aligned): a kDescHeader-word
+// header, n_q entries of 4 words (query, dest, limit, 0), then the item's
+// block ids, padded to a multiple of 4 words.
+enum : int {
+    kDescKind = 0,        // KVATTN_VARIANT_VALU / _MFMA
+    kDescTile = 1,        // VALU rows template; MFMA 16-row tiles per wave
+    kDescHead = 2,        // first KV head
+    kDescTokens = 3,      // tokens of the range (with a folded leaf)
+    kDescNq = 4,          // entries
+    kDescRows = 5,        // n_q * G
+    kDescBlocks = 6,      // ceil(tokens / 16)
+    kDescLimAll = 7,      // min limit over the entries: tokens every row attends
+    kDescWords = 8,       // words of this descriptor
+    kDescNextWords = 9,   // words of the next descriptor of the same static list, 0 if last
+    kDescHeader = 16
+};
+constexpr int kMaxItemQueries = kMfmaMaxRows;   // rows per item >= queries per item
+constexpr int kDescMaxWords = kDescHeader + 4 * kMaxItemQueries + kMaxItemBlocks;
+inline int32_t desc_words(int n_q, int nblk) { return kDescHeader + 4 * n_q + ((nblk + 3) & ~3); }
+
+// LDS window of the VALU phase: the MFMA stages (kMfmaStages x 2 x 32 tokens x
+// D bf16 = 512 D bytes) are reused for the list's VALU descriptors and, per
+// wave, four q slots of R rows x D bf16.  Returns the descriptor words that fit.
+constexpr int valu_window_words(int D, int R) { return (512 * D - kWaves * 4 * R * D * 2) / 4; }
+
 // Header at offset 0 of the device workspace.  Offsets are in bytes from the
 // workspace base and 256-byte aligned.
 struct BlobHeader {
     uint32_t magic, version;
-    int32_t n_items, n_entries, n_block_ids, n_merge_q, n_slots, head_dim;
-    int32_t n_tasks, n_launches, pad0, pad1;
-    uint64_t off_items, off_entries, off_block_ids, off_merge_query, off_merge_ptr, off_merge_dest, off_zero;
-    uint64_t off_tasks;       // Task [n_tasks], grouped by launch, then queue, longest first
-    uint64_t off_queue_ptr;   // int32 [n_launches][kQueues + 1]: task ranges of each queue
-    uint64_t off_counters;    // int32 [n_launches][kCounters]: zero at upload, zero after every launch
+    int32_t n_desc_words, n_merge_q, n_slots, head_dim;
+    int32_t n_tasks, n_launches, n_lists, pad0;
+    uint64_t off_desc;        // int32 [n_desc_words]: task descriptors
+    uint64_t off_list_ptr;    // int32 [n_launches][n_lists][3]: word offsets (MFMA begin, VALU begin, end) per list
+    uint64_t off_merge_query, off_merge_ptr, off_merge_dest, off_zero;
     uint64_t blob_bytes;      // bytes copied by kvattn_plan_upload
     uint64_t off_part_ml;     // float2 [n_slots]: (m in log2 units, l)
     uint64_t off_part_acc;    // float [n_slots][head_dim]
     uint64_t total_bytes;     // workspace bytes
 };
 
-// One forward launch: persistent workgroups draining its queues of MFMA and
-// VALU tasks.  A plan needs more than one only when its VALU items use
-// several row templates or its MFMA items several row tilings.
+// One forward launch: persistent workgroups, each running one static list
+// (MFMA tasks, then VALU tasks as per-wave streams).  A plan needs more than
+// one only when its VALU items use several row templates or its MFMA items
+// several row tilings.
 struct Launch {
     int valu_rows;     // VALU row template (1, 2, 4, 8)
     int mfma_tiles;    // MFMA 16-row tiles per wave (1, 2)
-    int index;         // queue set
+    int index;         // list set
     int n_tasks;
-    int task_base;     // first task of the launch
+    int task_base;     // first task of the launch in the host schedule
 };
 
 // Pointers the kernels take, resolved from the bound workspace.
 struct DevPlan {
-    const Item* items;
-    const Entry* entries;
-    const int32_t* block_ids;
-    const Task* tasks;
-    const int32_t* queue_ptr;   // this launch's kQueues + 1 offsets into tasks
-    int32_t* counters;          // this launch's kCounters counters
+    const int32_t* desc;
+    const int32_t* list_ptr;    // this launch's n_lists x 3 word offsets into desc
+    int32_t n_lists;
     const int32_t* merge_query;
     const int32_t* merge_ptr;
     const int32_t* merge_dest;

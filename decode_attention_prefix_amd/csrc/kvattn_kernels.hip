@@ -94,28 +94,35 @@ __device__ __forceinline__ const KV_CONST T* cptr(const T* x) {
     return (const KV_CONST T*)(x);
 }
 
-// Schedule records read field by field through the constant address space;
-// items come out as wave-uniform values (SGPRs).
-__device__ __forceinline__ Item load_item(const Item* base, int i) {
-    const KV_CONST int32_t* f = cptr(reinterpret_cast<const int32_t*>(base + i));
-    Item u;
-    u.kind = __builtin_amdgcn_readfirstlane(f[0]);
-    u.tile = __builtin_amdgcn_readfirstlane(f[1]);
-    u.pos_begin = __builtin_amdgcn_readfirstlane(f[2]);
-    u.n_tokens = __builtin_amdgcn_readfirstlane(f[3]);
-    u.q_begin = __builtin_amdgcn_readfirstlane(f[4]);
-    u.n_q = __builtin_amdgcn_readfirstlane(f[5]);
-    u.blk_begin = __builtin_amdgcn_readfirstlane(f[6]);
-    u.n_rows = __builtin_amdgcn_readfirstlane(f[7]);
-    return u;
+// A task as the kernels see it: header fields as wave-uniform values, entries
+// and block ids left in the LDS copy of the task's descriptor.
+struct TaskView {
+    int kind, tile, head, n_tokens, n_q, n_rows, nblk, lim_all;
+    const int32_t* ent;   // LDS: n_q entries of 4 words (query, dest, limit, 0)
+    const int32_t* blk;   // LDS: nblk block ids
+};
+
+__device__ __forceinline__ TaskView view_of(const int32_t* d) {
+    TaskView v;
+    v.kind = __builtin_amdgcn_readfirstlane(d[kDescKind]);
+    v.tile = __builtin_amdgcn_readfirstlane(d[kDescTile]);
+    v.head = __builtin_amdgcn_readfirstlane(d[kDescHead]);
+    v.n_tokens = __builtin_amdgcn_readfirstlane(d[kDescTokens]);
+    v.n_q = __builtin_amdgcn_readfirstlane(d[kDescNq]);
+    v.n_rows = __builtin_amdgcn_readfirstlane(d[kDescRows]);
+    v.nblk = __builtin_amdgcn_readfirstlane(d[kDescBlocks]);
+    v.lim_all = __builtin_amdgcn_readfirstlane(d[kDescLimAll]);
+    v.ent = d + kDescHeader;
+    v.blk = d + kDescHeader + 4 * v.n_q;
+    return v;
 }
 
-__device__ __forceinline__ Entry load_entry(const Entry* base, int i) {
-    const KV_CONST int32_t* f = cptr(reinterpret_cast<const int32_t*>(base + i));
+__device__ __forceinline__ Entry entry_of(const TaskView& v, int i) {
+    const int4 e4 = *reinterpret_cast<const int4*>(v.ent + 4 * i);
     Entry e;
-    e.query = f[0];
-    e.dest = f[1];
-    e.limit = f[2];
+    e.query = e4.x;
+    e.dest = e4.y;
+    e.limit = e4.z;
     e.pad = 0;
     return e;
 }
@@ -128,79 +135,140 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 }
 
 // ============================================================================
-// VALU task: one wave per KV head; a workgroup covers 4 consecutive KV heads.
+// VALU stream: a wave runs the VALU tasks of its workgroup's list for KV head
+// (task head + wave) as one continuous stream of 16-token blocks.  Its
+// three-deep register ring crosses task boundaries, so blocks of the next
+// task are in flight while the current one finishes and nothing drains
+// between tasks.  The list's descriptors sit in an LDS window; the q rows of a
+// task are copied into one of four per-wave LDS slots by DMA when the load
+// side enters the task, ahead of its first block.
 // Lane = 8 * t + c: token slots t and t + 8 of each 16-token block, and the
 // head-dim chunk set of c (elements [8c, 8c+8) and, for D = 128, [64+8c, 64+8c+8)),
 // so every load instruction reads whole 128-byte rows of a block.
 // ============================================================================
 template <int D, int R>
-__device__ __forceinline__ void valu_task(const DevPlan& p, const Dims& dm, const Item& it, int g,
-                                          const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-                                          const uint16_t* __restrict__ vc, float* __restrict__ out) {
+__device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, const int32_t* win, int n_words,
+                                            uint16_t* qs, const uint16_t* __restrict__ q,
+                                            const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+                                            float* __restrict__ out) {
     constexpr int NPC = D / 64;      // 16-byte pieces per token per lane
     constexpr int NE = 8 * NPC;      // elements per token per lane
     constexpr int NWD = NE / 2;      // bf16 pairs per token per lane
+    constexpr int LPB = 2 * NPC * 2; // loads per block per lane (2 token slots, NPC pieces, K and V)
+    constexpr int QSLOT = R * D;     // bf16 elements of one q slot
+    constexpr int QCH = QSLOT / 8;   // its 16-byte chunks
     const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     const int Hkv = dm.num_kv_heads;
+    const int Hq = dm.num_q_heads;
     const int G = dm.group;
     const int t = lane >> 3, c = lane & 7;
-
-    uint32_t qv[R][NWD];
-    int limit[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        if (r < it.n_rows) {
-            const Entry e = load_entry(p.entries, it.q_begin + r / G);
-            const int h = g * G + r % G;
-            const uint16_t* qrow = q + (size_t(e.query) * dm.num_q_heads + h) * D;
-#pragma unroll
-            for (int pc = 0; pc < NPC; ++pc) {
-                const uint4 v = *reinterpret_cast<const uint4*>(qrow + pc * 64 + 8 * c);
-                qv[r][4 * pc + 0] = v.x;
-                qv[r][4 * pc + 1] = v.y;
-                qv[r][4 * pc + 2] = v.z;
-                qv[r][4 * pc + 3] = v.w;
-            }
-            limit[r] = e.limit;
-        } else {
-#pragma unroll
-            for (int w = 0; w < NWD; ++w) qv[r][w] = 0u;
-            limit[r] = 0;
-        }
-    }
-
-    float m[R], l[R], acc[R][NE];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        m[r] = kNegSentinel;
-        l[r] = 0.f;
-#pragma unroll
-        for (int e = 0; e < NE; ++e) acc[r][e] = 0.f;
-    }
-
-    const int n_tok = it.n_tokens;
-    const int nblk = (n_tok + 15) >> 4;
     const size_t head_elems = size_t(16) * D;
     const size_t blk_elems = size_t(Hkv) * head_elems;
-    const KV_CONST int32_t* bids = cptr(p.block_ids) + it.blk_begin;
     const float sl2 = dm.scale_log2;
+    const uint32_t qs_lds = uint32_t(uintptr_t(qs));
 
-    // Blocks past the end of the range are loaded from the zero page and masked,
-    // so the ring below needs no branches (and the compiler keeps its loads in flight).
-    auto load_block = [&](int k, uint4 (&kb)[2][NPC], uint4 (&vb)[2][NPC]) {
-        const int blk = bids[k < nblk ? k : nblk - 1];
-        const uint16_t* kbase = kc + size_t(blk) * blk_elems + size_t(g) * head_elems;
-        const uint16_t* vbase = vc + size_t(blk) * blk_elems + size_t(g) * head_elems;
+    auto hdr = [&](int off, int f) { return __builtin_amdgcn_readfirstlane(win[off + f]); };
+    // first task at or after `off` that has a KV head for this wave
+    auto skip = [&](int off) {
+        while (off < n_words && hdr(off, kDescHead) + wave >= Hkv) off += hdr(off, kDescWords);
+        return off;
+    };
+    // copy the q rows of the task at `off` into slot `s` of this wave
+    auto fetch_q = [&](int off, int s) {
+        const int nrows = hdr(off, kDescRows);
+        const int g = hdr(off, kDescHead) + wave;
+#pragma unroll
+        for (int c0 = 0; c0 < QCH; c0 += 64) {
+            const int ch = c0 + lane;
+            const int r = ch / (D / 8), pc = ch % (D / 8);
+            if (ch < QCH && r < nrows) {
+                const int query = win[off + kDescHeader + 4 * (r / G)];
+                const uint16_t* src = q + (size_t(query) * Hq + g * G + r % G) * D + pc * 8;
+                dma16(src, qs_lds + uint32_t((s * QSLOT + c0 * 8) * 2));
+            }
+        }
+    };
+
+    // ---- load side
+    int l_off = skip(0);
+    int l_blk = 0, l_slot = 0;
+    int l_nblk = 0, l_ntok = 0, l_bids = 0, l_g = 0;
+    auto l_enter = [&]() {
+        if (l_off < n_words) {
+            l_nblk = hdr(l_off, kDescBlocks);
+            l_ntok = hdr(l_off, kDescTokens);
+            l_bids = l_off + kDescHeader + 4 * hdr(l_off, kDescNq);
+            l_g = hdr(l_off, kDescHead) + wave;
+            fetch_q(l_off, l_slot);
+        }
+    };
+    l_enter();
+    int total = 0;   // blocks of this wave's stream
+    for (int off = l_off; off < n_words; off = skip(off + hdr(off, kDescWords))) total += hdr(off, kDescBlocks);
+
+    // Past the end of the stream the loads come from the zero page, so the ring
+    // below needs no branches around its loads (the compiler keeps them in flight).
+    auto load_block = [&](uint4 (&kb)[2][NPC], uint4 (&vb)[2][NPC]) {
+        const bool live = l_off < n_words;
+        const int blk = live ? __builtin_amdgcn_readfirstlane(win[l_bids + l_blk]) : 0;
+        const uint16_t* kbase = kc + size_t(blk) * blk_elems + size_t(l_g) * head_elems;
+        const uint16_t* vbase = vc + size_t(blk) * blk_elems + size_t(l_g) * head_elems;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const int slot = t + 8 * tt;
-            const bool ok = k * 16 + slot < n_tok;
+            const bool ok = live && l_blk * 16 + slot < l_ntok;
 #pragma unroll
             for (int pc = 0; pc < NPC; ++pc) {
-                const int off = slot * D + pc * 64 + 8 * c;
-                kb[tt][pc] = *reinterpret_cast<const uint4*>(ok ? kbase + off : p.zero);
-                vb[tt][pc] = *reinterpret_cast<const uint4*>(ok ? vbase + off : p.zero);
+                const int o = slot * D + pc * 64 + 8 * c;
+                kb[tt][pc] = *reinterpret_cast<const uint4*>(ok ? kbase + o : p.zero);
+                vb[tt][pc] = *reinterpret_cast<const uint4*>(ok ? vbase + o : p.zero);
             }
+        }
+        if (live && ++l_blk == l_nblk) {
+            l_off = skip(l_off + hdr(l_off, kDescWords));
+            l_blk = 0;
+            l_slot = (l_slot + 1) & 3;
+            l_enter();
+        }
+    };
+
+    // ---- process side
+    int p_off = skip(0);
+    int p_blk = 0, p_slot = 0, p_nblk = 0;
+    uint32_t qv[R][NWD];
+    int limit[R];
+    float m[R], l[R], acc[R][NE];
+
+    auto begin_task = [&]() {
+        // the q copy of this task is older than its first block's loads, which
+        // are complete once at most two blocks' loads remain outstanding
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm<2 * LPB>());
+        __builtin_amdgcn_sched_barrier(0);   // no LDS read of the slot moves above the wait
+        p_nblk = hdr(p_off, kDescBlocks);
+        const int nrows = hdr(p_off, kDescRows);
+        const uint16_t* qsl = qs + p_slot * QSLOT;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (r < nrows) {
+#pragma unroll
+                for (int pc = 0; pc < NPC; ++pc) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(qsl + r * D + pc * 64 + 8 * c);
+                    qv[r][4 * pc + 0] = v.x;
+                    qv[r][4 * pc + 1] = v.y;
+                    qv[r][4 * pc + 2] = v.z;
+                    qv[r][4 * pc + 3] = v.w;
+                }
+                limit[r] = win[p_off + kDescHeader + 4 * (r / G) + 2];
+            } else {
+#pragma unroll
+                for (int w = 0; w < NWD; ++w) qv[r][w] = 0u;
+                limit[r] = 0;
+            }
+            m[r] = kNegSentinel;
+            l[r] = 0.f;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) acc[r][e] = 0.f;
         }
     };
 
@@ -267,95 +335,110 @@ __device__ __forceinline__ void valu_task(const DevPlan& p, const Dims& dm, cons
         }
     };
 
-    // three-deep register ring: blocks k+1 and k+2 are in flight while k is processed
+    // combine the 8 token lanes of each chunk set (lanes c, c+8, ..., c+56) and store
+    auto end_task = [&]() {
+        const int nrows = hdr(p_off, kDescRows);
+        const int g = hdr(p_off, kDescHead) + wave;
+        float ltot[R], mrow[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float M = m[r];
+            M = fmaxf(M, __shfl_xor(M, 8));
+            M = fmaxf(M, __shfl_xor(M, 16));
+            M = fmaxf(M, __shfl_xor(M, 32));
+            const float f = fast_exp2(m[r] - M);
+            float lr = l[r] * f;
+            lr += __shfl_xor(lr, 8);
+            lr += __shfl_xor(lr, 16);
+            lr += __shfl_xor(lr, 32);
+            ltot[r] = lr;
+            mrow[r] = M;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) acc[r][e] *= f;
+        }
+        // reduce-scatter over t: after three halving exchanges each lane owns NE/8 elements
+        const bool u32 = (lane & 32) != 0, u16 = (lane & 16) != 0, u8 = (lane & 8) != 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int i = 0; i < NE / 2; ++i) {
+                const float send = u32 ? acc[r][i] : acc[r][NE / 2 + i];
+                const float keep = u32 ? acc[r][NE / 2 + i] : acc[r][i];
+                acc[r][i] = keep + __shfl_xor(send, 32);
+            }
+#pragma unroll
+            for (int i = 0; i < NE / 4; ++i) {
+                const float send = u16 ? acc[r][i] : acc[r][NE / 4 + i];
+                const float keep = u16 ? acc[r][NE / 4 + i] : acc[r][i];
+                acc[r][i] = keep + __shfl_xor(send, 16);
+            }
+#pragma unroll
+            for (int i = 0; i < NE / 8; ++i) {
+                const float send = u8 ? acc[r][i] : acc[r][NE / 8 + i];
+                const float keep = u8 ? acc[r][NE / 8 + i] : acc[r][i];
+                acc[r][i] = keep + __shfl_xor(send, 8);
+            }
+        }
+        const int ebase = (u32 ? NE / 2 : 0) + (u16 ? NE / 4 : 0) + (u8 ? NE / 8 : 0);
+        // element e of chunk set c is head-dim index 8c + e (e < 8) or 64 + 8c + (e - 8)
+        const int d0 = (ebase < 8) ? 8 * c + ebase : 64 + 8 * c + (ebase - 8);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (r >= nrows) continue;
+            const int4 e = *reinterpret_cast<const int4*>(win + p_off + kDescHeader + 4 * (r / G));
+            const int h = g * G + r % G;
+            if (e.y < 0) {
+                float* o = out + (size_t(e.x) * Hq + h) * D + d0;
+                const float inv = 1.f / ltot[r];
+                if constexpr (NE / 8 == 2) {
+                    *reinterpret_cast<float2*>(o) = make_float2(acc[r][0] * inv, acc[r][1] * inv);
+                } else {
+                    o[0] = acc[r][0] * inv;
+                }
+            } else {
+                const size_t sl = size_t(e.y) + h;
+                float* o = p.part_acc + sl * D + d0;
+                if constexpr (NE / 8 == 2) {
+                    *reinterpret_cast<float2*>(o) = make_float2(acc[r][0], acc[r][1]);
+                } else {
+                    o[0] = acc[r][0];
+                }
+                if (lane == 0) *reinterpret_cast<float2*>(p.part_ml + sl * 2) = make_float2(mrow[r], ltot[r]);
+            }
+        }
+    };
+
+    auto proc_block = [&](const uint4 (&kb)[2][NPC], const uint4 (&vb)[2][NPC]) {
+        if (p_blk == 0) begin_task();
+        process(p_blk, kb, vb);
+        if (++p_blk == p_nblk) {
+            end_task();
+            p_off = skip(p_off + hdr(p_off, kDescWords));
+            p_blk = 0;
+            p_slot = (p_slot + 1) & 3;
+        }
+    };
+
+    // three-deep register ring across the whole stream
     uint4 k0[2][NPC], v0[2][NPC], k1[2][NPC], v1[2][NPC], k2[2][NPC], v2[2][NPC];
-    load_block(0, k0, v0);
-    load_block(1, k1, v1);
-    load_block(2, k2, v2);
+    load_block(k0, v0);
+    load_block(k1, v1);
+    load_block(k2, v2);
     // scheduling barriers keep each refill after the compute that frees its registers,
     // so two blocks stay in flight and register pressure stays bounded
-    for (int k = 0; k < nblk; k += 3) {
-        process(k, k0, v0);
+    for (int j = 0; j < total; j += 3) {
+        proc_block(k0, v0);
         __builtin_amdgcn_sched_barrier(0);
-        load_block(k + 3, k0, v0);
+        load_block(k0, v0);
         __builtin_amdgcn_sched_barrier(0);
-        process(k + 1, k1, v1);
+        if (j + 1 < total) proc_block(k1, v1);
         __builtin_amdgcn_sched_barrier(0);
-        load_block(k + 4, k1, v1);
+        load_block(k1, v1);
         __builtin_amdgcn_sched_barrier(0);
-        process(k + 2, k2, v2);
+        if (j + 2 < total) proc_block(k2, v2);
         __builtin_amdgcn_sched_barrier(0);
-        load_block(k + 5, k2, v2);
+        load_block(k2, v2);
         __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // ---- combine the 8 token lanes of each chunk set (lanes c, c+8, ..., c+56) ----
-    float ltot[R], mrow[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        float M = m[r];
-        M = fmaxf(M, __shfl_xor(M, 8));
-        M = fmaxf(M, __shfl_xor(M, 16));
-        M = fmaxf(M, __shfl_xor(M, 32));
-        const float f = fast_exp2(m[r] - M);
-        float lr = l[r] * f;
-        lr += __shfl_xor(lr, 8);
-        lr += __shfl_xor(lr, 16);
-        lr += __shfl_xor(lr, 32);
-        ltot[r] = lr;
-        mrow[r] = M;
-#pragma unroll
-        for (int e = 0; e < NE; ++e) acc[r][e] *= f;
-    }
-    // reduce-scatter over t: after three halving exchanges each lane owns NE/8 elements
-    const bool u32 = (lane & 32) != 0, u16 = (lane & 16) != 0, u8 = (lane & 8) != 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-#pragma unroll
-        for (int i = 0; i < NE / 2; ++i) {
-            const float send = u32 ? acc[r][i] : acc[r][NE / 2 + i];
-            const float keep = u32 ? acc[r][NE / 2 + i] : acc[r][i];
-            acc[r][i] = keep + __shfl_xor(send, 32);
-        }
-#pragma unroll
-        for (int i = 0; i < NE / 4; ++i) {
-            const float send = u16 ? acc[r][i] : acc[r][NE / 4 + i];
-            const float keep = u16 ? acc[r][NE / 4 + i] : acc[r][i];
-            acc[r][i] = keep + __shfl_xor(send, 16);
-        }
-#pragma unroll
-        for (int i = 0; i < NE / 8; ++i) {
-            const float send = u8 ? acc[r][i] : acc[r][NE / 8 + i];
-            const float keep = u8 ? acc[r][NE / 8 + i] : acc[r][i];
-            acc[r][i] = keep + __shfl_xor(send, 8);
-        }
-    }
-    const int ebase = (u32 ? NE / 2 : 0) + (u16 ? NE / 4 : 0) + (u8 ? NE / 8 : 0);
-    // element e of chunk set c is head-dim index 8c + e (e < 8) or 64 + 8c + (e - 8)
-    const int d0 = (ebase < 8) ? 8 * c + ebase : 64 + 8 * c + (ebase - 8);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        if (r >= it.n_rows) continue;
-        const Entry e = load_entry(p.entries, it.q_begin + r / G);
-        const int h = g * G + r % G;
-        if (e.dest < 0) {
-            float* o = out + (size_t(e.query) * dm.num_q_heads + h) * D + d0;
-            const float inv = 1.f / ltot[r];
-            if constexpr (NE / 8 == 2) {
-                *reinterpret_cast<float2*>(o) = make_float2(acc[r][0] * inv, acc[r][1] * inv);
-            } else {
-                o[0] = acc[r][0] * inv;
-            }
-        } else {
-            const size_t slot = size_t(e.dest) + h;
-            float* o = p.part_acc + slot * D + d0;
-            if constexpr (NE / 8 == 2) {
-                *reinterpret_cast<float2*>(o) = make_float2(acc[r][0], acc[r][1]);
-            } else {
-                o[0] = acc[r][0];
-            }
-            if (lane == 0) *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(mrow[r], ltot[r]);
-        }
     }
 }
 
@@ -372,10 +455,10 @@ __device__ __forceinline__ void valu_task(const DevPlan& p, const Dims& dm, cons
 // (token mod D/8) to keep the 16 row-strided reads of an operand conflict free.
 // ============================================================================
 template <int D, int TPW>
-__device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, const Item& it, int g,
+__device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, const TaskView& it, int g,
                                           const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                                           const uint16_t* __restrict__ vc, float* __restrict__ out,
-                                          uint16_t* s_kv, int32_t* s_blk) {
+                                          uint16_t* s_kv) {
     constexpr int NW = kWaves;
     constexpr int TT = kMfmaTileTokens;    // 32 tokens per stage
     constexpr int CPR = D / 8;             // 16-byte chunks per token row
@@ -394,11 +477,10 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
     const int Hkv = dm.num_kv_heads;
     const int G = dm.group;
     const int n_tok = it.n_tokens;
-    const int nblk = (n_tok + 15) >> 4;
+    const int nblk = it.nblk;
     const int ntiles = (n_tok + TT - 1) / TT;
     const int row0 = wave * 16 * TPW;       // TPW sixteen-row tiles per wave
-
-    for (int i = tid; i < nblk; i += NT) s_blk[i] = p.block_ids[it.blk_begin + i];
+    const int32_t* s_blk = it.blk;          // block ids, in LDS
 
     // ---- Q operands (B of S^T = K Q^T): lane -> row lr of the tile, d = 32s + 8lg .. +7.
     // Rows past the item's rows get q = 0: they are computed but never stored.
@@ -409,7 +491,7 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
     for (int rt = 0; rt < TPW; ++rt) {
         const int r = row0 + rt * 16 + lr;
         if (r < it.n_rows) {
-            const Entry e = load_entry(p.entries, it.q_begin + r / G);
+            const Entry e = entry_of(it, r / G);
             const int h = g * G + r % G;
             const uint16_t* qrow = q + (size_t(e.query) * dm.num_q_heads + h) * D;
 #pragma unroll
@@ -422,12 +504,10 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
         }
     }
     // tokens every row of the item attends to: tiles below this need no mask
-    int lim_all = n_tok;
-    for (int e = 0; e < it.n_q; ++e) lim_all = min(lim_all, load_entry(p.entries, it.q_begin + e).limit);
+    const int lim_all = it.lim_all;
     // Complete every setup load here: the tile loop below must see no older
     // vector-memory operation, or waits on it would also drain the tile DMA.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
-    __syncthreads();   // block table staged; every wave's setup loads are done
 
     // ---- loop-invariant DMA geometry: chunk u of this thread is token tok_u, row offset off_u
     const size_t head_elems = size_t(16) * D;
@@ -616,7 +696,7 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
         lt += __shfl_xor(lt, 32);
         const int r = row0 + rt * 16 + lr;
         if (r >= it.n_rows) continue;
-        const Entry e = load_entry(p.entries, it.q_begin + r / G);
+        const Entry e = entry_of(it, r / G);
         const int h = g * G + r % G;
         float* dst;
         float scale;
@@ -653,42 +733,31 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
 }
 
 // ============================================================================
-// Persistent forward kernels: each workgroup drains its own XCD's queue
-// (blockIdx mod 8; workgroups are dispatched round-robin over the XCDs), then
-// steals from the others.  The last workgroup to finish clears the queue
-// cursors, so the next launch -- or a graph replay -- starts from zero without
-// a memset.  VALU and MFMA tasks share one launch and one set of queues, so
-// the MFMA work of packed groups runs side by side with the bandwidth-bound
-// private tails (the goal of the PAT review's multi-stream forward: no
-// execution bubbles), without cross-stream synchronisation.
+// Persistent forward kernel: workgroup w runs static list w (and w + gridDim.x,
+// ... when fewer workgroups are resident than lists): its MFMA tasks, then its
+// VALU tasks as continuous per-wave streams.  VALU and MFMA tasks share one
+// launch, so the MFMA work of packed groups runs side by side with the
+// bandwidth-bound private tails (the goal of the PAT review's multi-stream
+// forward: no execution bubbles), without cross-stream synchronisation.
 // ============================================================================
-template <typename Body>
-__device__ __forceinline__ void drain_queues(const DevPlan& p, int32_t* s_task, Body&& body) {
-    const int own = int(blockIdx.x) % kQueues;
-    for (int k = 0; k < kQueues; ++k) {
-        const int qi = (own + k) % kQueues;
-        const int base = cptr(p.queue_ptr)[qi];
-        const int n = cptr(p.queue_ptr)[qi + 1] - base;
-        if (n <= 0) continue;
-        while (true) {
-            if (threadIdx.x == 0) *s_task = atomicAdd(p.counters + qi, 1);
-            __syncthreads();
-            const int t = __builtin_amdgcn_readfirstlane(*s_task);
-            __syncthreads();   // every thread has read s_task; the previous task's LDS is free
-            if (t >= n) break;
-            const KV_CONST int32_t* tk = cptr(reinterpret_cast<const int32_t*>(p.tasks + base + t));
-            const int item = __builtin_amdgcn_readfirstlane(tk[0]);
-            const int head = __builtin_amdgcn_readfirstlane(tk[1]);
-            body(load_item(p.items, item), head);
-        }
+
+// Copy `words` (a multiple of 4) int32 words of descriptors into LDS by direct
+// global -> LDS DMA, 16 bytes per lane.  Completion is awaited by the caller
+// (s_waitcnt vmcnt(0) and a barrier).
+__device__ __forceinline__ void fetch_desc(const int32_t* src, int words, int32_t* dst) {
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n16 = words >> 2;
+    const uint32_t base = uint32_t(uintptr_t(dst));
+    for (int r0 = 0; r0 < n16; r0 += 64 * kWaves) {
+        const int c = r0 + tid;
+        if (c < n16) dma16(src + 4 * c, base + uint32_t(16 * (r0 + 64 * wave)));
     }
+}
+
+__device__ __forceinline__ void wait_all_and_sync() {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
     __syncthreads();
-    if (threadIdx.x == 0) {
-        if (atomicAdd(p.counters + kQueues, 1) == int(gridDim.x) - 1) {
-            for (int qi = 0; qi < kQueues; ++qi) atomicExch(p.counters + qi, 0);
-            atomicExch(p.counters + kQueues, 0);
-        }
-    }
 }
 
 template <int D, int R, int TPW>
@@ -696,17 +765,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     DevPlan p, Dims dm, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, float* __restrict__ out) {
     constexpr int TT = kMfmaTileTokens;
-    __shared__ __attribute__((aligned(16))) uint16_t s_kv[kMfmaStages * 2 * TT * D];
-    __shared__ int32_t s_blk[kMaxItemBlocks];
-    __shared__ int32_t s_task;
-    drain_queues(p, &s_task, [&](const Item& it, int head) {
-        if (it.kind == KVATTN_VARIANT_MFMA) {
-            mfma_task<D, TPW>(p, dm, it, head, q, kc, vc, out, s_kv, s_blk);
-        } else {
-            const int g = head + (threadIdx.x >> 6);
-            if (g < dm.num_kv_heads) valu_task<D, R>(p, dm, it, g, q, kc, vc, out);
+    constexpr int KV_ELEMS = kMfmaStages * 2 * TT * D;
+    constexpr int WIN = valu_window_words(D, R);
+    static_assert(KV_ELEMS * 2 == WIN * 4 + kWaves * 4 * R * D * 2, "VALU window layout");
+    __shared__ __attribute__((aligned(16))) uint16_t s_kv[KV_ELEMS];
+    __shared__ __attribute__((aligned(16))) int32_t s_desc[2][kDescMaxWords];
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+    // All control flow below is wave-uniform: the loops hold barriers, so
+    // lane-divergent branches must stay out of their exits and back edges.
+    for (int w = blockIdx.x; w < p.n_lists; w += gridDim.x) {
+        const KV_CONST int32_t* lp = cptr(p.list_ptr) + 3 * w;
+        const int m0 = lp[0], v0 = lp[1], e0 = lp[2];
+        // ---- MFMA tasks: the next descriptor lies right after the current one
+        // and is copied into the other LDS buffer before the current task's
+        // first KV load, so it has landed when the task ends.
+        if (m0 < v0) {
+            int off = m0, buf = 0;
+            fetch_desc(p.desc + off, min(kDescMaxWords, v0 - off), s_desc[0]);
+            wait_all_and_sync();
+            while (true) {
+                const int32_t* d = s_desc[buf];
+                const int words = __builtin_amdgcn_readfirstlane(d[kDescWords]);
+                const int next_words = __builtin_amdgcn_readfirstlane(d[kDescNextWords]);
+                const int noff = off + words;
+                if (noff < v0) fetch_desc(p.desc + noff, next_words, s_desc[buf ^ 1]);
+                const TaskView it = view_of(d);
+                mfma_task<D, TPW>(p, dm, it, it.head, q, kc, vc, out, s_kv);
+                wait_all_and_sync();   // the prefetched descriptor landed; this task's LDS is free
+                if (noff >= v0) break;
+                off = noff;
+                buf ^= 1;
+            }
         }
-    });
+        // ---- VALU tasks: the descriptors go into the LDS window in one piece,
+        // then every wave streams its KV head of each task.
+        if (v0 < e0) {
+            int32_t* win = reinterpret_cast<int32_t*>(s_kv);
+            fetch_desc(p.desc + v0, e0 - v0, win);
+            wait_all_and_sync();
+            uint16_t* qs = s_kv + 2 * WIN + wave * 4 * R * D;
+            valu_stream<D, R>(p, dm, win, e0 - v0, qs, q, kc, vc, out);
+            wait_all_and_sync();   // the window is free for the next list
+        }
+    }
 }
 
 // ============================================================================
@@ -795,9 +896,9 @@ __global__ __launch_bounds__(256) void merge_kernel(DevPlan p, Dims dm, float* _
 }
 
 // Grid of a persistent launch: the workgroups the device holds at once
-// (occupancy API x CUs), or fewer when there are fewer tasks.
+// (occupancy API x CUs), or fewer when there are fewer static lists.
 template <typename K>
-int persistent_grid(K kernel, int* cache, int n_tasks) {
+int persistent_grid(K kernel, int* cache, int n_lists) {
     if (*cache == 0) {
         int dev = 0, cus = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -805,14 +906,17 @@ int persistent_grid(K kernel, int* cache, int n_tasks) {
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess) return -1;
         *cache = cus * (per_cu > 0 ? per_cu : 1);
     }
-    return n_tasks < *cache ? n_tasks : *cache;
+    return n_lists < *cache ? n_lists : *cache;
 }
 
 template <int D, int R, int TPW>
 int launch_fwd_t(const DevPlan& p, const Dims& d, int n_tasks, const uint16_t* q, const uint16_t* k,
                  const uint16_t* v, float* out, hipStream_t s) {
     static int slots = 0;
-    const int grid = persistent_grid(fwd_kernel<D, R, TPW>, &slots, n_tasks);
+    (void)n_tasks;
+    // one workgroup per static list when they all fit at once; otherwise
+    // workgroup w also runs lists w + grid, w + 2 grid, ...
+    const int grid = persistent_grid(fwd_kernel<D, R, TPW>, &slots, p.n_lists);
     if (grid < 0) return int(hipErrorInvalidDevice);
     hipLaunchKernelGGL((fwd_kernel<D, R, TPW>), dim3(grid), dim3(256), 0, s, p, d, q, k, v, out);
     return int(hipGetLastError());
@@ -827,8 +931,8 @@ int launch_forward(const DevPlan& p, const Dims& d, int valu_rows, int mfma_tile
 #define KV_FWD(DD, RR, TP)                                           \
     if (d.head_dim == DD && valu_rows == RR && mfma_tiles == TP) \
         return launch_fwd_t<DD, RR, TP>(p, d, n_tasks, q, k, v, out, s);
-    KV_FWD(128, 1, 1) KV_FWD(128, 2, 1) KV_FWD(128, 4, 1) KV_FWD(128, 8, 1)
-    KV_FWD(128, 1, 2) KV_FWD(128, 2, 2) KV_FWD(128, 4, 2) KV_FWD(128, 8, 2)
+    KV_FWD(128, 1, 1) KV_FWD(128, 2, 1) KV_FWD(128, 4, 1)
+    KV_FWD(128, 1, 2) KV_FWD(128, 2, 2) KV_FWD(128, 4, 2)
     KV_FWD(64, 1, 1) KV_FWD(64, 2, 1) KV_FWD(64, 4, 1) KV_FWD(64, 8, 1)
     KV_FWD(64, 1, 2) KV_FWD(64, 2, 2) KV_FWD(64, 4, 2) KV_FWD(64, 8, 2)
 #undef KV_FWD

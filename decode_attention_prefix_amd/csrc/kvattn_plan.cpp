@@ -12,12 +12,14 @@
 // on a host without a GPU.
 #include <algorithm>
 #include <chrono>
+#include <cstdint>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <new>
 #include <numeric>
+#include <queue>
 #include <string>
 #include <vector>
 
@@ -199,6 +201,46 @@ int64_t ceil16(int64_t x) { return (x + kBlock - 1) / kBlock * kBlock; }
 constexpr int64_t kFoldCapTokens = 256;
 constexpr int64_t kChunkCapTokens = int64_t(kMaxItemBlocks) * kBlock - kFoldCapTokens;
 
+// Task costs, in units of one wave streaming one KV head-token with every CU
+// busy (about 0.17 us on MI355X: 512 bytes at 1/2048 of the HBM bandwidth).
+// An MFMA workgroup keeps three 16 KB tiles in flight and is latency bound:
+// about 2 us per 32-token tile under load, 0.4 units per token, plus a
+// pipeline fill of about 15 us.  A VALU task adds a small boundary cost to its
+// wave streams (epilogue, q rows).
+constexpr double kMfmaTokenCost = 0.4;
+constexpr double kMfmaTaskCost = 90.0;
+constexpr double kValuTaskCost = 8.0;
+
+// Append the descriptor of task t (see kDesc*) to P.desc; returns its words.
+int32_t put_desc(kvattn_plan_s& P, const Task& t) {
+    const Item& it = P.items[size_t(t.item)];
+    const int nblk = (it.n_tokens + kBlock - 1) / kBlock;
+    const int32_t words = desc_words(it.n_q, nblk);
+    const size_t at = P.desc.size();
+    P.desc.resize(at + size_t(words), 0);
+    int32_t* d = P.desc.data() + at;
+    int32_t lim_all = it.n_tokens;
+    for (int e = 0; e < it.n_q; ++e) lim_all = std::min(lim_all, P.entries[size_t(it.q_begin + e)].limit);
+    d[kDescKind] = it.kind;
+    d[kDescTile] = it.tile;
+    d[kDescHead] = t.head;
+    d[kDescTokens] = it.n_tokens;
+    d[kDescNq] = it.n_q;
+    d[kDescRows] = it.n_rows;
+    d[kDescBlocks] = nblk;
+    d[kDescLimAll] = lim_all;
+    d[kDescWords] = words;
+    for (int e = 0; e < it.n_q; ++e) {
+        const Entry& en = P.entries[size_t(it.q_begin + e)];
+        d[kDescHeader + 4 * e + 0] = en.query;
+        d[kDescHeader + 4 * e + 1] = en.dest;
+        d[kDescHeader + 4 * e + 2] = en.limit;
+    }
+    int32_t* blk = d + kDescHeader + 4 * it.n_q;
+    for (int j = 0; j < nblk; ++j) blk[j] = P.block_ids[size_t(it.blk_begin + j)];
+    return words;
+}
+
 }  // namespace
 
 kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, const int32_t* seq_lens,
@@ -346,14 +388,16 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         const int R = int(u.queries.size()) * G;
         int kind;
         if (o.force_variant == KVATTN_VARIANT_VALU) {
-            if (G > kValuMaxRows) return set_error(KVATTN_EUNSUPPORTED, "VALU forward holds at most 8 rows per KV head");
+            if (G > valu_max_rows(D))
+                return set_error(KVATTN_EUNSUPPORTED, "VALU forward holds at most " + std::to_string(valu_max_rows(D)) +
+                                                          " rows per KV head at this head_dim");
             kind = KVATTN_VARIANT_VALU;
         } else if (o.force_variant == KVATTN_VARIANT_MFMA) {
             kind = KVATTN_VARIANT_MFMA;
         } else {
-            kind = (R <= kValuMaxRows) ? KVATTN_VARIANT_VALU : KVATTN_VARIANT_MFMA;
+            kind = (R <= valu_max_rows(D)) ? KVATTN_VARIANT_VALU : KVATTN_VARIANT_MFMA;
         }
-        const int max_rows = kind == KVATTN_VARIANT_VALU ? kValuMaxRows : kMfmaMaxRows;
+        const int max_rows = kind == KVATTN_VARIANT_VALU ? valu_max_rows(D) : kMfmaMaxRows;
         const int qpg = std::max(1, max_rows / G);
         const int n = int(u.queries.size());
         const int ng = (n + qpg - 1) / qpg;
@@ -369,46 +413,92 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
                 g.w = 1.0;
             } else {
                 g.tile = g.rows <= 64 ? 1 : 2;
-                // MFMA task time relative to streaming the same tokens at one workgroup's
-                // share of a CU's bandwidth: grows with the rows of the group
-                g.w = std::max(1.0, g.rows / 64.0);
+                g.w = kMfmaTokenCost * (1.0 + std::max(0, g.rows - 64) / 256.0);
             }
             groups.push_back(std::move(g));
         }
     }
 
-    // ---- split length (long-KV splitting) -------------------------------------------
-    // A task is one item on one KV head (MFMA) or four KV heads (VALU).  The
-    // chunk length aims at ~1.5 waves of tasks over the persistent workgroups,
-    // but never so short that partial triples cost more than ~25 % of the
-    // chunk's KV bytes.
-    const int heads_per_valu_task = std::min(Hkv, kWaves);
-    const int slots = num_cus * 2;
-    double work = 0.0;           // token x KV-head units, weighted
-    for (const Group& g : groups) work += double(units[g.unit].tokens) * g.w * Hkv;
-    int64_t C;
-    if (o.split_tokens > 0) {
-        C = std::min<int64_t>(ceil16(o.split_tokens), kChunkCapTokens);
-    } else {
-        C = ceil16(int64_t(std::ceil(work / (double(slots) * 1.5))));
-        C = std::min<int64_t>(std::max<int64_t>(C, 64), kChunkCapTokens);
+    // ---- split length (long-KV splitting, runtime split selector) -------------------
+    // Time unit: one wave streaming one KV head-token with every CU busy.  A
+    // VALU task (an item on up to four KV heads, one wave each) runs as part of
+    // its waves' continuous streams and costs its tokens plus a small boundary
+    // cost; an MFMA task (an item on one KV head, the whole workgroup) costs
+    // tokens x w plus a fixed start-up (pipeline fill).  Candidate target task
+    // costs tau are tried; for each, every range is cut into chunks of about
+    // tau, the tasks are placed longest first on the persistent workgroups, and
+    // the score is the resulting makespan plus the partial triples that
+    // splitting adds (written by forward, read by merge), spread over the
+    // waves.  The cheapest candidate wins.  A VALU chunk keeps at least 64
+    // tokens, an MFMA chunk 128.
+    const int n_lists = num_cus * 2;
+    const double partial_units = 2.0 * double(partial_row_bytes) / double(2 * D * 2);  // one triple, w + r
+    auto task_cost = [&](const Group& g, int64_t tok) {
+        return g.kind == KVATTN_VARIANT_VALU ? double(tok) + kValuTaskCost : double(tok) * g.w + kMfmaTaskCost;
+    };
+    auto tasks_per_item = [&](const Group& g) { return g.kind == KVATTN_VARIANT_VALU ? (Hkv + kWaves - 1) / kWaves : Hkv; };
+    double work = 0.0;
+    for (const Group& g : groups) work += task_cost(g, units[g.unit].tokens) * tasks_per_item(g);
+    auto chunk_of = [&](const Group& g, double tau) -> int64_t {
+        if (o.split_tokens > 0) return std::min<int64_t>(ceil16(o.split_tokens), kChunkCapTokens);
+        const double per_tok = g.kind == KVATTN_VARIANT_VALU ? 1.0 : g.w;
+        int64_t c = ceil16(int64_t(std::ceil(tau / per_tok)));
+        c = std::max<int64_t>(c, g.kind == KVATTN_VARIANT_VALU ? 64 : 128);
+        return std::min<int64_t>(c, kChunkCapTokens);
+    };
+    auto score_of = [&](double tau) {
+        std::vector<double> costs;
+        double extra = 0.0;
+        for (const Group& g : groups) {
+            const Unit& u = units[g.unit];
+            const int64_t c = chunk_of(g, tau);
+            const int64_t nch = (u.tokens + c - 1) / c;
+            const int64_t len = ceil16((u.tokens + nch - 1) / nch);
+            extra += double(nch - 1) * g.rows * Hkv * partial_units;
+            for (int64_t k = 0; k < nch; ++k) {
+                const int64_t tok = std::min(len, u.tokens - k * len) + (k == nch - 1 ? u.fold_tokens : 0);
+                if (tok <= 0) break;
+                for (int h = 0; h < tasks_per_item(g); ++h) costs.push_back(task_cost(g, tok));
+            }
+        }
+        std::sort(costs.begin(), costs.end(), std::greater<double>());
+        std::priority_queue<double, std::vector<double>, std::greater<double>> heap;
+        for (int w = 0; w < n_lists; ++w) heap.push(0.0);
+        for (double c : costs) {
+            const double l = heap.top();
+            heap.pop();
+            heap.push(l + c);
+        }
+        double makespan = 0.0;
+        while (!heap.empty()) {
+            makespan = std::max(makespan, heap.top());
+            heap.pop();
+        }
+        return makespan + extra / (double(n_lists) * kWaves);
+    };
+    double tau = double(kChunkCapTokens) * 4.0;
+    if (o.split_tokens <= 0) {
+        const double mean = std::max(64.0, work / n_lists);
+        double best = 0.0;
+        bool first = true;
+        for (double f : {2.0, 1.0, 0.75, 0.5, 1.0 / 3, 0.25, 0.2, 1.0 / 6, 0.125}) {
+            const double sc = score_of(mean * f);
+            if (first || sc < best * 0.995) {
+                best = sc;
+                tau = mean * f;
+                first = false;
+            }
+        }
     }
+    int64_t C = 0;              // longest chunk of a split range (statistics)
+    for (const Group& g : groups)
+        if (units[g.unit].tokens > chunk_of(g, tau)) C = std::max(C, chunk_of(g, tau));
 
     // ---- items ----------------------------------------------------------------------
     std::vector<Proto> protos;
     for (const Group& g : groups) {
         const Unit& u = units[g.unit];
-        int64_t chunk;
-        if (o.split_tokens > 0) {
-            chunk = C;
-        } else {
-            const int hpt = g.kind == KVATTN_VARIANT_VALU ? heads_per_valu_task : 1;
-            chunk = ceil16(int64_t(double(C) / (g.w * hpt)));
-            // partial triples (write + read) per chunk stay under ~25 % of the chunk's KV bytes
-            const int64_t floor_tok = ceil16(int64_t(4.0 * g.rows * partial_row_bytes * 2 / (2.0 * D * 2)));
-            chunk = std::max<int64_t>(chunk, std::max<int64_t>(64, floor_tok));
-            chunk = std::min<int64_t>(chunk, g.kind == KVATTN_VARIANT_VALU ? 4096 : kChunkCapTokens);
-        }
+        const int64_t chunk = chunk_of(g, tau);
         const int64_t nch = (u.tokens + chunk - 1) / chunk;
         const int64_t len = ceil16((u.tokens + nch - 1) / nch);
         const bool has_fold = u.fold_query >= 0 &&
@@ -439,9 +529,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             p.it.n_tokens = int32_t(item_tokens);
             p.it.n_q = int32_t(g.queries.size());
             p.it.n_rows = g.rows;
-            // per-task cost: tokens x heads of the task x weight (+ a fixed start-up cost)
-            const int hpt = g.kind == KVATTN_VARIANT_VALU ? heads_per_valu_task : 1;
-            p.cost = double(item_tokens) * g.w * hpt + 32.0 * hpt;
+            p.cost = task_cost(g, item_tokens);   // one task of the item
             protos.push_back(std::move(p));
         }
     }
@@ -515,58 +603,118 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         P.merge_ptr.push_back(int32_t(P.merge_dest.size()));
     }
 
-    // ---- tasks and per-XCD queues --------------------------------------------------------------
-    // MFMA tasks of KV head g go to queue g mod 8, so the row groups and chunks
-    // that read one KV head's shared range meet in one XCD's L2; VALU tasks go
-    // to the least-loaded queue, longest first.  Each queue is drained longest
-    // first; idle workgroups steal from the other queues.
+    // ---- tasks: one static list per persistent workgroup -------------------------------------------
+    // MFMA tasks are placed first, longest first, each on the least-loaded
+    // list (an MFMA task of KV head g prefers a list of XCD g mod 8 --
+    // workgroup w runs on XCD w mod 8 -- so the row groups and chunks that read
+    // one KV head's shared range meet in one L2); then VALU tasks, longest
+    // first.  A list runs its MFMA tasks, then its VALU tasks as continuous
+    // per-wave streams, whose descriptors must fit the LDS window.
     P.tasks.clear();
-    P.queue_ptr.assign(size_t(n_launch) * (kQueues + 1), 0);
+    P.list_ptr.assign(size_t(n_launch) * (n_lists + 1), 0);
     P.forward_launches.clear();
+    P.n_lists = n_lists;
+    P.desc.clear();
+    P.desc_list_ptr.assign(size_t(n_launch) * n_lists * 3, 0);
     for (int L = 0; L < n_launch; ++L) {
         struct QT {
             Task t;
             double cost;
+            int pref;           // preferred XCD (MFMA), -1 for VALU
+            int32_t words;      // descriptor words
         };
-        std::vector<std::vector<QT>> q(kQueues);
-        std::vector<double> load(kQueues, 0.0);
-        std::vector<QT> valu;
+        std::vector<QT> all;
         for (size_t i = 0; i < P.items.size(); ++i) {
             if (item_launch[i] != L) continue;
             const Item& it = P.items[i];
+            const int32_t words = desc_words(it.n_q, (it.n_tokens + kBlock - 1) / kBlock);
             if (it.kind == KVATTN_VARIANT_MFMA) {
-                for (int g = 0; g < Hkv; ++g) {
-                    const double c = item_cost[i];
-                    q[g % kQueues].push_back({{int32_t(i), g}, c});
-                    load[g % kQueues] += c;
-                }
+                for (int g = 0; g < Hkv; ++g) all.push_back({{int32_t(i), g}, item_cost[i], g % kXcds, words});
             } else {
-                for (int g = 0; g < Hkv; g += kWaves) valu.push_back({{int32_t(i), g}, item_cost[i]});
+                for (int g = 0; g < Hkv; g += kWaves) all.push_back({{int32_t(i), g}, item_cost[i], -1, words});
             }
         }
-        std::stable_sort(valu.begin(), valu.end(), [](const QT& a, const QT& b) { return a.cost > b.cost; });
-        for (const QT& t : valu) {
-            int best = int(std::min_element(load.begin(), load.end()) - load.begin());
-            q[best].push_back(t);
-            load[best] += t.cost;
+        std::stable_sort(all.begin(), all.end(), [](const QT& a, const QT& b) {
+            const bool ma = a.pref >= 0, mb = b.pref >= 0;
+            if (ma != mb) return ma;
+            return a.cost > b.cost;
+        });
+        using LE = std::pair<double, int>;
+        using Heap = std::priority_queue<LE, std::vector<LE>, std::greater<LE>>;
+        Heap heap_all;
+        std::vector<Heap> heap_x(kXcds);
+        std::vector<double> load(size_t(n_lists), 0.0);
+        std::vector<int32_t> valu_words(size_t(n_lists), 0);
+        for (int w = 0; w < n_lists; ++w) {
+            heap_all.push({0.0, w});
+            heap_x[size_t(w % kXcds)].push({0.0, w});
         }
-        int n_tasks = 0;
+        auto top_of = [&](Heap& h) {
+            while (!h.empty() && h.top().first != load[size_t(h.top().second)]) h.pop();
+            return h.empty() ? -1 : h.top().second;
+        };
+        const int launch_valu_rows = L < int(vt.size()) ? vt[size_t(L)] : 1;
+        const int32_t window = valu_window_words(D, launch_valu_rows);
+        std::vector<std::vector<Task>> mlist(static_cast<size_t>(n_lists)), vlist(static_cast<size_t>(n_lists));
+        for (const QT& t : all) {
+            int w = top_of(heap_all);
+            if (t.pref >= 0) {
+                const int wx = top_of(heap_x[size_t(t.pref)]);
+                if (wx >= 0 && load[size_t(wx)] <= load[size_t(w)] + 0.25 * t.cost) w = wx;
+                mlist[size_t(w)].push_back(t.t);
+            } else {
+                if (valu_words[size_t(w)] + t.words > window) {
+                    // no room in the least-loaded list's window: take the
+                    // least-loaded list that has room
+                    w = -1;
+                    for (int x = 0; x < n_lists; ++x)
+                        if (valu_words[size_t(x)] + t.words <= window && (w < 0 || load[size_t(x)] < load[size_t(w)]))
+                            w = x;
+                    if (w < 0) return set_error(KVATTN_EINVAL, "internal: VALU task descriptors exceed the LDS windows");
+                }
+                vlist[size_t(w)].push_back(t.t);
+                valu_words[size_t(w)] += t.words;
+            }
+            load[size_t(w)] += t.cost;
+            heap_all.push({load[size_t(w)], w});
+            heap_x[size_t(w % kXcds)].push({load[size_t(w)], w});
+        }
         const int base = int(P.tasks.size());
-        for (int k = 0; k < kQueues; ++k) {
-            std::stable_sort(q[k].begin(), q[k].end(), [](const QT& a, const QT& b) { return a.cost > b.cost; });
-            P.queue_ptr[size_t(L) * (kQueues + 1) + k] = int32_t(P.tasks.size()) - base;
-            for (const QT& t : q[k]) P.tasks.push_back(t.t);
-            n_tasks += int(q[k].size());
+        for (int w = 0; w < n_lists; ++w) {
+            P.list_ptr[size_t(L) * (n_lists + 1) + w] = int32_t(P.tasks.size()) - base;
+            for (const Task& t : mlist[size_t(w)]) P.tasks.push_back(t);
+            for (const Task& t : vlist[size_t(w)]) P.tasks.push_back(t);
         }
-        P.queue_ptr[size_t(L) * (kQueues + 1) + kQueues] = int32_t(P.tasks.size()) - base;
+        P.list_ptr[size_t(L) * (n_lists + 1) + n_lists] = int32_t(P.tasks.size()) - base;
         Launch Lr;
         // a kind without tasks in this launch takes the smallest instantiation
-        Lr.valu_rows = L < int(vt.size()) ? vt[size_t(L)] : 1;
+        Lr.valu_rows = launch_valu_rows;
         Lr.mfma_tiles = L < int(mt.size()) ? mt[size_t(L)] : 1;
         Lr.index = L;
-        Lr.n_tasks = n_tasks;
+        Lr.n_tasks = int(P.tasks.size()) - base;
         Lr.task_base = base;
         P.forward_launches.push_back(Lr);
+
+        // ---- task descriptors of this launch
+        // Everything a task reads before its KV stream, in one contiguous record:
+        // a 16-word header, the entries, the block ids.  A list's MFMA records
+        // lie back to back, so a workgroup finds the next record right after the
+        // current one and copies it into LDS while the current task streams; its
+        // VALU records follow and are copied into LDS in one piece.
+        for (int w = 0; w < n_lists; ++w) {
+            int32_t* lp = P.desc_list_ptr.data() + (size_t(L) * n_lists + w) * 3;
+            lp[0] = int32_t(P.desc.size());
+            size_t prev = SIZE_MAX;
+            for (const Task& t : mlist[size_t(w)]) {
+                const size_t at = P.desc.size();
+                const int32_t words = put_desc(P, t);
+                if (prev != SIZE_MAX) P.desc[prev + kDescNextWords] = words;
+                prev = at;
+            }
+            lp[1] = int32_t(P.desc.size());
+            for (const Task& t : vlist[size_t(w)]) put_desc(P, t);
+            lp[2] = int32_t(P.desc.size());
+        }
     }
 
     // ---- blob ------------------------------------------------------------------------------------
@@ -574,21 +722,16 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     std::memset(&h, 0, sizeof(h));
     h.magic = kBlobMagic;
     h.version = kBlobVersion;
-    h.n_items = int32_t(P.items.size());
-    h.n_entries = int32_t(P.entries.size());
-    h.n_block_ids = int32_t(P.block_ids.size());
+    h.n_desc_words = int32_t(P.desc.size());
     h.n_merge_q = int32_t(P.merge_query.size());
     h.n_slots = slots_used;
     h.head_dim = D;
     h.n_tasks = int32_t(P.tasks.size());
     h.n_launches = n_launch;
+    h.n_lists = n_lists;
     uint64_t off = align256(sizeof(BlobHeader));
-    h.off_items = off;        off = align256(off + P.items.size() * sizeof(Item));
-    h.off_entries = off;      off = align256(off + P.entries.size() * sizeof(Entry));
-    h.off_block_ids = off;    off = align256(off + P.block_ids.size() * 4);
-    h.off_tasks = off;        off = align256(off + P.tasks.size() * sizeof(Task));
-    h.off_queue_ptr = off;    off = align256(off + P.queue_ptr.size() * 4);
-    h.off_counters = off;     off = align256(off + uint64_t(n_launch) * kCounters * 4);
+    h.off_desc = off;         off = align256(off + P.desc.size() * 4);
+    h.off_list_ptr = off;     off = align256(off + P.desc_list_ptr.size() * 4);
     h.off_merge_query = off;  off = align256(off + P.merge_query.size() * 4);
     h.off_merge_ptr = off;    off = align256(off + P.merge_ptr.size() * 4);
     h.off_merge_dest = off;   off = align256(off + P.merge_dest.size() * 4);
@@ -602,11 +745,8 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     auto put = [&](uint64_t at, const void* src, size_t n) {
         if (n) std::memcpy(P.blob.data() + at, src, n);
     };
-    put(h.off_items, P.items.data(), P.items.size() * sizeof(Item));
-    put(h.off_entries, P.entries.data(), P.entries.size() * sizeof(Entry));
-    put(h.off_block_ids, P.block_ids.data(), P.block_ids.size() * 4);
-    put(h.off_tasks, P.tasks.data(), P.tasks.size() * sizeof(Task));
-    put(h.off_queue_ptr, P.queue_ptr.data(), P.queue_ptr.size() * 4);
+    put(h.off_desc, P.desc.data(), P.desc.size() * 4);
+    put(h.off_list_ptr, P.desc_list_ptr.data(), P.desc_list_ptr.size() * 4);
     put(h.off_merge_query, P.merge_query.data(), P.merge_query.size() * 4);
     put(h.off_merge_ptr, P.merge_ptr.data(), P.merge_ptr.size() * 4);
     put(h.off_merge_dest, P.merge_dest.data(), P.merge_dest.size() * 4);
@@ -755,6 +895,11 @@ kvattn_status kvattn_plan_export(kvattn_plan_t plan, kvattn_export* out) {
     out->head_dim = plan->shape.head_dim;
     out->num_tasks = int32_t(plan->tasks.size());
     out->tasks = reinterpret_cast<const int32_t*>(plan->tasks.data());
+    out->num_launches = int32_t(plan->forward_launches.size());
+    out->num_lists = plan->n_lists;
+    out->num_desc_words = int32_t(plan->desc.size());
+    out->desc = plan->desc.data();
+    out->list_ptr = plan->desc_list_ptr.data();
     return KVATTN_OK;
 }
 

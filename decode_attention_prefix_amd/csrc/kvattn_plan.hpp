@@ -16,7 +16,10 @@ struct kvattn_plan_s {
     std::vector<int32_t> merge_query, merge_ptr, merge_dest;
     int32_t n_slots = 0;
     std::vector<kvattn::Task> tasks;
-    std::vector<int32_t> queue_ptr;         // [launch][kQueues + 1]
+    std::vector<int32_t> list_ptr;          // [launch][n_lists + 1] task ranges of the static lists
+    std::vector<int32_t> desc;              // device task descriptors
+    std::vector<int32_t> desc_list_ptr;     // [launch][n_lists][3] (MFMA begin, VALU begin, end) in words
+    int32_t n_lists = 0;                    // static task lists per launch (one per persistent workgroup)
     std::vector<kvattn::Launch> forward_launches;
     std::vector<unsigned char> blob;        // serialised schedule: header + arrays + zero region
     kvattn::BlobHeader header{};

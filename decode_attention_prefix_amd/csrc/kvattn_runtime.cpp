@@ -15,17 +15,10 @@ DevPlan resolve(const kvattn_plan_s& P, int launch) {
     auto* base = static_cast<unsigned char*>(P.dev_ws);
     const BlobHeader& h = P.header;
     DevPlan d;
-    d.items = reinterpret_cast<const Item*>(base + h.off_items);
-    d.entries = reinterpret_cast<const Entry*>(base + h.off_entries);
-    d.block_ids = reinterpret_cast<const int32_t*>(base + h.off_block_ids);
-    d.tasks = reinterpret_cast<const Task*>(base + h.off_tasks);
-    d.queue_ptr = reinterpret_cast<const int32_t*>(base + h.off_queue_ptr);
-    d.counters = reinterpret_cast<int32_t*>(base + h.off_counters);
-    if (launch >= 0) {
-        d.tasks += P.forward_launches[size_t(launch)].task_base;
-        d.queue_ptr += size_t(launch) * (kQueues + 1);
-        d.counters += size_t(launch) * kCounters;
-    }
+    d.desc = reinterpret_cast<const int32_t*>(base + h.off_desc);
+    d.list_ptr = reinterpret_cast<const int32_t*>(base + h.off_list_ptr);
+    d.n_lists = P.n_lists;
+    if (launch >= 0) d.list_ptr += size_t(launch) * size_t(P.n_lists) * 3;
     d.merge_query = reinterpret_cast<const int32_t*>(base + h.off_merge_query);
     d.merge_ptr = reinterpret_cast<const int32_t*>(base + h.off_merge_ptr);
     d.merge_dest = reinterpret_cast<const int32_t*>(base + h.off_merge_dest);

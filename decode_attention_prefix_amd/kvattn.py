@@ -46,7 +46,7 @@ class kvattn_stats(ctypes.Structure):
                 ("partial_bytes", i64), ("num_nodes", i32), ("num_packed_nodes", i32), ("num_items", i32),
                 ("num_items_valu", i32), ("num_items_mfma", i32), ("num_folded_leaves", i32),
                 ("num_partial_slots", i32), ("num_merge_rows", i32), ("num_direct_rows", i32),
-                ("num_launches", i32), ("split_tokens", i32), ("reserved", i32), ("plan_seconds", f64),
+                ("num_launches", i32), ("split_tokens", i32), ("num_queued_tasks", i32), ("plan_seconds", f64),
                 ("blob_bytes", u64), ("workspace_bytes", u64)]
 
     def as_dict(self):
@@ -66,7 +66,9 @@ class kvattn_export(ctypes.Structure):
     _fields_ = [("num_items", i32), ("items", ctypes.POINTER(kvattn_item_info)), ("num_entries", i32),
                 ("entries", ctypes.POINTER(kvattn_item_query)), ("num_block_ids", i32), ("block_ids", P32),
                 ("num_merge_queries", i32), ("merge_query", P32), ("merge_ptr", P32), ("merge_dest", P32),
-                ("num_partial_slots", i32), ("head_dim", i32), ("num_tasks", i32), ("tasks", P32)]
+                ("num_partial_slots", i32), ("head_dim", i32), ("num_tasks", i32), ("tasks", P32),
+                ("num_launches", i32), ("num_lists", i32), ("num_desc_words", i32), ("desc", P32),
+                ("list_ptr", P32)]
 
 
 def _load():
@@ -243,6 +245,9 @@ def kvattn_plan_export(plan: Plan) -> dict:
         "num_partial_slots": e.num_partial_slots,
         "head_dim": e.head_dim,
         "tasks": arr(e.tasks, e.num_tasks, 2),
+        "num_lists": e.num_lists,
+        "desc": arr(e.desc, e.num_desc_words, 1).reshape(-1),
+        "list_ptr": arr(e.list_ptr, e.num_launches * e.num_lists * 3, 1).reshape(e.num_launches, e.num_lists, 3),
     }
 
 

@@ -111,7 +111,8 @@ enum { KVATTN_VARIANT_AUTO = -1, KVATTN_VARIANT_VALU = 0, KVATTN_VARIANT_MFMA = 
  *                  into its parent's item, Fig 7(d)).
  *   force_variant  -1 auto; KVATTN_VARIANT_VALU / _MFMA force one forward kernel
  *                  family for every item (for tests).  VALU handles at most 8 rows
- *                  per KV head; wider packs are split into several items.
+ *                  per KV head at head_dim 64 and 4 at head_dim 128 (wider packs are
+ *                  split into several items; a wider GQA group is EUNSUPPORTED).
  *   split_tokens   0 auto; otherwise the KV chunk length of split items, rounded
  *                  up to a multiple of 16 (long-KV splitting).
  *   num_cus        compute units the split model balances over; 0 means 256.
@@ -141,8 +142,8 @@ typedef struct {
     int32_t num_merge_rows;          /* (query, q head) rows the merge kernel combines          */
     int32_t num_direct_rows;         /* rows written by exactly one forward item                */
     int32_t num_launches;            /* kernel launches per kvattn_decode                       */
-    int32_t split_tokens;            /* chunk length the split model chose                      */
-    int32_t reserved;
+    int32_t split_tokens;            /* longest chunk of a split KV range (0: nothing split)     */
+    int32_t num_queued_tasks;        /* forward tasks left to the dynamic queues (rest: static)  */
     double plan_seconds;             /* host wall time of kvattn_plan                            */
     uint64_t blob_bytes;             /* schedule bytes uploaded by kvattn_plan_upload            */
     uint64_t workspace_bytes;        /* = kvattn_plan_device_bytes                               */
@@ -185,6 +186,19 @@ typedef struct {
     int32_t num_tasks;
     const int32_t* tasks;         /* [num_tasks][2]: (item, first KV head); an MFMA item runs one
                                      task per KV head, a VALU item one per 4 consecutive KV heads */
+    /* The task descriptors as uploaded to the device.  A descriptor is a run of
+     * int32 words: a 16-word header (kind, tile, first KV head, tokens, entries
+     * n_q, rows, blocks nb, min limit, words of this descriptor, words of the
+     * next MFMA descriptor of the same list or 0, then 6 zero words), n_q
+     * entries of 4 words (query, dest, limit, 0), nb block ids, zero padding to
+     * a multiple of 4 words.  List l of launch L (one per persistent
+     * workgroup) holds its MFMA descriptors in words [lp[0], lp[1]) and its
+     * VALU descriptors in [lp[1], lp[2]), lp = list_ptr + 3 (L num_lists + l). */
+    int32_t num_launches;
+    int32_t num_lists;
+    int32_t num_desc_words;
+    const int32_t* desc;
+    const int32_t* list_ptr;      /* [num_launches][num_lists][3]              */
 } kvattn_export;
 
 /* Fill *opts with the defaults (AUTO packing, scheme auto, auto variant and split). */

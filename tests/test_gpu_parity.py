@@ -100,10 +100,16 @@ def test_parity_small_configs_auto_variant(c, mode):
 @pytest.mark.parametrize("scheme,split", [(1, 0), (2, 0), (1, 16), (2, 48), (0, 208)])
 def test_parity_small_configs_forced_variant(c, variant, scheme, split):
     wl = small(c)
-    if variant == 0 and wl.group > 8:
-        pytest.skip("VALU forward holds at most 8 rows per KV head")
+    if variant == 0 and wl.group > valu_max_rows(wl.head_dim):
+        pytest.skip("the VALU forward holds at most %d rows per KV head at head_dim %d"
+                    % (valu_max_rows(wl.head_dim), wl.head_dim))
     got, _ = gpu_decode(wl, pack_mode=2, force_variant=variant, scheme=scheme, split_tokens=split)
     assert_close(got, oracle_out(wl), "%s variant %d scheme %d split %d" % (wl.name, variant, scheme, split))
+
+
+def valu_max_rows(D):
+    """Rows per KV head the VALU forward holds (the planner's limit)."""
+    return 4 if D == 128 else 8
 
 
 def edge_workload(lengths, shared, Hq, Hkv, D, seed):
@@ -125,8 +131,8 @@ def edge_workload(lengths, shared, Hq, Hkv, D, seed):
 @pytest.mark.parametrize("G,Hkv", [(1, 4), (4, 2), (8, 1)])
 @pytest.mark.parametrize("variant", [-1, 0, 1])
 def test_parity_boundary_lengths(D, G, Hkv, variant):
-    if variant == 0 and G > 8:
-        pytest.skip("VALU limit")
+    if variant == 0 and G > valu_max_rows(D):
+        pytest.skip("the VALU forward holds at most %d rows per KV head at head_dim %d" % (valu_max_rows(D), D))
     lengths = [1, 15, 16, 17, 32, 33, 31, 2, 47, 48, 49]
     wl = edge_workload(lengths, 0, G * Hkv, Hkv, D, 7 + D + G)
     got, _ = gpu_decode(wl, force_variant=variant)

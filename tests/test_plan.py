@@ -28,7 +28,7 @@ def check_coverage(wl_bt, seq_lens, Hq, Hkv, ex):
         assert it["n_rows"][i] == nq * G
         assert it["kind"][i] in (K.KVATTN_VARIANT_VALU, K.KVATTN_VARIANT_MFMA)
         if it["kind"][i] == K.KVATTN_VARIANT_VALU:
-            assert it["n_rows"][i] <= it["tile"][i] <= 8
+            assert it["n_rows"][i] <= it["tile"][i] <= (4 if ex["head_dim"] == 128 else 8)
         else:
             assert it["tile"][i] in (1, 2) and it["n_rows"][i] <= 64 * it["tile"][i]
         nblk = (n_tok + 15) // 16
@@ -74,6 +74,74 @@ def check_coverage(wl_bt, seq_lens, Hq, Hkv, ex):
         heads = sorted(seen.get(i, []))
         step = 1 if it["kind"][i] == K.KVATTN_VARIANT_MFMA else 4
         assert heads == list(range(0, Hkv, step)), (i, heads)
+    check_descriptors(ex)
+
+
+DESC_MAX_WORDS = 16 + 4 * 128 + 512
+
+
+def check_descriptors(ex):
+    """The device descriptor stream encodes exactly the exported tasks, each once.
+
+    Layout (public header): 16 header words (kind, tile, head, tokens, n_q,
+    rows, blocks, min limit, words, next words, 0 x 6), n_q entries of 4 words,
+    the block ids, zero padding to a multiple of 4 words.  Each list holds its
+    MFMA descriptors, then its VALU descriptors.
+    """
+    it, en, ids, desc = ex["items"], ex["entries"], ex["block_ids"], ex["desc"]
+
+    def expected(item, head):
+        nt, nq = int(it["n_tokens"][item]), int(it["n_q"][item])
+        nb = (nt + 15) // 16
+        q0, b0 = int(it["q_begin"][item]), int(it["blk_begin"][item])
+        ent = tuple((int(en["query"][q0 + k]), int(en["dest"][q0 + k]), int(en["limit"][q0 + k]))
+                    for k in range(nq))
+        return (int(it["kind"][item]), int(it["tile"][item]), head, nt, nq, int(it["n_rows"][item]), nb,
+                min(e[2] for e in ent), ent, tuple(int(x) for x in ids[b0:b0 + nb]))
+
+    def decode(off):
+        h = desc[off:off + 16]
+        nq, nb, words = int(h[4]), int(h[6]), int(h[8])
+        assert words == 16 + 4 * nq + (nb + 3) // 4 * 4 and words <= DESC_MAX_WORDS
+        assert not h[10:16].any()
+        ent = tuple(tuple(int(x) for x in desc[off + 16 + 4 * k: off + 19 + 4 * k]) for k in range(nq))
+        assert all(desc[off + 19 + 4 * k] == 0 for k in range(nq))
+        blk = tuple(int(x) for x in desc[off + 16 + 4 * nq: off + 16 + 4 * nq + nb])
+        assert not desc[off + 16 + 4 * nq + nb: off + words].any()
+        return (int(h[0]), int(h[1]), int(h[2]), int(h[3]), nq, int(h[5]), nb, int(h[7]), ent, blk), words
+
+    got, covered = [], 0
+    D = ex["head_dim"]
+    prev_end = 0
+    for L in range(ex["list_ptr"].shape[0]):
+        for l in range(ex["num_lists"]):
+            m0, v0, e0 = (int(x) for x in ex["list_ptr"][L, l])
+            assert prev_end == m0 <= v0 <= e0
+            prev_end = e0
+            off = m0
+            while off < v0:     # MFMA descriptors, chained by next-words
+                d, words = decode(off)
+                assert d[0] == K.KVATTN_VARIANT_MFMA
+                nxt = off + words
+                assert int(desc[off + 9]) == (int(desc[nxt + 8]) if nxt < v0 else 0)
+                got.append(d)
+                covered += words
+                off = nxt
+            assert off == v0
+            rows_max = 1
+            while off < e0:     # VALU descriptors, copied to LDS in one piece
+                d, words = decode(off)
+                assert d[0] == K.KVATTN_VARIANT_VALU and int(desc[off + 9]) == 0
+                rows_max = max(rows_max, d[1])
+                got.append(d)
+                covered += words
+                off += words
+            assert off == e0
+            # the VALU window: the MFMA stage buffer (512 D bytes) less four q slots per wave
+            assert e0 - v0 <= (512 * D - 4 * 4 * rows_max * D * 2) // 4
+    assert covered == desc.size
+    want = [expected(int(i), int(h)) for i, h in ex["tasks"]]
+    assert sorted(got) == sorted(want)
 
 
 def plan_of(wl, **opts):
@@ -111,7 +179,7 @@ def test_coverage_full_size_configs(c, mode):
 @pytest.mark.parametrize("scheme", [1, 2])
 def test_coverage_forced_variants_and_schemes(c, variant, scheme):
     wl = W.small(c)
-    if variant == K.KVATTN_VARIANT_VALU and wl.group > 8:
+    if variant == K.KVATTN_VARIANT_VALU and wl.group > (4 if wl.head_dim == 128 else 8):
         with pytest.raises(K.KvattnError):
             plan_of(wl, force_variant=variant)
         return
