@@ -1,21 +1,22 @@
 // gfx950 (MI355X) kernels of the forward and merge stages.
 //
 // Forward (PAT review, forward stage: multi-tile kernels picked per work item,
-// long KV split into chunks, several kernels kept busy at once to cut
-// bubbles): one persistent launch whose workgroups pull tasks from per-XCD
-// queues.  A task is one item (a run of paged KV blocks and the query rows
-// attending to it) on one KV head (MFMA path) or four KV heads (VALU path); it
-// yields either final output rows or partial triples (m, l, acc), m in log2
-// units.
-//   * VALU path -- at most 8 rows per KV head (a single query's GQA group, or a
-//                  few queries of a small pack).  Bandwidth bound: q K^T with
-//                  v_dot2_f32_bf16, p V with fp32 FMAs, 16-byte coalesced loads
-//                  straight into registers, 8-lane DPP reductions.
+// long KV split into chunks, no execution bubbles): one persistent launch;
+// workgroup w runs the static task list the planner built for it.  A task is
+// one item (a run of paged KV blocks and the query rows attending to it) on
+// one KV head (MFMA path) or four KV heads (VALU path); it yields either final
+// output rows or partial triples (m, l, acc), m in log2 units.
 //   * MFMA path -- packed groups (up to 128 rows per KV head): S^T = K Q^T and
 //                  O^T = V^T P^T on v_mfma_f32_16x16x32_bf16, K/V tiles staged
 //                  in LDS by direct global->LDS DMA, three stages deep.
+//   * VALU path -- at most 4 (D = 128) or 8 (D = 64) rows per KV head: a
+//                  query's GQA group or a few queries of a small pack.
+//                  Bandwidth bound: q K^T with v_dot2_f32_bf16, p V with fp32
+//                  FMAs, 16-byte coalesced loads into a register ring that
+//                  runs across the list's tasks, 8-lane DPP reductions.
 // Merge (PAT review, merge stage: online-softmax combination of the per-
-// workgroup partial results of a query): one workgroup per query, all heads.
+// workgroup partial results of a query): one wave per 256 output floats of a
+// query, single pass over its partials.
 //
 // Scores are kept in log2 units (q.k * scale * log2 e) so every exponential is
 // a single v_exp_f32.  The running max is refreshed lazily: a row is rescaled
@@ -31,11 +32,21 @@ namespace kvattn {
 namespace {
 
 constexpr float kRescaleLog2 = 8.0f;
+// VALU load ring depth in 16-token blocks.  Two (one block in flight while
+// one is processed) already saturates HBM with 2048 streaming waves; deeper
+// rings only lengthen the request queues (measured on MI355X: depth 2 beat 3
+// and 4 on every workload).
+constexpr int kValuRing = 2;
 constexpr float kNegSentinel = -1.0e30f;   // "no score yet"; finite so m - m stays 0
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format,
+// no swizzle): reads past the resource's size return zero.
+constexpr int kBufferWord3 = 0x00020000;
 
 __device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
@@ -65,6 +76,16 @@ template <int N>
 constexpr int waitcnt_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     return (N & 0xF) | ((N >> 4) << 14) | 0x0F70;
+}
+
+// Lane index, read by an instruction the compiler neither hoists nor merges.
+__device__ __forceinline__ int lane_id_volatile() {
+    int v;
+    asm volatile(
+        "v_mbcnt_lo_u32_b32 %0, -1, 0\n\t"
+        "v_mbcnt_hi_u32_b32 %0, -1, %0"
+        : "=v"(v));
+    return v;
 }
 
 // Direct global -> LDS copy of 16 bytes per lane: lane i writes LDS bytes
@@ -137,11 +158,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // ============================================================================
 // VALU stream: a wave runs the VALU tasks of its workgroup's list for KV head
 // (task head + wave) as one continuous stream of 16-token blocks.  Its
-// three-deep register ring crosses task boundaries, so blocks of the next
+// four-deep register ring crosses task boundaries, so blocks of the next
 // task are in flight while the current one finishes and nothing drains
 // between tasks.  The list's descriptors sit in an LDS window; the q rows of a
-// task are copied into one of four per-wave LDS slots by DMA when the load
-// side enters the task, ahead of its first block.
+// task are copied into one of four per-wave LDS slots by DMA right before the
+// loads of its first block.
 // Lane = 8 * t + c: token slots t and t + 8 of each 16-token block, and the
 // head-dim chunk set of c (elements [8c, 8c+8) and, for D = 128, [64+8c, 64+8c+8)),
 // so every load instruction reads whole 128-byte rows of a block.
@@ -153,8 +174,9 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
                                             float* __restrict__ out) {
     constexpr int NPC = D / 64;      // 16-byte pieces per token per lane
     constexpr int NE = 8 * NPC;      // elements per token per lane
-    constexpr int NWD = NE / 2;      // bf16 pairs per token per lane
     constexpr int LPB = 2 * NPC * 2; // loads per block per lane (2 token slots, NPC pieces, K and V)
+    constexpr int NR = kValuRing;    // load ring depth (blocks); also the q slots per wave
+    static_assert(NR >= 2 && NR <= 4, "the LDS layout holds four q slots per wave");
     constexpr int QSLOT = R * D;     // bf16 elements of one q slot
     constexpr int QCH = QSLOT / 8;   // its 16-byte chunks
     const int lane = threadIdx.x & 63;
@@ -178,14 +200,18 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
     auto fetch_q = [&](int off, int s) {
         const int nrows = hdr(off, kDescRows);
         const int g = hdr(off, kDescHead) + wave;
+        // The lane index is re-read here so that the per-lane terms below are
+        // not hoisted out of the stream loop as live registers: spilled, their
+        // reload would wait for every load in flight.
+        const int ln = lane_id_volatile();
 #pragma unroll
         for (int c0 = 0; c0 < QCH; c0 += 64) {
-            const int ch = c0 + lane;
+            const int ch = c0 + ln;
             const int r = ch / (D / 8), pc = ch % (D / 8);
             if (ch < QCH && r < nrows) {
                 const int query = win[off + kDescHeader + 4 * (r / G)];
-                const uint16_t* src = q + (size_t(query) * Hq + g * G + r % G) * D + pc * 8;
-                dma16(src, qs_lds + uint32_t((s * QSLOT + c0 * 8) * 2));
+                const uint32_t e = uint32_t((query * Hq + g * G + r % G) * D + pc * 8);   // q holds < 2^31 elements
+                dma16(q + e, qs_lds + uint32_t((s * QSLOT + c0 * 8) * 2));
             }
         }
     };
@@ -200,29 +226,43 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
             l_ntok = hdr(l_off, kDescTokens);
             l_bids = l_off + kDescHeader + 4 * hdr(l_off, kDescNq);
             l_g = hdr(l_off, kDescHead) + wave;
-            fetch_q(l_off, l_slot);
         }
     };
     l_enter();
     int total = 0;   // blocks of this wave's stream
     for (int off = l_off; off < n_words; off = skip(off + hdr(off, kDescWords))) total += hdr(off, kDescBlocks);
 
-    // Past the end of the stream the loads come from the zero page, so the ring
-    // below needs no branches around its loads (the compiler keeps them in flight).
+    // A block's K and V slices of KV head l_g are read through buffer resources
+    // whose size covers the block's valid tokens only: the hardware returns
+    // zeros for token slots past the range and for everything past the end of
+    // the stream (size 0), so the ring below has no branches around its loads
+    // (the compiler keeps them in flight) and needs no 64-bit per-lane addresses.
+    int voff[2][NPC];   // byte offsets of this lane's pieces within a head slice
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int pc = 0; pc < NPC; ++pc) voff[tt][pc] = ((t + 8 * tt) * D + pc * 64 + 8 * c) * 2;
     auto load_block = [&](uint4 (&kb)[2][NPC], uint4 (&vb)[2][NPC]) {
         const bool live = l_off < n_words;
+        // A task's q rows are copied right before its first block's loads: the
+        // copy is then older than those loads, and at most NR - 1 tasks (the
+        // blocks still in the ring) are pending, so NR slots never collide.
+        if (live && l_blk == 0) fetch_q(l_off, l_slot);
         const int blk = live ? __builtin_amdgcn_readfirstlane(win[l_bids + l_blk]) : 0;
-        const uint16_t* kbase = kc + size_t(blk) * blk_elems + size_t(l_g) * head_elems;
-        const uint16_t* vbase = vc + size_t(blk) * blk_elems + size_t(l_g) * head_elems;
+        const int valid = live ? min(16, l_ntok - l_blk * 16) : 0;
+        const size_t o = size_t(blk) * blk_elems + size_t(l_g) * head_elems;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + o), 0, valid * D * 2, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + o), 0, valid * D * 2, kBufferWord3);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const int slot = t + 8 * tt;
-            const bool ok = live && l_blk * 16 + slot < l_ntok;
 #pragma unroll
             for (int pc = 0; pc < NPC; ++pc) {
-                const int o = slot * D + pc * 64 + 8 * c;
-                kb[tt][pc] = *reinterpret_cast<const uint4*>(ok ? kbase + o : p.zero);
-                vb[tt][pc] = *reinterpret_cast<const uint4*>(ok ? vbase + o : p.zero);
+                const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rk, voff[tt][pc], 0, 0);
+                const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[tt][pc], 0, 0);
+                kb[tt][pc] = make_uint4(a.x, a.y, a.z, a.w);
+                vb[tt][pc] = make_uint4(b.x, b.y, b.z, b.w);
             }
         }
         if (live && ++l_blk == l_nblk) {
@@ -236,35 +276,20 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
     // ---- process side
     int p_off = skip(0);
     int p_blk = 0, p_slot = 0, p_nblk = 0;
-    uint32_t qv[R][NWD];
     int limit[R];
     float m[R], l[R], acc[R][NE];
 
     auto begin_task = [&]() {
         // the q copy of this task is older than its first block's loads, which
         // are complete once at most two blocks' loads remain outstanding
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm<2 * LPB>());
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm<(NR - 1) * LPB>());
         __builtin_amdgcn_sched_barrier(0);   // no LDS read of the slot moves above the wait
         p_nblk = hdr(p_off, kDescBlocks);
         const int nrows = hdr(p_off, kDescRows);
-        const uint16_t* qsl = qs + p_slot * QSLOT;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            if (r < nrows) {
-#pragma unroll
-                for (int pc = 0; pc < NPC; ++pc) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(qsl + r * D + pc * 64 + 8 * c);
-                    qv[r][4 * pc + 0] = v.x;
-                    qv[r][4 * pc + 1] = v.y;
-                    qv[r][4 * pc + 2] = v.z;
-                    qv[r][4 * pc + 3] = v.w;
-                }
-                limit[r] = win[p_off + kDescHeader + 4 * (r / G) + 2];
-            } else {
-#pragma unroll
-                for (int w = 0; w < NWD; ++w) qv[r][w] = 0u;
-                limit[r] = 0;
-            }
+            // rows past the task's rows read stale q but are fully masked (limit 0)
+            limit[r] = r < nrows ? win[p_off + kDescHeader + 4 * (r / G) + 2] : 0;
             m[r] = kNegSentinel;
             l[r] = 0.f;
 #pragma unroll
@@ -273,21 +298,27 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
     };
 
     auto process = [&](int k, const uint4 (&kb)[2][NPC], const uint4 (&vb)[2][NPC]) {
+        // q rows come from the task's LDS slot (every lane of a chunk set reads
+        // the same 16 bytes), which keeps the register file for the load ring
+        const uint16_t* qsl = qs + p_slot * QSLOT;
         float s[R][2];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int r = 0; r < R; ++r) {
+            float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                float a = 0.f;
-#pragma unroll
-                for (int pc = 0; pc < NPC; ++pc) {
-                    a = dot2_bf16(qv[r][4 * pc + 0], kb[tt][pc].x, a);
-                    a = dot2_bf16(qv[r][4 * pc + 1], kb[tt][pc].y, a);
-                    a = dot2_bf16(qv[r][4 * pc + 2], kb[tt][pc].z, a);
-                    a = dot2_bf16(qv[r][4 * pc + 3], kb[tt][pc].w, a);
-                }
-                s[r][tt] = octet_sum(a);
+            for (int pc = 0; pc < NPC; ++pc) {
+                const uint4 qq = *reinterpret_cast<const uint4*>(qsl + r * D + pc * 64 + 8 * c);
+                a0 = dot2_bf16(qq.x, kb[0][pc].x, a0);
+                a0 = dot2_bf16(qq.y, kb[0][pc].y, a0);
+                a0 = dot2_bf16(qq.z, kb[0][pc].z, a0);
+                a0 = dot2_bf16(qq.w, kb[0][pc].w, a0);
+                a1 = dot2_bf16(qq.x, kb[1][pc].x, a1);
+                a1 = dot2_bf16(qq.y, kb[1][pc].y, a1);
+                a1 = dot2_bf16(qq.z, kb[1][pc].z, a1);
+                a1 = dot2_bf16(qq.w, kb[1][pc].w, a1);
             }
+            s[r][0] = octet_sum(a0);
+            s[r][1] = octet_sum(a1);
         }
         bool need = false;
 #pragma unroll
@@ -335,11 +366,10 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
         }
     };
 
-    // combine the 8 token lanes of each chunk set (lanes c, c+8, ..., c+56) and store
+    // combine the 8 token lanes of each chunk set (lanes c, c+8, ..., c+56); the
+    // results stay in acc[r][0 .. NE/8), ltot, mrow until store_task writes them
+    float ltot[R], mrow[R];
     auto end_task = [&]() {
-        const int nrows = hdr(p_off, kDescRows);
-        const int g = hdr(p_off, kDescHead) + wave;
-        float ltot[R], mrow[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             float M = m[r];
@@ -379,13 +409,19 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
                 acc[r][i] = keep + __shfl_xor(send, 8);
             }
         }
+    };
+    // write the results of the task at `off` (output rows or partial triples)
+    auto store_task = [&](int off) {
+        const int nrows = hdr(off, kDescRows);
+        const int g = hdr(off, kDescHead) + wave;
+        const bool u32 = (lane & 32) != 0, u16 = (lane & 16) != 0, u8 = (lane & 8) != 0;
         const int ebase = (u32 ? NE / 2 : 0) + (u16 ? NE / 4 : 0) + (u8 ? NE / 8 : 0);
         // element e of chunk set c is head-dim index 8c + e (e < 8) or 64 + 8c + (e - 8)
         const int d0 = (ebase < 8) ? 8 * c + ebase : 64 + 8 * c + (ebase - 8);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             if (r >= nrows) continue;
-            const int4 e = *reinterpret_cast<const int4*>(win + p_off + kDescHeader + 4 * (r / G));
+            const int4 e = *reinterpret_cast<const int4*>(win + off + kDescHeader + 4 * (r / G));
             const int h = g * G + r % G;
             if (e.y < 0) {
                 float* o = out + (size_t(e.x) * Hq + h) * D + d0;
@@ -408,38 +444,48 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
         }
     };
 
+    // A finished task's stores are issued after the next block's loads: vmcnt
+    // retires loads and stores in issue order, so a store issued before a load
+    // would make the wait for that load also wait for the store's ack.  Issued
+    // after it, the stores have NR block-times to complete before any wait
+    // depends on them.
+    int f_off = -1;   // task whose results await their stores
     auto proc_block = [&](const uint4 (&kb)[2][NPC], const uint4 (&vb)[2][NPC]) {
         if (p_blk == 0) begin_task();
         process(p_blk, kb, vb);
         if (++p_blk == p_nblk) {
             end_task();
+            f_off = p_off;
             p_off = skip(p_off + hdr(p_off, kDescWords));
             p_blk = 0;
             p_slot = (p_slot + 1) & 3;
         }
     };
+    auto flush = [&]() {
+        if (f_off >= 0) {
+            store_task(f_off);
+            f_off = -1;
+        }
+    };
 
-    // three-deep register ring across the whole stream
-    uint4 k0[2][NPC], v0[2][NPC], k1[2][NPC], v1[2][NPC], k2[2][NPC], v2[2][NPC];
-    load_block(k0, v0);
-    load_block(k1, v1);
-    load_block(k2, v2);
-    // scheduling barriers keep each refill after the compute that frees its registers,
-    // so two blocks stay in flight and register pressure stays bounded
-    for (int j = 0; j < total; j += 3) {
-        proc_block(k0, v0);
-        __builtin_amdgcn_sched_barrier(0);
-        load_block(k0, v0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (j + 1 < total) proc_block(k1, v1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_block(k1, v1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (j + 2 < total) proc_block(k2, v2);
-        __builtin_amdgcn_sched_barrier(0);
-        load_block(k2, v2);
-        __builtin_amdgcn_sched_barrier(0);
+    // NR-deep register ring across the whole stream; scheduling barriers keep
+    // each refill after the compute that frees its registers, so NR - 1 blocks
+    // stay in flight and register pressure stays bounded
+    uint4 kr[NR][2][NPC], vr[NR][2][NPC];
+#pragma unroll
+    for (int u = 0; u < NR; ++u) load_block(kr[u], vr[u]);
+    for (int j = 0; j < total; j += NR) {
+#pragma unroll
+        for (int u = 0; u < NR; ++u) {
+            if (j + u < total) proc_block(kr[u], vr[u]);
+            __builtin_amdgcn_sched_barrier(0);
+            load_block(kr[u], vr[u]);
+            __builtin_amdgcn_sched_barrier(0);
+            flush();
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+    flush();
 }
 
 // ============================================================================
@@ -811,88 +857,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 }
 
 // ============================================================================
-// Merge: one workgroup per query with several partial triples, all q heads at
-// once.  The slots of one item entry are consecutive (slot = dest + h), so each
-// partial's accumulators for every head form one contiguous [Hq][D] block.
-//   M_h = max_i m_ih, w_ih = 2^(m_ih - M_h) / sum_i 2^(m_ih - M_h) l_ih,
-//   out[h] = sum_i w_ih acc_ih
+// Merge (one wave per workgroup): workgroup (query, y) combines, for the 256
+// output floats [256 y, 256 y + 256) of the query's [Hq][D] block, all partial
+// triples of the query in one pass with the online-softmax rule:
+//   M' = max(M, m_i);  A = A 2^(M - M') + 2^(m_i - M') acc_i;  L likewise with l_i
+// and writes A / L.  The slots of one item entry are consecutive (slot = dest +
+// h), so a partial's accumulators for every head form one contiguous [Hq][D]
+// block.  Partials are read in batches of eight with every load in flight.
 // ============================================================================
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(DevPlan p, Dims dm, float* __restrict__ out) {
-    constexpr int COLS = 1024;              // floats of [Hq][D] per workgroup (blockIdx.y selects the block)
-    constexpr int HB = COLS / D;            // heads per workgroup
-    constexpr int MAXW = 4096;              // weights staged per batch of partials
-    __shared__ float s_m[HB];
-    __shared__ float s_inv[HB];
-    __shared__ float s_w[MAXW];
+__global__ __launch_bounds__(64) void merge_kernel(DevPlan p, Dims dm, float* __restrict__ out) {
+    constexpr int BATCH = 8;
     const int Hq = dm.num_q_heads;
-    const int h_lo = int(blockIdx.y) * HB;
-    const int nh = min(HB, Hq - h_lo);
     const int mq = blockIdx.x;
+    const int col = int(blockIdx.y) * 256 + 4 * int(threadIdx.x);   // float index in [Hq][D]
+    if (col >= Hq * D) return;
+    const int h = col / D;
     const KV_CONST int32_t* mptr = cptr(p.merge_ptr);
     const KV_CONST int32_t* mdst = cptr(p.merge_dest);
     const int b = cptr(p.merge_query)[mq];
     const int i0 = mptr[mq], i1 = mptr[mq + 1];
-    const int tid = threadIdx.x;
-    // per head: M = max m_i, 1 / sum_i 2^(m_i - M) l_i  (one wave per head)
-    for (int hh = tid >> 6; hh < nh; hh += 4) {
-        const int h = h_lo + hh;
-        float M = -INFINITY;
-        for (int i = i0 + (tid & 63); i < i1; i += 64) M = fmaxf(M, p.part_ml[(size_t(mdst[i]) + h) * 2]);
+    float M = -INFINITY, L = 0.f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int ib = i0; ib < i1; ib += BATCH) {
+        float2 ml[BATCH];
+        float4 ac[BATCH];
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-        float L = 0.f;
-        for (int i = i0 + (tid & 63); i < i1; i += 64) {
-            const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + (size_t(mdst[i]) + h) * 2);
-            L += fast_exp2(ml.x - M) * ml.y;
+        for (int j = 0; j < BATCH; ++j) {
+            const int i = min(ib + j, i1 - 1);
+            const size_t slot = size_t(mdst[i]) + h;
+            ml[j] = *reinterpret_cast<const float2*>(p.part_ml + slot * 2);
+            ac[j] = *reinterpret_cast<const float4*>(p.part_acc + slot * D + (col - h * D));
         }
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-        if ((tid & 63) == 0) {
-            s_m[hh] = M;
-            s_inv[hh] = 1.f / L;
-        }
-    }
-    const int n4 = nh * D / 4;              // float4 of this workgroup's block (<= 256)
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    const int per = MAXW / nh;
-    const int hq = (4 * tid) / D;           // head of this thread's float4
-    for (int ib = i0; ib < i1; ib += per) {
-        const int nb = min(per, i1 - ib);
-        __syncthreads();
-        for (int x = tid; x < nb * nh; x += 256) {
-            const int i = x / nh, hh = x % nh;
-            const float m = p.part_ml[(size_t(mdst[ib + i]) + h_lo + hh) * 2];
-            s_w[x] = fast_exp2(m - s_m[hh]) * s_inv[hh];
-        }
-        __syncthreads();
-        if (tid < n4) {
-            int i = 0;
-            for (; i + 4 <= nb; i += 4) {
-                float4 v[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    v[u] = reinterpret_cast<const float4*>(p.part_acc + (size_t(mdst[ib + i + u]) + h_lo) * D)[tid];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float w = s_w[(i + u) * nh + hq];
-                    acc.x = fmaf(w, v[u].x, acc.x);
-                    acc.y = fmaf(w, v[u].y, acc.y);
-                    acc.z = fmaf(w, v[u].z, acc.z);
-                    acc.w = fmaf(w, v[u].w, acc.w);
-                }
-            }
-            for (; i < nb; ++i) {
-                const float4 v = reinterpret_cast<const float4*>(p.part_acc + (size_t(mdst[ib + i]) + h_lo) * D)[tid];
-                const float w = s_w[i * nh + hq];
-                acc.x = fmaf(w, v.x, acc.x);
-                acc.y = fmaf(w, v.y, acc.y);
-                acc.z = fmaf(w, v.z, acc.z);
-                acc.w = fmaf(w, v.w, acc.w);
-            }
+        for (int j = 0; j < BATCH; ++j) {
+            // past the query's last partial: no change (weight 0, same max)
+            const float mj = ib + j < i1 ? ml[j].x : -INFINITY;
+            const float Mn = fmaxf(M, mj);
+            const float so = fast_exp2(M - Mn);     // 0 while M is -inf
+            const float sn = fast_exp2(mj - Mn);    // 0 past the last partial
+            L = L * so + sn * ml[j].y;
+            A.x = fmaf(sn, ac[j].x, A.x * so);
+            A.y = fmaf(sn, ac[j].y, A.y * so);
+            A.z = fmaf(sn, ac[j].z, A.z * so);
+            A.w = fmaf(sn, ac[j].w, A.w * so);
+            M = Mn;
         }
     }
-    if (tid < n4) reinterpret_cast<float4*>(out + (size_t(b) * Hq + h_lo) * D)[tid] = acc;
+    const float inv = 1.f / L;
+    *reinterpret_cast<float4*>(out + size_t(b) * Hq * D + col) = make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
 }
 
 // Grid of a persistent launch: the workgroups the device holds at once
@@ -942,10 +955,11 @@ int launch_forward(const DevPlan& p, const Dims& d, int valu_rows, int mfma_tile
 int launch_merge(const DevPlan& p, const Dims& d, int q_count, float* out, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (q_count <= 0) return 0;
+    const unsigned ny = unsigned((d.num_q_heads * d.head_dim + 255) / 256);
     if (d.head_dim == 128)
-        hipLaunchKernelGGL((merge_kernel<128>), dim3(q_count, (d.num_q_heads + 7) / 8), dim3(256), 0, s, p, d, out);
+        hipLaunchKernelGGL((merge_kernel<128>), dim3(q_count, ny), dim3(64), 0, s, p, d, out);
     else if (d.head_dim == 64)
-        hipLaunchKernelGGL((merge_kernel<64>), dim3(q_count, (d.num_q_heads + 15) / 16), dim3(256), 0, s, p, d, out);
+        hipLaunchKernelGGL((merge_kernel<64>), dim3(q_count, ny), dim3(64), 0, s, p, d, out);
     else
         return int(hipErrorInvalidValue);
     return int(hipGetLastError());

@@ -202,14 +202,19 @@ constexpr int64_t kFoldCapTokens = 256;
 constexpr int64_t kChunkCapTokens = int64_t(kMaxItemBlocks) * kBlock - kFoldCapTokens;
 
 // Task costs, in units of one wave streaming one KV head-token with every CU
-// busy (about 0.17 us on MI355X: 512 bytes at 1/2048 of the HBM bandwidth).
-// An MFMA workgroup keeps three 16 KB tiles in flight and is latency bound:
-// about 2 us per 32-token tile under load, 0.4 units per token, plus a
-// pipeline fill of about 15 us.  A VALU task adds a small boundary cost to its
-// wave streams (epilogue, q rows).
-constexpr double kMfmaTokenCost = 0.4;
-constexpr double kMfmaTaskCost = 90.0;
+// busy (about 0.18 us on MI355X: 512 bytes at 1/2048 of the HBM bandwidth).
+// An MFMA workgroup streams one KV head at four to five times a VALU wave's
+// rate (measured on MI355X: ~45 ns against ~180-280 ns per head-token under
+// load) after a pipeline fill of ~7 us; wider row groups add matrix work per
+// token.  A VALU task adds a small boundary cost to its wave streams
+// (epilogue, q rows).
+constexpr double kMfmaTokenCost = 0.2;
+constexpr double kMfmaTaskCost = 40.0;
 constexpr double kValuTaskCost = 8.0;
+// Partial triples are written into a saturated HBM read stream; on MI355X
+// each written byte costs about as much time as twenty bytes read (measured:
+// a 2 KB partial store per VALU task costs about 45 KB of streaming).
+constexpr double kPartialWriteCost = 20.0;
 
 // Append the descriptor of task t (see kDesc*) to P.desc; returns its words.
 int32_t put_desc(kvattn_plan_s& P, const Task& t) {
@@ -432,7 +437,10 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     // waves.  The cheapest candidate wins.  A VALU chunk keeps at least 64
     // tokens, an MFMA chunk 128.
     const int n_lists = num_cus * 2;
-    const double partial_units = 2.0 * double(partial_row_bytes) / double(2 * D * 2);  // one triple, w + r
+    // one partial triple: written once (a write in the middle of a saturated
+    // read stream costs about kPartialWriteCost read bytes per byte) and read
+    // once by the merge
+    const double partial_units = (kPartialWriteCost + 1.0) * double(partial_row_bytes) / double(2 * D * 2);
     auto task_cost = [&](const Group& g, int64_t tok) {
         return g.kind == KVATTN_VARIANT_VALU ? double(tok) + kValuTaskCost : double(tok) * g.w + kMfmaTaskCost;
     };
