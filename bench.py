@@ -63,11 +63,13 @@ def describe(c, wl):
     return d
 
 
-def traffic_from_counters(c, launch_kind):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE summaries.
+def traffic_from_counters(c):
+    """HBM bytes per forward launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE summaries.
 
-    Null when no summary exists for this workload or the kernel source changed since
-    the counters were taken.
+    Each counter (KiB per dispatch) is scaled by what the same counter reads for a
+    plain device copy of known size (fetch_scale, write_scale in the summary).
+    Returns (read + written bytes, read bytes), both None when no summary exists
+    for this workload or the kernel source changed since the counters were taken.
     """
     path = os.path.join(PROFILES, "counters_c%d.json" % c)
     if not os.path.exists(path):
@@ -75,9 +77,10 @@ def traffic_from_counters(c, launch_kind):
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_src_sha") != kernel_src_sha():
-        return None, rec
-    kib = rec.get("forward_fetch_kib", 0.0) + rec.get("forward_write_kib", 0.0)
-    return kib * 1024.0 * rec.get("copy_scale", 1.0), rec
+        return None, None
+    fetch = rec["forward_fetch_kib"] * 1024.0 * rec["fetch_scale"]
+    write = rec["forward_write_kib"] * 1024.0 * rec["write_scale"]
+    return fetch + write, fetch
 
 
 def cpu_baseline(wl, budget_s=12.0):
@@ -255,7 +258,7 @@ def main():
     value = uniq / (ms_per_step * 1e-3) / 1e9
     fwd_avg = float(fwd_ms.mean())
     achieved = uniq / (fwd_avg * 1e-3) / 1e9
-    traffic, counters = traffic_from_counters(args.config, "forward")
+    traffic, fetched = traffic_from_counters(args.config)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None if traffic is None else int(traffic),
                 "kernel": "fwd_kernel (persistent; %d MFMA + %d VALU items)" % (st["num_items_mfma"],
@@ -270,7 +273,7 @@ def main():
         "us_per_call": round(ms_per_step * 1e3, 2),
         "us_per_call_gpu_events_median": round(float(np.median(call_ms)) * 1e3, 2),
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
-        "redundancy_fetch_over_unique": None if traffic is None else round(traffic / uniq, 4),
+        "redundancy_fetch_over_unique": None if fetched is None else round(fetched / uniq, 4),
         "plan_ms": round(st["plan_seconds"] * 1e3, 3), "plan_upload_ms": round(plan_upload_ms, 3),
         "plan": {k: st[k] for k in ("num_items", "num_items_valu", "num_items_mfma", "num_packed_nodes",
                                     "num_folded_leaves", "num_merge_rows", "num_launches", "split_tokens",
