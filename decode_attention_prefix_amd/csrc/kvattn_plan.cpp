@@ -17,6 +17,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <limits>
 #include <new>
 #include <numeric>
 #include <queue>
@@ -211,10 +212,12 @@ constexpr int64_t kChunkCapTokens = int64_t(kMaxItemBlocks) * kBlock - kFoldCapT
 constexpr double kMfmaTokenCost = 0.2;
 constexpr double kMfmaTaskCost = 40.0;
 constexpr double kValuTaskCost = 8.0;
-// Partial triples are written into a saturated HBM read stream; on MI355X
-// each written byte costs about as much time as twenty bytes read (measured:
-// a 2 KB partial store per VALU task costs about 45 KB of streaming).
-constexpr double kPartialWriteCost = 20.0;
+// Partial triples are written into a saturated HBM read stream; on MI355X a
+// VALU wave's small partial stores cost about twenty read bytes per byte
+// (measured), which is why the VALU work is cut at most once per stripe.  An
+// MFMA task writes its partials as one burst of up to 128 rows, which costs
+// far less per byte.
+constexpr double kPartialWriteCostMfma = 2.0;
 
 // Append the descriptor of task t (see kDesc*) to P.desc; returns its words.
 int32_t put_desc(kvattn_plan_s& P, const Task& t) {
@@ -424,148 +427,297 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         }
     }
 
-    // ---- split length (long-KV splitting, runtime split selector) -------------------
-    // Time unit: one wave streaming one KV head-token with every CU busy.  A
-    // VALU task (an item on up to four KV heads, one wave each) runs as part of
-    // its waves' continuous streams and costs its tokens plus a small boundary
-    // cost; an MFMA task (an item on one KV head, the whole workgroup) costs
-    // tokens x w plus a fixed start-up (pipeline fill).  Candidate target task
-    // costs tau are tried; for each, every range is cut into chunks of about
-    // tau, the tasks are placed longest first on the persistent workgroups, and
-    // the score is the resulting makespan plus the partial triples that
-    // splitting adds (written by forward, read by merge), spread over the
-    // waves.  The cheapest candidate wins.  A VALU chunk keeps at least 64
-    // tokens, an MFMA chunk 128.
-    const int n_lists = num_cus * 2;
-    // one partial triple: written once (a write in the middle of a saturated
-    // read stream costs about kPartialWriteCost read bytes per byte) and read
-    // once by the merge
-    const double partial_units = (kPartialWriteCost + 1.0) * double(partial_row_bytes) / double(2 * D * 2);
-    auto task_cost = [&](const Group& g, int64_t tok) {
-        return g.kind == KVATTN_VARIANT_VALU ? double(tok) + kValuTaskCost : double(tok) * g.w + kMfmaTaskCost;
-    };
-    auto tasks_per_item = [&](const Group& g) { return g.kind == KVATTN_VARIANT_VALU ? (Hkv + kWaves - 1) / kWaves : Hkv; };
-    double work = 0.0;
-    for (const Group& g : groups) work += task_cost(g, units[g.unit].tokens) * tasks_per_item(g);
-    auto chunk_of = [&](const Group& g, double tau) -> int64_t {
-        if (o.split_tokens > 0) return std::min<int64_t>(ceil16(o.split_tokens), kChunkCapTokens);
-        const double per_tok = g.kind == KVATTN_VARIANT_VALU ? 1.0 : g.w;
-        int64_t c = ceil16(int64_t(std::ceil(tau / per_tok)));
-        c = std::max<int64_t>(c, g.kind == KVATTN_VARIANT_VALU ? 64 : 128);
-        return std::min<int64_t>(c, kChunkCapTokens);
-    };
-    auto score_of = [&](double tau) {
-        std::vector<double> costs;
-        double extra = 0.0;
-        for (const Group& g : groups) {
-            const Unit& u = units[g.unit];
-            const int64_t c = chunk_of(g, tau);
-            const int64_t nch = (u.tokens + c - 1) / c;
-            const int64_t len = ceil16((u.tokens + nch - 1) / nch);
-            extra += double(nch - 1) * g.rows * Hkv * partial_units;
-            for (int64_t k = 0; k < nch; ++k) {
-                const int64_t tok = std::min(len, u.tokens - k * len) + (k == nch - 1 ? u.fold_tokens : 0);
-                if (tok <= 0) break;
-                for (int h = 0; h < tasks_per_item(g); ++h) costs.push_back(task_cost(g, tok));
-            }
-        }
-        std::sort(costs.begin(), costs.end(), std::greater<double>());
-        std::priority_queue<double, std::vector<double>, std::greater<double>> heap;
-        for (int w = 0; w < n_lists; ++w) heap.push(0.0);
-        for (double c : costs) {
-            const double l = heap.top();
-            heap.pop();
-            heap.push(l + c);
-        }
-        double makespan = 0.0;
-        while (!heap.empty()) {
-            makespan = std::max(makespan, heap.top());
-            heap.pop();
-        }
-        return makespan + extra / (double(n_lists) * kWaves);
-    };
-    double tau = double(kChunkCapTokens) * 4.0;
-    if (o.split_tokens <= 0) {
-        const double mean = std::max(64.0, work / n_lists);
-        double best = 0.0;
-        bool first = true;
-        for (double f : {2.0, 1.0, 0.75, 0.5, 1.0 / 3, 0.25, 0.2, 1.0 / 6, 0.125}) {
-            const double sc = score_of(mean * f);
-            if (first || sc < best * 0.995) {
-                best = sc;
-                tau = mean * f;
-                first = false;
-            }
-        }
-    }
-    int64_t C = 0;              // longest chunk of a split range (statistics)
-    for (const Group& g : groups)
-        if (units[g.unit].tokens > chunk_of(g, tau)) C = std::max(C, chunk_of(g, tau));
-
-    // ---- items ----------------------------------------------------------------------
-    std::vector<Proto> protos;
-    for (const Group& g : groups) {
-        const Unit& u = units[g.unit];
-        const int64_t chunk = chunk_of(g, tau);
-        const int64_t nch = (u.tokens + chunk - 1) / chunk;
-        const int64_t len = ceil16((u.tokens + nch - 1) / nch);
-        const bool has_fold = u.fold_query >= 0 &&
-                              std::find(g.queries.begin(), g.queries.end(), u.fold_query) != g.queries.end();
-        for (int64_t c = 0; c < nch; ++c) {
-            const int64_t tok0 = c * len;
-            if (tok0 >= u.tokens) break;
-            const int64_t ntok = std::min(len, u.tokens - tok0);
-            const bool last = tok0 + ntok == u.tokens;
-            Proto p;
-            p.it.kind = g.kind;
-            p.it.tile = g.tile;
-            p.it.pos_begin = u.pos_begin + int(tok0 / kBlock);
-            const int nblk = int((ntok + kBlock - 1) / kBlock);
-            for (int j = 0; j < nblk; ++j) p.blocks.push_back(bt.id(u.ref_query, p.it.pos_begin + j));
-            int64_t item_tokens = ntok;
-            for (int q : g.queries) {
-                Entry e{q, -1, int32_t(ntok), 0};
-                if (has_fold && last && q == u.fold_query) e.limit = int32_t(ntok + u.fold_tokens);
-                p.entries.push_back(e);
-            }
-            if (has_fold && last) {
-                for (int j = u.pos_end; j < u.fold_pos_end; ++j) p.blocks.push_back(bt.id(u.fold_query, j));
-                item_tokens = ntok + u.fold_tokens;
-            }
-            if ((item_tokens + kBlock - 1) / kBlock > kMaxItemBlocks)
-                return set_error(KVATTN_EINVAL, "internal: item exceeds the per-item block cap");
-            p.it.n_tokens = int32_t(item_tokens);
-            p.it.n_q = int32_t(g.queries.size());
-            p.it.n_rows = g.rows;
-            p.cost = task_cost(g, item_tokens);   // one task of the item
-            protos.push_back(std::move(p));
-        }
-    }
-
     // ---- forward launches ----------------------------------------------------------------
     // One launch runs VALU and MFMA tasks side by side.  Launch i takes the
     // i-th largest VALU row template and the i-th largest MFMA tiling, so a
     // plan needs max(#templates, #tilings) launches -- normally one.
     std::vector<int> vt, mt;
-    for (const Proto& p : protos) {
-        std::vector<int>& v = p.it.kind == KVATTN_VARIANT_MFMA ? mt : vt;
-        if (std::find(v.begin(), v.end(), p.it.tile) == v.end()) v.push_back(p.it.tile);
+    for (const Group& g : groups) {
+        std::vector<int>& v = g.kind == KVATTN_VARIANT_MFMA ? mt : vt;
+        if (std::find(v.begin(), v.end(), g.tile) == v.end()) v.push_back(g.tile);
     }
     std::sort(vt.begin(), vt.end(), std::greater<int>());
     std::sort(mt.begin(), mt.end(), std::greater<int>());
     const int n_launch = int(std::max(vt.size(), mt.size()));
-    auto launch_of = [&](const Proto& p) {
-        const std::vector<int>& v = p.it.kind == KVATTN_VARIANT_MFMA ? mt : vt;
-        return int(std::find(v.begin(), v.end(), p.it.tile) - v.begin());
+    auto launch_of = [&](const Group& g) {
+        const std::vector<int>& v = g.kind == KVATTN_VARIANT_MFMA ? mt : vt;
+        return int(std::find(v.begin(), v.end(), g.tile) - v.begin());
     };
 
-    // ---- item order: by launch, then longest first (stable) -------------------------------
+    // ---- schedule: MFMA tasks placed longest first, VALU work cut to fill -------------------
+    // Time unit: one wave streaming one KV head-token with every CU busy.  Each
+    // launch has n_lists static lists, one per persistent workgroup.
+    //  * MFMA items (packed groups) run one task per KV head on a whole
+    //    workgroup.  Their chunk length is chosen from a few candidates; for
+    //    each, the tasks are placed longest first on the least-loaded list (an
+    //    MFMA task of KV head g prefers a list of XCD g mod 8 -- workgroup w runs
+    //    on XCD w mod 8 -- so the row groups and chunks reading one head's shared
+    //    range meet in one L2).
+    //  * VALU items run one task per four KV heads, one wave per head, as part
+    //    of continuous per-wave streams.  The lists are taken in groups of
+    //    ceil(Hkv / 4) consecutive lists ("stripes", all KV heads of an item);
+    //    the VALU token stream of the launch (every VALU range in order) is cut
+    //    into pieces that fill every stripe up to one common level above its
+    //    MFMA load.  The stripes then end together, and at most one cut per
+    //    stripe adds partial triples.
+    //  The candidate with the lowest makespan plus partial-write cost wins.
+    //  Forced split lengths (tests) cut every range uniformly instead and place
+    //  VALU items on the least-loaded stripe.
+    const int n_lists = num_cus * 2;
+    const int quads = (Hkv + kWaves - 1) / kWaves;
+    const int n_stripes = std::max(1, n_lists / quads);
+    const double pu_mfma = (kPartialWriteCostMfma + 1.0) * double(partial_row_bytes) / double(2 * D * 2);
+    auto mfma_cost = [&](const Group& g, int64_t tok) { return double(tok) * g.w + kMfmaTaskCost; };
+    auto unit_tokens = [&](const Group& g) { return units[g.unit].tokens; };
+
+    struct Piece {                      // a chunk of one group's range, before it becomes an item
+        int group;
+        int64_t tok0, ntok;             // range within the group's unit (ntok excludes a folded leaf)
+        bool last;
+        int stripe = -1;                // VALU: stripe; MFMA: -1
+        std::vector<int> head_list;     // MFMA: list of each KV head's task
+    };
+    std::vector<Piece> pieces;
+    int64_t C = 0;                      // longest chunk of a split range (statistics)
+
+    for (int L = 0; L < n_launch; ++L) {
+        std::vector<int> mg, vg;
+        for (size_t gi = 0; gi < groups.size(); ++gi) {
+            if (launch_of(groups[gi]) != L) continue;
+            (groups[gi].kind == KVATTN_VARIANT_MFMA ? mg : vg).push_back(int(gi));
+        }
+        double w_valu = 0.0, w_mfma = 0.0;
+        for (int gi : vg) w_valu += double(unit_tokens(groups[gi])) * quads;
+        for (int gi : mg) w_mfma += double(unit_tokens(groups[gi])) * groups[gi].w * Hkv;
+        const double mean0 = std::max(64.0, (w_valu + w_mfma) / n_lists);
+
+        // MFMA chunking and placement for a target task cost `target`
+        struct MfmaPlan {
+            std::vector<Piece> pieces;
+            std::vector<double> load;
+            double extra = 0.0;
+        };
+        auto place_mfma = [&](double target) {
+            MfmaPlan mp;
+            mp.load.assign(size_t(n_lists), 0.0);
+            struct T {
+                int piece, head;
+                double cost;
+            };
+            std::vector<T> tasks;
+            for (int gi : mg) {
+                const Group& g = groups[size_t(gi)];
+                const int64_t tokens = unit_tokens(g);
+                int64_t chunk;
+                if (o.split_tokens > 0) {
+                    chunk = std::min<int64_t>(ceil16(o.split_tokens), kChunkCapTokens);
+                } else {
+                    chunk = ceil16(int64_t(std::ceil((target - kMfmaTaskCost) / g.w)));
+                    chunk = std::min<int64_t>(std::max<int64_t>(chunk, 128), kChunkCapTokens);
+                }
+                const int64_t nch = (tokens + chunk - 1) / chunk;
+                const int64_t len = ceil16((tokens + nch - 1) / nch);
+                mp.extra += double(nch - 1) * g.rows * Hkv * pu_mfma;
+                for (int64_t c = 0; c < nch; ++c) {
+                    const int64_t tok0 = c * len;
+                    if (tok0 >= tokens) break;
+                    Piece pc;
+                    pc.group = gi;
+                    pc.tok0 = tok0;
+                    pc.ntok = std::min(len, tokens - tok0);
+                    pc.last = tok0 + pc.ntok == tokens;
+                    pc.head_list.assign(size_t(Hkv), 0);
+                    const int64_t with_fold = pc.ntok + (pc.last ? units[g.unit].fold_tokens : 0);
+                    for (int h = 0; h < Hkv; ++h)
+                        tasks.push_back({int(mp.pieces.size()), h, mfma_cost(g, with_fold)});
+                    mp.pieces.push_back(std::move(pc));
+                }
+            }
+            std::stable_sort(tasks.begin(), tasks.end(), [](const T& a, const T& b) { return a.cost > b.cost; });
+            using LE = std::pair<double, int>;
+            using Heap = std::priority_queue<LE, std::vector<LE>, std::greater<LE>>;
+            Heap heap_all;
+            std::vector<Heap> heap_x(kXcds);
+            for (int w = 0; w < n_lists; ++w) {
+                heap_all.push({0.0, w});
+                heap_x[size_t(w % kXcds)].push({0.0, w});
+            }
+            auto top_of = [&](Heap& h) {
+                while (!h.empty() && h.top().first != mp.load[size_t(h.top().second)]) h.pop();
+                return h.empty() ? -1 : h.top().second;
+            };
+            for (const T& t : tasks) {
+                int w = top_of(heap_all);
+                const int wx = top_of(heap_x[size_t(t.head % kXcds)]);
+                if (wx >= 0 && mp.load[size_t(wx)] <= mp.load[size_t(w)] + 0.25 * t.cost) w = wx;
+                mp.pieces[size_t(t.piece)].head_list[size_t(t.head)] = w;
+                mp.load[size_t(w)] += t.cost;
+                heap_all.push({mp.load[size_t(w)], w});
+                heap_x[size_t(w % kXcds)].push({mp.load[size_t(w)], w});
+            }
+            return mp;
+        };
+        // the stripes' common fill level for the VALU work above their MFMA loads
+        auto stripe_base = [&](const std::vector<double>& load) {
+            std::vector<double> base(size_t(n_stripes), 0.0);
+            for (int s = 0; s < n_stripes; ++s)
+                for (int q = 0; q < quads; ++q) base[size_t(s)] = std::max(base[size_t(s)], load[size_t(s * quads + q)]);
+            return base;
+        };
+        // the level at which the stripes, each filled from its base, hold `work`
+        auto fill_level = [&](const std::vector<double>& base, double work) {
+            double lo = *std::min_element(base.begin(), base.end());
+            double hi = *std::max_element(base.begin(), base.end()) + work / n_stripes + 1.0;
+            for (int it = 0; it < 60; ++it) {
+                const double mid = 0.5 * (lo + hi);
+                double cap = 0.0;
+                for (int s = 0; s < n_stripes; ++s) cap += std::max(0.0, mid - base[size_t(s)]);
+                (cap >= work ? hi : lo) = mid;
+            }
+            return hi;
+        };
+        const double valu_work = w_valu / quads + kValuTaskCost * double(vg.size() + size_t(n_stripes));
+
+        MfmaPlan best;
+        bool have = false;
+        double best_score = 0.0;
+        std::vector<double> targets{mean0};
+        if (!mg.empty() && o.split_tokens <= 0) {
+            targets.push_back(2.0 * mean0);
+            for (int i = 1; i <= 24; ++i) targets.push_back(mean0 * std::pow(2.0, -i / 4.0));
+        }
+        for (double target : targets) {
+            MfmaPlan mp = place_mfma(target);
+            const std::vector<double> base = stripe_base(mp.load);
+            double makespan = *std::max_element(mp.load.begin(), mp.load.end());
+            if (!vg.empty()) makespan = std::max(makespan, fill_level(base, valu_work));
+            const double score = makespan + mp.extra / (double(n_lists) * kWaves);
+            if (!have || score < best_score * 0.995) {
+                best = std::move(mp);
+                best_score = score;
+                have = true;
+            }
+        }
+        for (const Piece& pc : best.pieces) C = std::max(C, pc.ntok < unit_tokens(groups[size_t(pc.group)]) ? pc.ntok : 0);
+        const std::vector<double> base = stripe_base(best.load);
+
+        // VALU pieces
+        if (o.split_tokens > 0) {
+            const int64_t chunk = std::min<int64_t>(ceil16(o.split_tokens), kChunkCapTokens);
+            std::vector<double> sload = base;
+            for (int gi : vg) {
+                const int64_t tokens = unit_tokens(groups[size_t(gi)]);
+                const int64_t nch = (tokens + chunk - 1) / chunk;
+                const int64_t len = ceil16((tokens + nch - 1) / nch);
+                for (int64_t c = 0; c < nch; ++c) {
+                    const int64_t tok0 = c * len;
+                    if (tok0 >= tokens) break;
+                    Piece pc;
+                    pc.group = gi;
+                    pc.tok0 = tok0;
+                    pc.ntok = std::min(len, tokens - tok0);
+                    pc.last = tok0 + pc.ntok == tokens;
+                    pc.stripe = int(std::min_element(sload.begin(), sload.end()) - sload.begin());
+                    sload[size_t(pc.stripe)] += double(pc.ntok) + kValuTaskCost;
+                    if (pc.ntok < tokens) C = std::max(C, pc.ntok);
+                    best.pieces.push_back(std::move(pc));
+                }
+            }
+        } else if (!vg.empty()) {
+            // Greedy pass: stripes in order, each filled up to `level` with whole
+            // blocks.  Returns the work left over for the last stripe past level.
+            auto fill = [&](double level, std::vector<Piece>* out) {
+                int s = 0;
+                double room = level - base[0];
+                double over = 0.0;
+                for (int gi : vg) {
+                    const int64_t tokens = unit_tokens(groups[size_t(gi)]);
+                    int64_t t0 = 0;
+                    while (t0 < tokens) {
+                        // move on when the stripe cannot take one more block
+                        while (s < n_stripes - 1 && room < kValuTaskCost + kBlock) {
+                            ++s;
+                            room = level - base[size_t(s)];
+                        }
+                        int64_t take = tokens - t0;
+                        if (s < n_stripes - 1) {
+                            const int64_t fit = int64_t(std::floor((room - kValuTaskCost) / kBlock)) * kBlock;
+                            take = std::min(take, std::max<int64_t>(fit, kBlock));
+                        }
+                        take = std::min<int64_t>(take, kChunkCapTokens);
+                        if (out) {
+                            Piece pc;
+                            pc.group = gi;
+                            pc.tok0 = t0;
+                            pc.ntok = take;
+                            pc.last = t0 + take == tokens;
+                            pc.stripe = s;
+                            if (take < tokens) C = std::max(C, take);
+                            out->push_back(std::move(pc));
+                        }
+                        room -= double(take) + kValuTaskCost;
+                        t0 += take;
+                    }
+                }
+                if (room < 0) over = -room;
+                return over;
+            };
+            // lowest level at which the last stripe ends within one block of it
+            double lo = fill_level(base, valu_work), hi = lo;
+            while (fill(hi, nullptr) > kBlock + kValuTaskCost) hi += std::max(1.0, hi - lo) + kBlock;
+            for (int it = 0; it < 40 && hi - lo > 0.5; ++it) {
+                const double mid = 0.5 * (lo + hi);
+                (fill(mid, nullptr) > kBlock + kValuTaskCost ? lo : hi) = mid;
+            }
+            fill(hi, &best.pieces);
+        }
+        for (Piece& pc : best.pieces) pieces.push_back(std::move(pc));
+    }
+
+    // ---- items ----------------------------------------------------------------------
+    std::vector<Proto> protos;
+    std::vector<const Piece*> proto_piece;
+    for (const Piece& pc : pieces) {
+        const Group& g = groups[size_t(pc.group)];
+        const Unit& u = units[g.unit];
+        const bool has_fold = u.fold_query >= 0 &&
+                              std::find(g.queries.begin(), g.queries.end(), u.fold_query) != g.queries.end();
+        Proto p;
+        p.it.kind = g.kind;
+        p.it.tile = g.tile;
+        p.it.pos_begin = u.pos_begin + int(pc.tok0 / kBlock);
+        const int nblk = int((pc.ntok + kBlock - 1) / kBlock);
+        for (int j = 0; j < nblk; ++j) p.blocks.push_back(bt.id(u.ref_query, p.it.pos_begin + j));
+        int64_t item_tokens = pc.ntok;
+        for (int q : g.queries) {
+            Entry e{q, -1, int32_t(pc.ntok), 0};
+            if (has_fold && pc.last && q == u.fold_query) e.limit = int32_t(pc.ntok + u.fold_tokens);
+            p.entries.push_back(e);
+        }
+        if (has_fold && pc.last) {
+            for (int j = u.pos_end; j < u.fold_pos_end; ++j) p.blocks.push_back(bt.id(u.fold_query, j));
+            item_tokens = pc.ntok + u.fold_tokens;
+        }
+        if ((item_tokens + kBlock - 1) / kBlock > kMaxItemBlocks)
+            return set_error(KVATTN_EINVAL, "internal: item exceeds the per-item block cap");
+        p.it.n_tokens = int32_t(item_tokens);
+        p.it.n_q = int32_t(g.queries.size());
+        p.it.n_rows = g.rows;
+        p.cost = g.kind == KVATTN_VARIANT_MFMA ? mfma_cost(g, item_tokens) : double(item_tokens) + kValuTaskCost;
+        protos.push_back(std::move(p));
+        proto_piece.push_back(&pc);
+    }
+    auto proto_launch = [&](size_t i) { return launch_of(groups[size_t(proto_piece[i]->group)]); };
+
+    // ---- item order: by launch, MFMA before VALU; MFMA longest first, VALU in stream order
     std::vector<int> order(protos.size());
     std::iota(order.begin(), order.end(), 0);
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
-        const int la = launch_of(protos[a]), lb = launch_of(protos[b]);
+        const int la = proto_launch(size_t(a)), lb = proto_launch(size_t(b));
         if (la != lb) return la < lb;
-        return protos[a].cost > protos[b].cost;
+        const bool ma = protos[size_t(a)].it.kind == KVATTN_VARIANT_MFMA, mb = protos[size_t(b)].it.kind == KVATTN_VARIANT_MFMA;
+        if (ma != mb) return ma;
+        return ma && protos[size_t(a)].cost > protos[size_t(b)].cost;
     });
 
     // ---- destinations and merge map ----------------------------------------------------
@@ -576,11 +728,10 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     P.entries.clear();
     P.block_ids.clear();
     std::vector<std::vector<int32_t>> dests(B);
-    std::vector<double> item_cost;
-    std::vector<int> item_launch;
+    std::vector<int> item_proto;
     int32_t slots_used = 0;
     for (int idx : order) {
-        Proto& p = protos[idx];
+        Proto& p = protos[size_t(idx)];
         p.it.q_begin = int32_t(P.entries.size());
         p.it.blk_begin = int32_t(P.block_ids.size());
         for (Entry e : p.entries) {
@@ -593,8 +744,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         }
         P.block_ids.insert(P.block_ids.end(), p.blocks.begin(), p.blocks.end());
         P.items.push_back(p.it);
-        item_cost.push_back(p.cost);
-        item_launch.push_back(launch_of(p));
+        item_proto.push_back(idx);
     }
     P.n_slots = slots_used;
     P.merge_query.clear();
@@ -612,12 +762,9 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     }
 
     // ---- tasks: one static list per persistent workgroup -------------------------------------------
-    // MFMA tasks are placed first, longest first, each on the least-loaded
-    // list (an MFMA task of KV head g prefers a list of XCD g mod 8 --
-    // workgroup w runs on XCD w mod 8 -- so the row groups and chunks that read
-    // one KV head's shared range meet in one L2); then VALU tasks, longest
-    // first.  A list runs its MFMA tasks, then its VALU tasks as continuous
-    // per-wave streams, whose descriptors must fit the LDS window.
+    // A list runs its MFMA tasks (longest first), then its VALU tasks as
+    // continuous per-wave streams (in stream order), whose descriptors must fit
+    // the LDS window.
     P.tasks.clear();
     P.list_ptr.assign(size_t(n_launch) * (n_lists + 1), 0);
     P.forward_launches.clear();
@@ -625,67 +772,34 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     P.desc.clear();
     P.desc_list_ptr.assign(size_t(n_launch) * n_lists * 3, 0);
     for (int L = 0; L < n_launch; ++L) {
-        struct QT {
-            Task t;
-            double cost;
-            int pref;           // preferred XCD (MFMA), -1 for VALU
-            int32_t words;      // descriptor words
-        };
-        std::vector<QT> all;
-        for (size_t i = 0; i < P.items.size(); ++i) {
-            if (item_launch[i] != L) continue;
-            const Item& it = P.items[i];
-            const int32_t words = desc_words(it.n_q, (it.n_tokens + kBlock - 1) / kBlock);
-            if (it.kind == KVATTN_VARIANT_MFMA) {
-                for (int g = 0; g < Hkv; ++g) all.push_back({{int32_t(i), g}, item_cost[i], g % kXcds, words});
-            } else {
-                for (int g = 0; g < Hkv; g += kWaves) all.push_back({{int32_t(i), g}, item_cost[i], -1, words});
-            }
-        }
-        std::stable_sort(all.begin(), all.end(), [](const QT& a, const QT& b) {
-            const bool ma = a.pref >= 0, mb = b.pref >= 0;
-            if (ma != mb) return ma;
-            return a.cost > b.cost;
-        });
-        using LE = std::pair<double, int>;
-        using Heap = std::priority_queue<LE, std::vector<LE>, std::greater<LE>>;
-        Heap heap_all;
-        std::vector<Heap> heap_x(kXcds);
-        std::vector<double> load(size_t(n_lists), 0.0);
-        std::vector<int32_t> valu_words(size_t(n_lists), 0);
-        for (int w = 0; w < n_lists; ++w) {
-            heap_all.push({0.0, w});
-            heap_x[size_t(w % kXcds)].push({0.0, w});
-        }
-        auto top_of = [&](Heap& h) {
-            while (!h.empty() && h.top().first != load[size_t(h.top().second)]) h.pop();
-            return h.empty() ? -1 : h.top().second;
-        };
         const int launch_valu_rows = L < int(vt.size()) ? vt[size_t(L)] : 1;
         const int32_t window = valu_window_words(D, launch_valu_rows);
         std::vector<std::vector<Task>> mlist(static_cast<size_t>(n_lists)), vlist(static_cast<size_t>(n_lists));
-        for (const QT& t : all) {
-            int w = top_of(heap_all);
-            if (t.pref >= 0) {
-                const int wx = top_of(heap_x[size_t(t.pref)]);
-                if (wx >= 0 && load[size_t(wx)] <= load[size_t(w)] + 0.25 * t.cost) w = wx;
-                mlist[size_t(w)].push_back(t.t);
+        std::vector<int32_t> vwords(static_cast<size_t>(n_lists), 0);
+        for (size_t i = 0; i < P.items.size(); ++i) {
+            const int pi = item_proto[i];
+            if (proto_launch(size_t(pi)) != L) continue;
+            const Piece& pc = *proto_piece[size_t(pi)];
+            const Item& it = P.items[i];
+            if (it.kind == KVATTN_VARIANT_MFMA) {
+                for (int h = 0; h < Hkv; ++h) mlist[size_t(pc.head_list[size_t(h)])].push_back({int32_t(i), h});
             } else {
-                if (valu_words[size_t(w)] + t.words > window) {
-                    // no room in the least-loaded list's window: take the
-                    // least-loaded list that has room
-                    w = -1;
-                    for (int x = 0; x < n_lists; ++x)
-                        if (valu_words[size_t(x)] + t.words <= window && (w < 0 || load[size_t(x)] < load[size_t(w)]))
-                            w = x;
-                    if (w < 0) return set_error(KVATTN_EINVAL, "internal: VALU task descriptors exceed the LDS windows");
+                const int32_t words = desc_words(it.n_q, (it.n_tokens + kBlock - 1) / kBlock);
+                for (int q = 0; q < quads; ++q) {
+                    int w = pc.stripe * quads + q;
+                    if (vwords[size_t(w)] + words > window) {
+                        // the stripe's window is full: the least-filled list with room takes it
+                        int best_w = -1;
+                        for (int x = 0; x < n_lists; ++x)
+                            if (vwords[size_t(x)] + words <= window && (best_w < 0 || vwords[size_t(x)] < vwords[size_t(best_w)]))
+                                best_w = x;
+                        if (best_w < 0) return set_error(KVATTN_EINVAL, "internal: VALU task descriptors exceed the LDS windows");
+                        w = best_w;
+                    }
+                    vlist[size_t(w)].push_back({int32_t(i), q * kWaves});
+                    vwords[size_t(w)] += words;
                 }
-                vlist[size_t(w)].push_back(t.t);
-                valu_words[size_t(w)] += t.words;
             }
-            load[size_t(w)] += t.cost;
-            heap_all.push({load[size_t(w)], w});
-            heap_x[size_t(w % kXcds)].push({load[size_t(w)], w});
         }
         const int base = int(P.tasks.size());
         for (int w = 0; w < n_lists; ++w) {
