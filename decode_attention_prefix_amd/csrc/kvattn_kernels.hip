@@ -43,6 +43,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format,
 // no swizzle): reads past the resource's size return zero.
@@ -69,6 +70,26 @@ __device__ __forceinline__ float octet_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// v_max3_f32 without the NaN-quieting canonicalisations fmaxf adds for values
+// the compiler cannot prove canonical (MFMA results).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each 16-lane group,
+// lane a + 4e (a, e in [0, 4)) supplies the address of four 16-bit values; lane
+// 4a + c receives value c of the lanes a, a + 4, a + 8, a + 12, in that order.
+// `base` points into LDS; `off` is a byte offset.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* base, uint32_t off) {
+    typedef __attribute__((address_space(3))) char lds_char;
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const lds_char* b = (const lds_char*)(base);
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b + off));
+    return __builtin_bit_cast(uint2, r);
+}
 
 // s_waitcnt immediate (gfx9 encoding) waiting until at most N vector-memory
 // operations are outstanding; expcnt and lgkmcnt are left at their maximum.
@@ -493,13 +514,26 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
 // rows [16 t w, 16 t (w + 1)) as t = 1 or 2 sixteen-row tiles.  Per 32-token tile:
 //   S^T[16 tok x 16 rows] = K[16 x 32 d] . Q^T[32 d x 16 rows]   (4 k-steps at D = 128)
 //   O^T[16 d x 16 rows]  += V^T[16 d x 32 tok] . P^T[32 tok x 16 rows]
-// The head-dim index of O^T row m in output tile j is 8m + j (D = 128) or 4m + j
-// (D = 64), so each lane reads 16 (8) contiguous bytes of a V row and an 8 x 8
-// (8 x 4) register transpose yields the A operands of every output tile.
+// Output tile j holds head dims [16j, 16j + 16).  Its A operand V^T (16 d x 32
+// tokens) comes straight from the row-major V tile through two transposing LDS
+// reads (tokens 4lg + e, then 16 + 4lg + e), the token order of the P^T operand.
 // P is split into bf16 hi + lo parts (two MFMAs) so the weights keep ~16 bits.
-// K and V tiles live in LDS in rows of D/8 16-byte chunks, chunk index XOR
-// (token mod D/8) to keep the 16 row-strided reads of an operand conflict free.
+// K and V tiles live in LDS in rows of D/8 16-byte chunks, permuted per token
+// row so that both reads are bank-conflict free: K chunk c of token t sits at
+// c ^ (t mod D/8) (16 row-strided 16-byte reads), V chunk c at c ^ vswz(t) (the
+// transposing read takes 4 or 8 rows at one 32-byte column).
 // ============================================================================
+// V chunk permutation of token row t (t mod 16 suffices): XOR with an even
+// value, so the two chunks of a 32-byte column stay together, and the rows
+// t = 0..7 land that column on 8 distinct 32-byte bank groups (4 at D = 64).
+template <int D>
+__device__ __forceinline__ int vswz(int t) {
+    if constexpr (D == 128)
+        return ((t & 3) << 1) | (((t >> 2) & 1) << 3);
+    else
+        return ((t & 3) ^ ((t >> 2) & 1)) << 1;
+}
+
 template <int D, int TPW>
 __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, const TaskView& it, int g,
                                           const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
@@ -565,6 +599,7 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
     static_assert(LPT == 1 || (NT / CPR) % 16 == 0, "DMA chunk stride");
     const int tok0 = tid / CPR;
     const int off0 = (tok0 & 15) * D + ((tid % CPR) ^ (tok0 & (CPR - 1))) * 8;
+    const int offv0 = (tok0 & 15) * D + ((tid % CPR) ^ vswz<D>(tok0)) * 8;
     const uint32_t lds_base = uint32_t(uintptr_t(s_kv));
     auto issue_tile = [&](int i) {
         const uint32_t st = lds_base + uint32_t((i % NS) * STAGE * 2);
@@ -577,10 +612,10 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
             if (u * NT + wave * 64 >= TCH) continue;    // wave-uniform: waves past the tile issue nothing
             const int tok = tok0 + u * (NT / CPR);
             const bool ok = i * TT + tok < n_tok;
-            const size_t o = (tok < 16 ? o0 : o1) + off0;
+            const size_t ob = tok < 16 ? o0 : o1;
             const uint32_t dst = st + uint32_t((u * NT + wave * 64) * 16);
-            dma16(ok ? static_cast<const void*>(kh + o) : static_cast<const void*>(p.zero), dst);
-            dma16(ok ? static_cast<const void*>(vh + o) : static_cast<const void*>(p.zero), dst + TT * D * 2);
+            dma16(ok ? static_cast<const void*>(kh + ob + off0) : static_cast<const void*>(p.zero), dst);
+            dma16(ok ? static_cast<const void*>(vh + ob + offv0) : static_cast<const void*>(p.zero), dst + TT * D * 2);
         }
     };
 
@@ -595,36 +630,52 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
     }
     const float sl2 = dm.scale_log2;
 
-    // per-lane LDS element offsets of the K (A of QK) and V (to be transposed)
-    // operands for token half 0; half 1 adds 16 rows (the XOR swizzle only sees
-    // token mod 16, which both halves share)
+    // per-lane LDS offsets of the K operand (A of QK, elements) and of the
+    // transposing V reads (bytes, output tile j) for token half 0; half 1 adds 16
+    // rows (both permutations only see token mod 16, which the halves share).
+    // Lane a + 4e of a 16-lane group addresses token 4lg + e, head dims
+    // 16j + 4a .. 16j + 4a + 3.
     constexpr int HALF = 16 * CPR * 8;
-    int koff[KS], voff[4];
+    int koff[KS];
+    uint32_t vtr[NDT];
 #pragma unroll
     for (int s = 0; s < KS; ++s) koff[s] = (lr * CPR + ((4 * s + lg) ^ (lr & (CPR - 1)))) * 8;
+    {
+        const int t = 4 * lg + (lr >> 2);
+        const int sw = vswz<D>(t);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int tok = 4 * lg + u;
-        if constexpr (D == 128)
-            voff[u] = TT * D + (tok * CPR + (lr ^ (tok & (CPR - 1)))) * 8;
-        else
-            voff[u] = TT * D + (tok * CPR + ((lr >> 1) ^ (tok & (CPR - 1)))) * 8 + (lr & 1) * 4;
+        for (int j = 0; j < NDT; ++j)
+            vtr[j] = uint32_t(2 * (TT * D + t * D) + ((2 * j + ((lr & 3) >> 1)) ^ sw) * 16 + (lr & 1) * 8);
+        // vtr[j] reads head dims 16j + 4(lr mod 4) .. + 3 of token t
+
     }
 
     auto compute = [&](int i, const uint16_t* sb) {
         if (!active) return;
+        // ---- LDS reads of the whole tile: K operands, then the V^T operands (lane
+        // (m, lg) of output tile j gets head dim 16j + m of tokens 4lg + e and
+        // 16 + 4lg + e), whose latency the QK products and the softmax hide
+        bf16x8 kop[2][KS];
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) kop[half][s] = *reinterpret_cast<const bf16x8*>(sb + koff[s] + half * HALF);
+        uint2 vr[NDT][2];
+#pragma unroll
+        for (int j = 0; j < NDT; ++j) {
+            vr[j][0] = lds_read_tr16(sb, vtr[j]);
+            vr[j][1] = lds_read_tr16(sb, vtr[j] + 2 * HALF);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         // ---- S^T tiles (unscaled q.k)
         f32x4 sc[TPW][2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            bf16x8 kop[KS];
-#pragma unroll
-            for (int s = 0; s < KS; ++s) kop[s] = *reinterpret_cast<const bf16x8*>(sb + koff[s] + half * HALF);
 #pragma unroll
             for (int rt = 0; rt < TPW; ++rt) {
                 f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < KS; ++s) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[s], qop[rt][s], a, 0, 0, 0);
+                for (int s = 0; s < KS; ++s) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[half][s], qop[rt][s], a, 0, 0, 0);
                 sc[rt][half] = a;
             }
         }
@@ -644,9 +695,9 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
         float tmax[TPW];
 #pragma unroll
         for (int rt = 0; rt < TPW; ++rt) {
-            const float m4a = fmaxf(fmaxf(sc[rt][0][0], sc[rt][0][1]), fmaxf(sc[rt][0][2], sc[rt][0][3]));
-            const float m4b = fmaxf(fmaxf(sc[rt][1][0], sc[rt][1][1]), fmaxf(sc[rt][1][2], sc[rt][1][3]));
-            tmax[rt] = fmaxf(m4a, m4b) * sl2;
+            const float m3a = max3f(sc[rt][0][0], sc[rt][0][1], sc[rt][0][2]);
+            const float m3b = max3f(sc[rt][0][3], sc[rt][1][0], sc[rt][1][1]);
+            tmax[rt] = max3f(m3a, m3b, fmaxf(sc[rt][1][2], sc[rt][1][3])) * sl2;
             need |= tmax[rt] > mref[rt] + kRescaleLog2;
         }
         if (__any(need)) {
@@ -684,27 +735,10 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
             plo[rt] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
         }
         __builtin_amdgcn_sched_barrier(0);
-        // ---- V^T operands, built one output tile at a time from an 8 x 8 (8 x 4) register block
-        constexpr int RAWW = D == 128 ? 4 : 2;   // dwords per lane per token
-        uint32_t raw[8][RAWW];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const uint16_t* src = sb + voff[u & 3] + (u >> 2) * HALF;
-            if constexpr (D == 128) {
-                const uint4 r4 = *reinterpret_cast<const uint4*>(src);
-                raw[u][0] = r4.x; raw[u][1] = r4.y; raw[u][2] = r4.z; raw[u][3] = r4.w;
-            } else {
-                const uint2 r2 = *reinterpret_cast<const uint2*>(src);
-                raw[u][0] = r2.x; raw[u][1] = r2.y;
-            }
-        }
+        // ---- O^T += V^T P^T
 #pragma unroll
         for (int j = 0; j < NDT; ++j) {
-            uint32_t w[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-                w[x] = __builtin_amdgcn_perm(raw[2 * x + 1][j >> 1], raw[2 * x][j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
-            const bf16x8 vt = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+            const bf16x8 vt = __builtin_bit_cast(bf16x8, make_uint4(vr[j][0].x, vr[j][0].y, vr[j][1].x, vr[j][1].y));
 #pragma unroll
             for (int rt = 0; rt < TPW; ++rt) {
                 acc[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, phi[rt], acc[rt][j], 0, 0, 0);
@@ -733,7 +767,7 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
         compute(i, s_kv + (i % NS) * STAGE);
     }
 
-    // ---- epilogue: lane holds row lr of each tile, head dims of output tile j, row m = 4lg + e
+    // ---- epilogue: lane holds row lr of each tile and, in output tile j, head dims 16j + 4lg + e
 #pragma unroll
     for (int rt = 0; rt < TPW; ++rt) {
         if (!active) continue;
@@ -755,26 +789,10 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
             scale = 1.f;
             if (lg == 0) *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(mref[rt], lt);
         }
-        if constexpr (D == 128) {
-            // d = 8 * (4lg + e) + j = 32lg + 8e + j
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                float4 a = make_float4(acc[rt][0][e4] * scale, acc[rt][1][e4] * scale, acc[rt][2][e4] * scale,
-                                       acc[rt][3][e4] * scale);
-                float4 b = make_float4(acc[rt][4][e4] * scale, acc[rt][5][e4] * scale, acc[rt][6][e4] * scale,
-                                       acc[rt][7][e4] * scale);
-                *reinterpret_cast<float4*>(dst + 32 * lg + 8 * e4) = a;
-                *reinterpret_cast<float4*>(dst + 32 * lg + 8 * e4 + 4) = b;
-            }
-        } else {
-            // d = 4 * (4lg + e) + j = 16lg + 4e + j
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                float4 a = make_float4(acc[rt][0][e4] * scale, acc[rt][1][e4] * scale, acc[rt][2][e4] * scale,
-                                       acc[rt][3][e4] * scale);
-                *reinterpret_cast<float4*>(dst + 16 * lg + 4 * e4) = a;
-            }
-        }
+        for (int j = 0; j < NDT; ++j)
+            *reinterpret_cast<float4*>(dst + 16 * j + 4 * lg) =
+                make_float4(acc[rt][j][0] * scale, acc[rt][j][1] * scale, acc[rt][j][2] * scale, acc[rt][j][3] * scale);
     }
 }
 
