@@ -33,7 +33,7 @@ constexpr int kMaxItemBlocks = 512;     // KV blocks per item (8192 tokens)
 constexpr int kMaxGroup = 64;           // q heads per KV head supported
 constexpr int kXcds = 8;                // XCDs of an MI355X (L2 domains)
 constexpr uint32_t kBlobMagic = 0x4B564154u;  // "KVAT"
-constexpr uint32_t kBlobVersion = 5;
+constexpr uint32_t kBlobVersion = 6;
 
 // Device view of one item; identical layout to kvattn_item_info.
 struct Item {
@@ -97,14 +97,16 @@ struct BlobHeader {
     uint64_t off_desc;        // int32 [n_desc_words]: task descriptors
     uint64_t off_list_ptr;    // int32 [n_launches][n_lists][3]: word offsets (MFMA begin, VALU begin, end) per list
     uint64_t off_merge_query, off_merge_ptr, off_merge_dest, off_zero;
+    uint64_t off_claim;       // int32: list claim counter, zero between launches
     uint64_t blob_bytes;      // bytes copied by kvattn_plan_upload
     uint64_t off_part_ml;     // float2 [n_slots]: (m in log2 units, l)
     uint64_t off_part_acc;    // float [n_slots][head_dim]
     uint64_t total_bytes;     // workspace bytes
 };
 
-// One forward launch: persistent workgroups, each running one static list
-// (MFMA tasks, then VALU tasks as per-wave streams).  A plan needs more than
+// One forward launch: persistent workgroups, each running static list
+// blockIdx.x, then lists claimed at run time (MFMA tasks, then VALU tasks as
+// per-wave streams).  A plan needs more than
 // one only when its VALU items use several row templates or its MFMA items
 // several row tilings.
 struct Launch {
@@ -124,6 +126,7 @@ struct DevPlan {
     const int32_t* merge_ptr;
     const int32_t* merge_dest;
     const uint16_t* zero;       // >= 256 zero bytes: source for token slots outside a range
+    int32_t* claim;             // list claim counter (zero between launches)
     float* part_ml;
     float* part_acc;
 };

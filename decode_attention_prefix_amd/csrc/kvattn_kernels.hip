@@ -99,6 +99,15 @@ constexpr int waitcnt_vm() {
     return (N & 0xF) | ((N >> 4) << 14) | 0x0F70;
 }
 
+// Zero in a VGPR the compiler cannot see through.  An atomic on an address
+// offset by it is not turned into a wave-aggregated atomic (whose expansion
+// waits for the result at once); the result's wait lands at its first use.
+__device__ __forceinline__ int opaque_zero() {
+    int v;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(v));
+    return v;
+}
+
 // Lane index, read by an instruction the compiler neither hoists nor merges.
 __device__ __forceinline__ int lane_id_volatile() {
     int v;
@@ -837,7 +846,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     // All control flow below is wave-uniform: the loops hold barriers, so
     // lane-divergent branches must stay out of their exits and back edges.
-    for (int w = blockIdx.x; w < p.n_lists; w += gridDim.x) {
+    //
+    // Lists [0, gridDim.x) run one per workgroup; the rest are claimed in order
+    // from a counter in the workspace.  A workgroup asks for its next list when
+    // it starts one (the atomic's latency hides behind the list's first loads)
+    // and reads the answer when the list ends.  The claims of a launch draw
+    // 0 .. n_lists - 1 once each (valid ones, plus one failing claim per
+    // workgroup), so the workgroup that draws n_lists - 1 made the launch's
+    // last claim and returns the counter to zero for the next launch.
+    __shared__ int s_next[2];
+    const bool claims = p.n_lists > int(gridDim.x);
+    int w = blockIdx.x;
+    for (int round = 0; w < p.n_lists; ++round) {
+        int ticket = 0;
+        if (claims && threadIdx.x == 0) ticket = atomicAdd(p.claim + opaque_zero(), 1);
         const KV_CONST int32_t* lp = cptr(p.list_ptr) + 3 * w;
         const int m0 = lp[0], v0 = lp[1], e0 = lp[2];
         // ---- MFMA tasks: the next descriptor lies right after the current one
@@ -871,6 +893,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             valu_stream<D, R>(p, dm, win, e0 - v0, qs, q, kc, vc, out);
             wait_all_and_sync();   // the window is free for the next list
         }
+        if (!claims) break;
+        if (threadIdx.x == 0) {
+            if (ticket == p.n_lists - 1) __hip_atomic_store(p.claim, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_next[round & 1] = int(gridDim.x) + ticket;
+        }
+        __syncthreads();
+        w = __builtin_amdgcn_readfirstlane(s_next[round & 1]);
     }
 }
 
@@ -945,8 +974,8 @@ int launch_fwd_t(const DevPlan& p, const Dims& d, int n_tasks, const uint16_t* q
                  const uint16_t* v, float* out, hipStream_t s) {
     static int slots = 0;
     (void)n_tasks;
-    // one workgroup per static list when they all fit at once; otherwise
-    // workgroup w also runs lists w + grid, w + 2 grid, ...
+    // one workgroup per list when they all fit at once; otherwise the
+    // workgroups claim the lists past the grid as they finish theirs
     const int grid = persistent_grid(fwd_kernel<D, R, TPW>, &slots, p.n_lists);
     if (grid < 0) return int(hipErrorInvalidDevice);
     hipLaunchKernelGGL((fwd_kernel<D, R, TPW>), dim3(grid), dim3(256), 0, s, p, d, q, k, v, out);

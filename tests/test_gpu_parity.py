@@ -107,6 +107,29 @@ def test_parity_small_configs_forced_variant(c, variant, scheme, split):
     assert_close(got, oracle_out(wl), "%s variant %d scheme %d split %d" % (wl.name, variant, scheme, split))
 
 
+@pytest.mark.parametrize("c", [2, 3, 5])
+@pytest.mark.parametrize("variant", [-1, 0, 1])
+def test_parity_lists_claimed_past_the_grid(c, variant):
+    """A plan for more workgroup slots than the GPU has (num_cus 1024: 2048
+    lists) leaves the lists past the grid to run-time claims.  Two decodes in
+    a row: the claim counter must be back at zero after the first."""
+    wl = small(c)
+    if variant == 0 and wl.group > valu_max_rows(wl.head_dim):
+        pytest.skip("VALU rows limit")
+    k = K()
+    print("case %s claims variant %d" % (wl.name, variant), flush=True)
+    dec = k.Decoder(wl.shape_tuple(), wl.block_tables, wl.seq_lens,
+                    options=k.make_options(num_cus=1024, force_variant=variant))
+    q, kc, vc = device_inputs(wl)
+    for rep in range(2):
+        out = torch.full((wl.num_queries, wl.num_q_heads, wl.head_dim), float("nan"), dtype=torch.float32,
+                         device="cuda")
+        dec.decode(q, kc, vc, out)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy().astype(np.float64), oracle_out(wl),
+                     "%s claims variant %d decode %d" % (wl.name, variant, rep))
+
+
 def valu_max_rows(D):
     """Rows per KV head the VALU forward holds (the planner's limit)."""
     return 4 if D == 128 else 8
