@@ -33,7 +33,7 @@ constexpr int kMaxItemBlocks = 512;     // KV blocks per item (8192 tokens)
 constexpr int kMaxGroup = 64;           // q heads per KV head supported
 constexpr int kXcds = 8;                // XCDs of an MI355X (L2 domains)
 constexpr uint32_t kBlobMagic = 0x4B564154u;  // "KVAT"
-constexpr uint32_t kBlobVersion = 6;
+constexpr uint32_t kBlobVersion = 7;
 
 // Device view of one item; identical layout to kvattn_item_info.
 struct Item {
@@ -96,7 +96,7 @@ struct BlobHeader {
     int32_t n_tasks, n_launches, n_lists, pad0;
     uint64_t off_desc;        // int32 [n_desc_words]: task descriptors
     uint64_t off_list_ptr;    // int32 [n_launches][n_lists][3]: word offsets (MFMA begin, VALU begin, end) per list
-    uint64_t off_merge_query, off_merge_ptr, off_merge_dest, off_zero;
+    uint64_t off_merge_query, off_merge_ptr, off_merge_dest;
     uint64_t off_claim;       // int32: list claim counter, zero between launches
     uint64_t blob_bytes;      // bytes copied by kvattn_plan_upload
     uint64_t off_part_ml;     // float2 [n_slots]: (m in log2 units, l)
@@ -125,7 +125,6 @@ struct DevPlan {
     const int32_t* merge_query;
     const int32_t* merge_ptr;
     const int32_t* merge_dest;
-    const uint16_t* zero;       // >= 256 zero bytes: source for token slots outside a range
     int32_t* claim;             // list claim counter (zero between launches)
     float* part_ml;
     float* part_acc;

@@ -136,6 +136,35 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
         : "memory");
 }
 
+// Buffer resource (raw, 32-bit data format) over `bytes` bytes at `base`.
+// All inputs must be wave-uniform: the result lives in SGPRs.
+__device__ __forceinline__ u32x4 raw_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = uint64_t(uintptr_t(base));
+    u32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane(uint32_t(a));
+    r.y = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32) & 0xFFFFu);   // base[47:32]; stride 0, no swizzle
+    r.z = __builtin_amdgcn_readfirstlane(bytes);
+    r.w = uint32_t(kBufferWord3);
+    return r;
+}
+
+// Buffer -> LDS copy of 16 bytes per lane: lane i reads bytes [voff, voff + 16)
+// of the resource and writes LDS bytes [lds + 16 i, lds + 16 i + 16); dwords
+// past the resource's size are written as zeros.  Inline assembly for the same
+// reason as dma16; M0 is saved and restored around the copy.
+__device__ __forceinline__ void dma16_buf(u32x4 rsrc, uint32_t voff, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(rsrc)
+        : "memory");
+}
+
 // Schedule arrays are read-only for a whole launch: reading them through the
 // constant address space lets uniform reads become scalar (SMEM) loads, which
 // do not count against vmcnt and so never stall the in-flight KV loads.
@@ -606,25 +635,31 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
     // chunk u of this thread is token tok0 + u * (NT / CPR): the same row offset in
     // every u, since NT / CPR is a multiple of 16 (or LPT is 1)
     static_assert(LPT == 1 || (NT / CPR) % 16 == 0, "DMA chunk stride");
+    // Each copy instruction of a wave covers 64 consecutive chunks, i.e. whole
+    // token rows of one block (16 rows at D = 128 per u, 8 rows at D = 64 per
+    // wave), so the block and its buffer resource are wave-uniform.  A block's
+    // resource spans its valid tokens: rows past the range land in LDS as zeros.
     const int tok0 = tid / CPR;
-    const int off0 = (tok0 & 15) * D + ((tid % CPR) ^ (tok0 & (CPR - 1))) * 8;
-    const int offv0 = (tok0 & 15) * D + ((tid % CPR) ^ vswz<D>(tok0)) * 8;
+    const uint32_t voff_k = uint32_t((tok0 & 15) * D + ((tid % CPR) ^ (tok0 & (CPR - 1))) * 8) * 2;
+    const uint32_t voff_v = uint32_t((tok0 & 15) * D + ((tid % CPR) ^ vswz<D>(tok0)) * 8) * 2;
     const uint32_t lds_base = uint32_t(uintptr_t(s_kv));
     auto issue_tile = [&](int i) {
         const uint32_t st = lds_base + uint32_t((i % NS) * STAGE * 2);
         const int kb = 2 * i;
         const int blk0 = __builtin_amdgcn_readfirstlane(s_blk[kb]);
         const int blk1 = __builtin_amdgcn_readfirstlane(kb + 1 < nblk ? s_blk[kb + 1] : blk0);
-        const size_t o0 = size_t(blk0) * blk_elems, o1 = size_t(blk1) * blk_elems;
+        const int rem = n_tok - kb * kBlock;   // tokens from this tile's first block on (>= 1)
+        const uint32_t bytes0 = uint32_t(min(rem, kBlock)) * D * 2;
+        const uint32_t bytes1 = uint32_t(max(0, min(rem - kBlock, kBlock))) * D * 2;
 #pragma unroll
         for (int u = 0; u < LPT; ++u) {
             if (u * NT + wave * 64 >= TCH) continue;    // wave-uniform: waves past the tile issue nothing
-            const int tok = tok0 + u * (NT / CPR);
-            const bool ok = i * TT + tok < n_tok;
-            const size_t ob = tok < 16 ? o0 : o1;
+            const bool second = (u * NT + wave * 64) / CPR >= kBlock;   // wave-uniform
+            const size_t ob = size_t(second ? blk1 : blk0) * blk_elems;
+            const uint32_t nb = second ? bytes1 : bytes0;
             const uint32_t dst = st + uint32_t((u * NT + wave * 64) * 16);
-            dma16(ok ? static_cast<const void*>(kh + ob + off0) : static_cast<const void*>(p.zero), dst);
-            dma16(ok ? static_cast<const void*>(vh + ob + offv0) : static_cast<const void*>(p.zero), dst + TT * D * 2);
+            dma16_buf(raw_rsrc(kh + ob, nb), voff_k, dst);
+            dma16_buf(raw_rsrc(vh + ob, nb), voff_v, dst + TT * D * 2);
         }
     };
 

@@ -857,7 +857,6 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     h.off_merge_query = off;  off = align256(off + P.merge_query.size() * 4);
     h.off_merge_ptr = off;    off = align256(off + P.merge_ptr.size() * 4);
     h.off_merge_dest = off;   off = align256(off + P.merge_dest.size() * 4);
-    h.off_zero = off;         off = align256(off + 256);
     h.off_claim = off;        off = align256(off + 4);
     h.blob_bytes = off;
     h.off_part_ml = off;      off = align256(off + uint64_t(slots_used) * 8);

@@ -22,7 +22,6 @@ DevPlan resolve(const kvattn_plan_s& P, int launch) {
     d.merge_query = reinterpret_cast<const int32_t*>(base + h.off_merge_query);
     d.merge_ptr = reinterpret_cast<const int32_t*>(base + h.off_merge_ptr);
     d.merge_dest = reinterpret_cast<const int32_t*>(base + h.off_merge_dest);
-    d.zero = reinterpret_cast<const uint16_t*>(base + h.off_zero);
     d.claim = reinterpret_cast<int32_t*>(base + h.off_claim);
     d.part_ml = reinterpret_cast<float*>(base + h.off_part_ml);
     d.part_acc = reinterpret_cast<float*>(base + h.off_part_acc);
