@@ -643,8 +643,8 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
     const uint32_t voff_k = uint32_t((tok0 & 15) * D + ((tid % CPR) ^ (tok0 & (CPR - 1))) * 8) * 2;
     const uint32_t voff_v = uint32_t((tok0 & 15) * D + ((tid % CPR) ^ vswz<D>(tok0)) * 8) * 2;
     const uint32_t lds_base = uint32_t(uintptr_t(s_kv));
-    auto issue_tile = [&](int i) {
-        const uint32_t st = lds_base + uint32_t((i % NS) * STAGE * 2);
+    auto issue_tile = [&](int i, int stage) {
+        const uint32_t st = lds_base + uint32_t(stage * STAGE * 2);
         const int kb = 2 * i;
         const int blk0 = __builtin_amdgcn_readfirstlane(s_blk[kb]);
         const int blk1 = __builtin_amdgcn_readfirstlane(kb + 1 < nblk ? s_blk[kb + 1] : blk0);
@@ -773,7 +773,11 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 hi[x] = pack_bf16(pv[2 * x], pv[2 * x + 1]);
-                lo[x] = pack_bf16(pv[2 * x] - bf_lo(hi[x]), pv[2 * x + 1] - bf_hi(hi[x]));
+                // low half moved up by v_perm_b32 (bytes 4, 5 are the first operand's low
+                // half; selector 0x0c gives a zero byte), which the compiler does not
+                // rewrite into a second conversion
+                const float h0 = __uint_as_float(__builtin_amdgcn_perm(hi[x], 0u, 0x05040c0cu));
+                lo[x] = pack_bf16(pv[2 * x] - h0, pv[2 * x + 1] - bf_hi(hi[x]));
             }
             phi[rt] = __builtin_bit_cast(bf16x8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
             plo[rt] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
@@ -792,23 +796,32 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
     };
 
     // ---- NS-stage pipeline: tiles i+1 .. i+NS-1 stream in while tile i is computed ----
+// Unrolled by NS so that every stage offset is a constant: LDS reads then
+    // take it in their offset field instead of a vector add per address.
+    static_assert(NS == 4, "the wait counts below assume at most two younger tiles");
 #pragma unroll
     for (int i = 0; i < NS - 1; ++i)
-        if (i < ntiles) issue_tile(i);
-    for (int i = 0; i < ntiles; ++i) {
-        // this thread's DMA for tile i is complete once at most the loads of the
-        // (up to NS - 2) younger tiles remain outstanding
-        const int younger = min(ntiles - 1 - i, NS - 2);
-        if (younger >= 2) {
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm<4 * LPT>());
-        } else if (younger == 1) {
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm<2 * LPT>());
-        } else {
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
+        if (i < ntiles) issue_tile(i, i);
+    for (int i0 = 0; i0 < ntiles; i0 += NS) {
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            const int i = i0 + st;
+            if (i < ntiles) {
+                // this thread's DMA for tile i is complete once at most the loads of the
+                // (up to NS - 2) younger tiles remain outstanding
+                const int younger = min(ntiles - 1 - i, NS - 2);
+                if (younger >= 2) {
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm<4 * LPT>());
+                } else if (younger == 1) {
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm<2 * LPT>());
+                } else {
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
+                }
+                __builtin_amdgcn_s_barrier();   // every wave's DMA for tile i landed; tile i-1 is consumed
+                if (i + NS - 1 < ntiles) issue_tile(i + NS - 1, (st + NS - 1) % NS);
+                compute(i, s_kv + st * STAGE);
+            }
         }
-        __builtin_amdgcn_s_barrier();   // every wave's DMA for tile i landed; tile i-1 is consumed
-        if (i + NS - 1 < ntiles) issue_tile(i + NS - 1);
-        compute(i, s_kv + (i % NS) * STAGE);
     }
 
     // ---- epilogue: lane holds row lr of each tile and, in output tile j, head dims 16j + 4lg + e
