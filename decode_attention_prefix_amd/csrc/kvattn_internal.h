@@ -29,7 +29,9 @@ constexpr int kWaves = 4;               // waves per forward workgroup (both pat
 constexpr int kMfmaMaxRows = 128;       // rows per MFMA item: 4 waves x 32 rows
 constexpr int kMfmaTileTokens = 32;     // KV tokens per LDS stage
 constexpr int kMfmaStages = 4;          // LDS stages of the MFMA pipeline (3 tiles in flight)
-constexpr int kMaxItemBlocks = 512;     // KV blocks per item (8192 tokens)
+constexpr int kMaxItemBlocks = 512;     // KV blocks per VALU item (8192 tokens): descriptors share the VALU LDS window
+constexpr int kMfmaMaxItemBlocks = 1408;  // KV blocks per MFMA item (22528 tokens): two descriptors beside the 64 KB
+                                          // of MFMA stages keep a workgroup within 80 KB of LDS (two per CU)
 constexpr int kMaxGroup = 64;           // q heads per KV head supported
 constexpr int kXcds = 8;                // XCDs of an MI355X (L2 domains)
 constexpr uint32_t kBlobMagic = 0x4B564154u;  // "KVAT"
@@ -80,7 +82,7 @@ enum : int {
     kDescHeader = 16
 };
 constexpr int kMaxItemQueries = kMfmaMaxRows;   // rows per item >= queries per item
-constexpr int kDescMaxWords = kDescHeader + 4 * kMaxItemQueries + kMaxItemBlocks;
+constexpr int kDescMaxWords = kDescHeader + 4 * kMaxItemQueries + kMfmaMaxItemBlocks;
 inline int32_t desc_words(int n_q, int nblk) { return kDescHeader + 4 * n_q + ((nblk + 3) & ~3); }
 
 // LDS window of the VALU phase: the MFMA stages (kMfmaStages x 2 x 32 tokens x

@@ -891,6 +891,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     static_assert(KV_ELEMS * 2 == WIN * 4 + kWaves * 4 * R * D * 2, "VALU window layout");
     __shared__ __attribute__((aligned(16))) uint16_t s_kv[KV_ELEMS];
     __shared__ __attribute__((aligned(16))) int32_t s_desc[2][kDescMaxWords];
+    static_assert(D != 128 || KV_ELEMS * 2 + sizeof(s_desc) + 64 <= 80 * 1024, "two workgroups per CU");
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     // All control flow below is wave-uniform: the loops hold barriers, so
     // lane-divergent branches must stay out of their exits and back edges.

@@ -198,9 +198,11 @@ int next_pow2(int x) {
 
 int64_t ceil16(int64_t x) { return (x + kBlock - 1) / kBlock * kBlock; }
 
-// Item size caps: a chunk plus a folded leaf stays within kMaxItemBlocks blocks.
+// Item size caps: a chunk plus a folded leaf stays within kMaxItemBlocks
+// (VALU) or kMfmaMaxItemBlocks (MFMA) blocks.
 constexpr int64_t kFoldCapTokens = 256;
 constexpr int64_t kChunkCapTokens = int64_t(kMaxItemBlocks) * kBlock - kFoldCapTokens;
+constexpr int64_t kMfmaChunkCapTokens = int64_t(kMfmaMaxItemBlocks) * kBlock - kFoldCapTokens;
 
 // Task costs, in units of one wave streaming one KV head-token with every CU
 // busy (about 0.18 us on MI355X: 512 bytes at 1/2048 of the HBM bandwidth).
@@ -307,7 +309,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     int folded = 0;
     if (o.scheme != 1) {
         // a folded leaf rides on the parent's last chunk; the cap keeps an item
-        // within kMaxItemBlocks together with the chunk cap below
+        // within the item block caps together with the chunk caps below
         const int64_t fold_max = o.scheme == 2 ? kFoldCapTokens : 128;
         for (size_t ni = 0; ni < nodes.size(); ++ni) {
             Node& n = nodes[ni];
@@ -510,10 +512,10 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
                 const int64_t tokens = unit_tokens(g);
                 int64_t chunk;
                 if (o.split_tokens > 0) {
-                    chunk = std::min<int64_t>(ceil16(o.split_tokens), kChunkCapTokens);
+                    chunk = std::min<int64_t>(ceil16(o.split_tokens), kMfmaChunkCapTokens);
                 } else {
                     chunk = ceil16(int64_t(std::ceil((target - kMfmaTaskCost) / g.w)));
-                    chunk = std::min<int64_t>(std::max<int64_t>(chunk, 128), kChunkCapTokens);
+                    chunk = std::min<int64_t>(std::max<int64_t>(chunk, 128), kMfmaChunkCapTokens);
                 }
                 const int64_t nch = (tokens + chunk - 1) / chunk;
                 const int64_t len = ceil16((tokens + nch - 1) / nch);
@@ -698,7 +700,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             for (int j = u.pos_end; j < u.fold_pos_end; ++j) p.blocks.push_back(bt.id(u.fold_query, j));
             item_tokens = pc.ntok + u.fold_tokens;
         }
-        if ((item_tokens + kBlock - 1) / kBlock > kMaxItemBlocks)
+        if ((item_tokens + kBlock - 1) / kBlock > (g.kind == KVATTN_VARIANT_MFMA ? kMfmaMaxItemBlocks : kMaxItemBlocks))
             return set_error(KVATTN_EINVAL, "internal: item exceeds the per-item block cap");
         p.it.n_tokens = int32_t(item_tokens);
         p.it.n_q = int32_t(g.queries.size());

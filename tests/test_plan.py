@@ -32,7 +32,7 @@ def check_coverage(wl_bt, seq_lens, Hq, Hkv, ex):
         else:
             assert it["tile"][i] in (1, 2) and it["n_rows"][i] <= 64 * it["tile"][i]
         nblk = (n_tok + 15) // 16
-        assert nblk <= 512
+        assert nblk <= (512 if it["kind"][i] == K.KVATTN_VARIANT_VALU else 1408)
         blk = ids[int(it["blk_begin"][i]): int(it["blk_begin"][i]) + nblk]
         assert blk.size == nblk
         assert any(int(en["limit"][q0 + k]) == n_tok for k in range(nq))
@@ -77,7 +77,7 @@ def check_coverage(wl_bt, seq_lens, Hq, Hkv, ex):
     check_descriptors(ex)
 
 
-DESC_MAX_WORDS = 16 + 4 * 128 + 512
+DESC_MAX_WORDS = 16 + 4 * 128 + 1408
 
 
 def check_descriptors(ex):
