@@ -587,6 +587,9 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         if (!mg.empty() && o.split_tokens <= 0) {
             targets.push_back(2.0 * mean0);
             for (int i = 1; i <= 24; ++i) targets.push_back(mean0 * std::pow(2.0, -i / 4.0));
+            // task costs at which the MFMA work makes whole numbers of tasks per list
+            for (int k = 1; k <= 8; ++k)
+                targets.push_back((w_mfma + double(k) * n_lists * kMfmaTaskCost) / (double(k) * n_lists));
         }
         for (double target : targets) {
             MfmaPlan mp = place_mfma(target);
