@@ -21,6 +21,7 @@
 #include <new>
 #include <numeric>
 #include <queue>
+#include <set>
 #include <string>
 #include <vector>
 
@@ -493,6 +494,17 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         for (int gi : mg) w_mfma += double(unit_tokens(groups[gi])) * groups[gi].w * Hkv;
         const double mean0 = std::max(64.0, (w_valu + w_mfma) / n_lists);
 
+        // chunks of MFMA group g at a target task cost `target`
+        auto mfma_chunks = [&](const Group& g, double target) {
+            int64_t chunk;
+            if (o.split_tokens > 0) {
+                chunk = std::min<int64_t>(ceil16(o.split_tokens), kMfmaChunkCapTokens);
+            } else {
+                chunk = ceil16(int64_t(std::ceil((target - kMfmaTaskCost) / g.w)));
+                chunk = std::min<int64_t>(std::max<int64_t>(chunk, 128), kMfmaChunkCapTokens);
+            }
+            return (unit_tokens(g) + chunk - 1) / chunk;
+        };
         // MFMA chunking and placement for a target task cost `target`
         struct MfmaPlan {
             std::vector<Piece> pieces;
@@ -510,14 +522,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             for (int gi : mg) {
                 const Group& g = groups[size_t(gi)];
                 const int64_t tokens = unit_tokens(g);
-                int64_t chunk;
-                if (o.split_tokens > 0) {
-                    chunk = std::min<int64_t>(ceil16(o.split_tokens), kMfmaChunkCapTokens);
-                } else {
-                    chunk = ceil16(int64_t(std::ceil((target - kMfmaTaskCost) / g.w)));
-                    chunk = std::min<int64_t>(std::max<int64_t>(chunk, 128), kMfmaChunkCapTokens);
-                }
-                const int64_t nch = (tokens + chunk - 1) / chunk;
+                const int64_t nch = mfma_chunks(g, target);
                 const int64_t len = ceil16((tokens + nch - 1) / nch);
                 mp.extra += double(nch - 1) * g.rows * Hkv * pu_mfma;
                 for (int64_t c = 0; c < nch; ++c) {
@@ -536,26 +541,25 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
                 }
             }
             std::stable_sort(tasks.begin(), tasks.end(), [](const T& a, const T& b) { return a.cost > b.cost; });
+            // one min-heap of (load, list) per XCD; the least-loaded list overall is
+            // the least of the XCD minima
             using LE = std::pair<double, int>;
             using Heap = std::priority_queue<LE, std::vector<LE>, std::greater<LE>>;
-            Heap heap_all;
             std::vector<Heap> heap_x(kXcds);
-            for (int w = 0; w < n_lists; ++w) {
-                heap_all.push({0.0, w});
-                heap_x[size_t(w % kXcds)].push({0.0, w});
-            }
-            auto top_of = [&](Heap& h) {
-                while (!h.empty() && h.top().first != mp.load[size_t(h.top().second)]) h.pop();
-                return h.empty() ? -1 : h.top().second;
-            };
+            for (int w = 0; w < n_lists; ++w) heap_x[size_t(w % kXcds)].push({0.0, w});
             for (const T& t : tasks) {
-                int w = top_of(heap_all);
-                const int wx = top_of(heap_x[size_t(t.head % kXcds)]);
-                if (wx >= 0 && mp.load[size_t(wx)] <= mp.load[size_t(w)] + 0.25 * t.cost) w = wx;
+                int xb = -1;
+                for (int x = 0; x < kXcds; ++x)
+                    if (!heap_x[size_t(x)].empty() && (xb < 0 || heap_x[size_t(x)].top() < heap_x[size_t(xb)].top())) xb = x;
+                const int xp = t.head % kXcds;
+                int x = xb;
+                if (!heap_x[size_t(xp)].empty() && heap_x[size_t(xp)].top().first <= heap_x[size_t(xb)].top().first + 0.25 * t.cost)
+                    x = xp;
+                const int w = heap_x[size_t(x)].top().second;
+                heap_x[size_t(x)].pop();
                 mp.pieces[size_t(t.piece)].head_list[size_t(t.head)] = w;
                 mp.load[size_t(w)] += t.cost;
-                heap_all.push({mp.load[size_t(w)], w});
-                heap_x[size_t(w % kXcds)].push({mp.load[size_t(w)], w});
+                heap_x[size_t(x)].push({mp.load[size_t(w)], w});
             }
             return mp;
         };
@@ -591,7 +595,17 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             for (int k = 1; k <= 8; ++k)
                 targets.push_back((w_mfma + double(k) * n_lists * kMfmaTaskCost) / (double(k) * n_lists));
         }
+        std::set<std::vector<int64_t>> tried;   // chunk counts per group already placed
         for (double target : targets) {
+            std::vector<int64_t> key;
+            int64_t n_tasks = 0;
+            for (int gi : mg) {
+                key.push_back(mfma_chunks(groups[size_t(gi)], target));
+                n_tasks += key.back() * Hkv;
+            }
+            // more than 16 MFMA tasks per list never pays for its partials
+            if (have && n_tasks > 16 * int64_t(n_lists)) continue;
+            if (!tried.insert(key).second) continue;
             MfmaPlan mp = place_mfma(target);
             const std::vector<double> base = stripe_base(mp.load);
             double makespan = *std::max_element(mp.load.begin(), mp.load.end());
