@@ -221,6 +221,10 @@ constexpr double kValuTaskCost = 8.0;
 // MFMA task writes its partials as one burst of up to 128 rows, which costs
 // far less per byte.
 constexpr double kPartialWriteCostMfma = 2.0;
+// Measured on MI355X (per-task traces): workgroups on odd XCDs stream ~10 %
+// slower than on even ones, whatever the KV heads they read; VALU stripes on
+// odd XCDs are filled to 0.9 of the common level.
+constexpr double kOddXcdRate = 0.9;
 
 // Append the descriptor of task t (see kDesc*) to P.desc; returns its words.
 int32_t put_desc(kvattn_plan_s& P, const Task& t) {
@@ -469,6 +473,13 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     const int n_lists = num_cus * 2;
     const int quads = (Hkv + kWaves - 1) / kWaves;
     const int n_stripes = std::max(1, n_lists / quads);
+    // A stripe's lists sit on one XCD (list w runs on XCD w mod 8): members
+    // w, w + 8, ... when the lists split evenly, so they stream at one rate.
+    const bool xcd_stripes = n_lists % (kXcds * quads) == 0;
+    auto stripe_list = [&](int s, int q) {
+        return xcd_stripes ? (s / kXcds) * kXcds * quads + s % kXcds + kXcds * q : s * quads + q;
+    };
+    auto stripe_rate = [&](int s) { return (stripe_list(s, 0) % kXcds) % 2 ? kOddXcdRate : 1.0; };
     const double pu_mfma = (kPartialWriteCostMfma + 1.0) * double(partial_row_bytes) / double(2 * D * 2);
     auto mfma_cost = [&](const Group& g, int64_t tok) { return double(tok) * g.w + kMfmaTaskCost; };
     auto unit_tokens = [&](const Group& g) { return units[g.unit].tokens; };
@@ -567,17 +578,19 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         auto stripe_base = [&](const std::vector<double>& load) {
             std::vector<double> base(size_t(n_stripes), 0.0);
             for (int s = 0; s < n_stripes; ++s)
-                for (int q = 0; q < quads; ++q) base[size_t(s)] = std::max(base[size_t(s)], load[size_t(s * quads + q)]);
+                for (int q = 0; q < quads; ++q) base[size_t(s)] = std::max(base[size_t(s)], load[size_t(stripe_list(s, q))]);
             return base;
         };
         // the level at which the stripes, each filled from its base, hold `work`
         auto fill_level = [&](const std::vector<double>& base, double work) {
             double lo = *std::min_element(base.begin(), base.end());
-            double hi = *std::max_element(base.begin(), base.end()) + work / n_stripes + 1.0;
+            double hi = 0.0;
+            for (int s = 0; s < n_stripes; ++s) hi = std::max(hi, base[size_t(s)] / stripe_rate(s));
+            hi += work / (n_stripes * kOddXcdRate) + 1.0;
             for (int it = 0; it < 60; ++it) {
                 const double mid = 0.5 * (lo + hi);
                 double cap = 0.0;
-                for (int s = 0; s < n_stripes; ++s) cap += std::max(0.0, mid - base[size_t(s)]);
+                for (int s = 0; s < n_stripes; ++s) cap += std::max(0.0, mid * stripe_rate(s) - base[size_t(s)]);
                 (cap >= work ? hi : lo) = mid;
             }
             return hi;
@@ -647,7 +660,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             // blocks.  Returns the work left over for the last stripe past level.
             auto fill = [&](double level, std::vector<Piece>* out) {
                 int s = 0;
-                double room = level - base[0];
+                double room = level * stripe_rate(0) - base[0];
                 double over = 0.0;
                 for (int gi : vg) {
                     const int64_t tokens = unit_tokens(groups[size_t(gi)]);
@@ -656,7 +669,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
                         // move on when the stripe cannot take one more block
                         while (s < n_stripes - 1 && room < kValuTaskCost + kBlock) {
                             ++s;
-                            room = level - base[size_t(s)];
+                            room = level * stripe_rate(s) - base[size_t(s)];
                         }
                         int64_t take = tokens - t0;
                         if (s < n_stripes - 1) {
@@ -805,7 +818,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             } else {
                 const int32_t words = desc_words(it.n_q, (it.n_tokens + kBlock - 1) / kBlock);
                 for (int q = 0; q < quads; ++q) {
-                    int w = pc.stripe * quads + q;
+                    int w = stripe_list(pc.stripe, q);
                     if (vwords[size_t(w)] + words > window) {
                         // the stripe's window is full: the least-filled list with room takes it
                         int best_w = -1;
