@@ -35,7 +35,7 @@ constexpr int kMfmaMaxItemBlocks = 1408;  // KV blocks per MFMA item (22528 toke
 constexpr int kMaxGroup = 64;           // q heads per KV head supported
 constexpr int kXcds = 8;                // XCDs of an MI355X (L2 domains)
 constexpr uint32_t kBlobMagic = 0x4B564154u;  // "KVAT"
-constexpr uint32_t kBlobVersion = 7;
+constexpr uint32_t kBlobVersion = 8;
 
 // Device view of one item; identical layout to kvattn_item_info.
 struct Item {
@@ -98,7 +98,7 @@ struct BlobHeader {
     int32_t n_tasks, n_launches, n_lists, pad0;
     uint64_t off_desc;        // int32 [n_desc_words]: task descriptors
     uint64_t off_list_ptr;    // int32 [n_launches][n_lists][3]: word offsets (MFMA begin, VALU begin, end) per list
-    uint64_t off_merge_query, off_merge_ptr, off_merge_dest;
+    uint64_t off_merge_rec;   // int32 [n_merge_q][4]: (query, first slot, partials, 0); partial k at first + k Hq
     uint64_t off_claim;       // int32: list claim counter, zero between launches
     uint64_t blob_bytes;      // bytes copied by kvattn_plan_upload
     uint64_t off_part_ml;     // float2 [n_slots]: (m in log2 units, l)
@@ -119,14 +119,18 @@ struct Launch {
     int task_base;     // first task of the launch in the host schedule
 };
 
+// Merge record of one query whose rows have several partials: partial k of
+// q head h sits in slot first + k * Hq + h.
+struct alignas(16) MergeRec {
+    int32_t query, first, count, pad;
+};
+
 // Pointers the kernels take, resolved from the bound workspace.
 struct DevPlan {
     const int32_t* desc;
     const int32_t* list_ptr;    // this launch's n_lists x 3 word offsets into desc
     int32_t n_lists;
-    const int32_t* merge_query;
-    const int32_t* merge_ptr;
-    const int32_t* merge_dest;
+    const MergeRec* merge_rec;  // per merged query
     int32_t* claim;             // list claim counter (zero between launches)
     float* part_ml;
     float* part_acc;

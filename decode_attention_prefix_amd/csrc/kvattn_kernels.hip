@@ -957,9 +957,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 // output floats [256 y, 256 y + 256) of the query's [Hq][D] block, all partial
 // triples of the query in one pass with the online-softmax rule:
 //   M' = max(M, m_i);  A = A 2^(M - M') + 2^(m_i - M') acc_i;  L likewise with l_i
-// and writes A / L.  The slots of one item entry are consecutive (slot = dest +
-// h), so a partial's accumulators for every head form one contiguous [Hq][D]
-// block.  Partials are read in batches of eight with every load in flight.
+// and writes A / L.  A query's partials are consecutive [Hq][D] blocks of
+// slots (partial k of q head h in slot first + k Hq + h), located from one
+// record.  Partials are read in batches of eight with every load in flight.
 // ============================================================================
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(DevPlan p, Dims dm, float* __restrict__ out) {
@@ -969,26 +969,25 @@ __global__ __launch_bounds__(64) void merge_kernel(DevPlan p, Dims dm, float* __
     const int col = int(blockIdx.y) * 256 + 4 * int(threadIdx.x);   // float index in [Hq][D]
     if (col >= Hq * D) return;
     const int h = col / D;
-    const KV_CONST int32_t* mptr = cptr(p.merge_ptr);
-    const KV_CONST int32_t* mdst = cptr(p.merge_dest);
-    const int b = cptr(p.merge_query)[mq];
-    const int i0 = mptr[mq], i1 = mptr[mq + 1];
+    // the query, its first partial slot and its partial count (one scalar load)
+    const KV_CONST MergeRec* rec = cptr(p.merge_rec) + mq;
+    const int b = rec->query, n = rec->count;
+    const size_t slot0 = size_t(rec->first) + h;
     float M = -INFINITY, L = 0.f;
     float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int ib = i0; ib < i1; ib += BATCH) {
+    for (int ib = 0; ib < n; ib += BATCH) {
         float2 ml[BATCH];
         float4 ac[BATCH];
 #pragma unroll
         for (int j = 0; j < BATCH; ++j) {
-            const int i = min(ib + j, i1 - 1);
-            const size_t slot = size_t(mdst[i]) + h;
+            const size_t slot = slot0 + size_t(min(ib + j, n - 1)) * Hq;
             ml[j] = *reinterpret_cast<const float2*>(p.part_ml + slot * 2);
             ac[j] = *reinterpret_cast<const float4*>(p.part_acc + slot * D + (col - h * D));
         }
 #pragma unroll
         for (int j = 0; j < BATCH; ++j) {
             // past the query's last partial: no change (weight 0, same max)
-            const float mj = ib + j < i1 ? ml[j].x : -INFINITY;
+            const float mj = ib + j < n ? ml[j].x : -INFINITY;
             const float Mn = fmaxf(M, mj);
             const float so = fast_exp2(M - Mn);     // 0 while M is -inf
             const float sn = fast_exp2(mj - Mn);    // 0 past the last partial

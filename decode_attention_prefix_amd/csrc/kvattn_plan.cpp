@@ -759,17 +759,24 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     P.items.clear();
     P.entries.clear();
     P.block_ids.clear();
+    // A query's partials take consecutive slot blocks (partial k of query b at
+    // base_b + k Hq), so the merge finds them from (base, count) alone.
     std::vector<std::vector<int32_t>> dests(B);
+    std::vector<int32_t> slot_base(B, -1);
     std::vector<int> item_proto;
     int32_t slots_used = 0;
+    for (int b = 0; b < B; ++b)
+        if (count[b] > 1) {
+            slot_base[b] = slots_used;
+            slots_used += count[b] * Hq;
+        }
     for (int idx : order) {
         Proto& p = protos[size_t(idx)];
         p.it.q_begin = int32_t(P.entries.size());
         p.it.blk_begin = int32_t(P.block_ids.size());
         for (Entry e : p.entries) {
             if (count[e.query] > 1) {
-                e.dest = slots_used;
-                slots_used += Hq;
+                e.dest = slot_base[e.query] + int32_t(dests[e.query].size()) * Hq;
                 dests[e.query].push_back(e.dest);
             }
             P.entries.push_back(e);
@@ -782,12 +789,14 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     P.merge_query.clear();
     P.merge_dest.clear();
     P.merge_ptr.assign(1, 0);
+    P.merge_rec.clear();
     int direct_rows = 0;
     for (int b = 0; b < B; ++b) {
         if (count[b] == 1) {
             direct_rows += Hq;
             continue;
         }
+        P.merge_rec.insert(P.merge_rec.end(), {b, slot_base[b], count[b], 0});
         P.merge_query.push_back(b);
         P.merge_dest.insert(P.merge_dest.end(), dests[b].begin(), dests[b].end());
         P.merge_ptr.push_back(int32_t(P.merge_dest.size()));
@@ -886,9 +895,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     uint64_t off = align256(sizeof(BlobHeader));
     h.off_desc = off;         off = align256(off + P.desc.size() * 4);
     h.off_list_ptr = off;     off = align256(off + P.desc_list_ptr.size() * 4);
-    h.off_merge_query = off;  off = align256(off + P.merge_query.size() * 4);
-    h.off_merge_ptr = off;    off = align256(off + P.merge_ptr.size() * 4);
-    h.off_merge_dest = off;   off = align256(off + P.merge_dest.size() * 4);
+    h.off_merge_rec = off;    off = align256(off + P.merge_rec.size() * 4);
     h.off_claim = off;        off = align256(off + 4);
     h.blob_bytes = off;
     h.off_part_ml = off;      off = align256(off + uint64_t(slots_used) * 8);
@@ -901,9 +908,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     };
     put(h.off_desc, P.desc.data(), P.desc.size() * 4);
     put(h.off_list_ptr, P.desc_list_ptr.data(), P.desc_list_ptr.size() * 4);
-    put(h.off_merge_query, P.merge_query.data(), P.merge_query.size() * 4);
-    put(h.off_merge_ptr, P.merge_ptr.data(), P.merge_ptr.size() * 4);
-    put(h.off_merge_dest, P.merge_dest.data(), P.merge_dest.size() * 4);
+    put(h.off_merge_rec, P.merge_rec.data(), P.merge_rec.size() * 4);
 
     // ---- statistics ------------------------------------------------------------------------------
     kvattn_stats& st = P.stats;

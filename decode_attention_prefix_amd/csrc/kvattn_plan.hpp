@@ -13,7 +13,8 @@ struct kvattn_plan_s {
     std::vector<kvattn::Item> items;
     std::vector<kvattn::Entry> entries;
     std::vector<int32_t> block_ids;
-    std::vector<int32_t> merge_query, merge_ptr, merge_dest;
+    std::vector<int32_t> merge_query, merge_ptr, merge_dest;   // host copy (export)
+    std::vector<int32_t> merge_rec;                            // device: (b, slot base, partials, 0) per merged query
     int32_t n_slots = 0;
     std::vector<kvattn::Task> tasks;
     std::vector<int32_t> list_ptr;          // [launch][n_lists + 1] task ranges of the static lists

@@ -19,9 +19,7 @@ DevPlan resolve(const kvattn_plan_s& P, int launch) {
     d.list_ptr = reinterpret_cast<const int32_t*>(base + h.off_list_ptr);
     d.n_lists = P.n_lists;
     if (launch >= 0) d.list_ptr += size_t(launch) * size_t(P.n_lists) * 3;
-    d.merge_query = reinterpret_cast<const int32_t*>(base + h.off_merge_query);
-    d.merge_ptr = reinterpret_cast<const int32_t*>(base + h.off_merge_ptr);
-    d.merge_dest = reinterpret_cast<const int32_t*>(base + h.off_merge_dest);
+    d.merge_rec = reinterpret_cast<const MergeRec*>(base + h.off_merge_rec);
     d.claim = reinterpret_cast<int32_t*>(base + h.off_claim);
     d.part_ml = reinterpret_cast<float*>(base + h.off_part_ml);
     d.part_acc = reinterpret_cast<float*>(base + h.off_part_acc);
