@@ -445,6 +445,14 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     }
     std::sort(vt.begin(), vt.end(), std::greater<int>());
     std::sort(mt.begin(), mt.end(), std::greater<int>());
+    // VALU groups share the largest row template: a second launch (its gap,
+    // ramp and tail, ~5 us) costs more than the idle rows of the smaller groups,
+    // whose streams are bandwidth-bound anyway
+    if (vt.size() > 1 && vt.size() > mt.size()) {
+        for (Group& g : groups)
+            if (g.kind == KVATTN_VARIANT_VALU) g.tile = vt[0];
+        vt.resize(1);
+    }
     const int n_launch = int(std::max(vt.size(), mt.size()));
     auto launch_of = [&](const Group& g) {
         const std::vector<int>& v = g.kind == KVATTN_VARIANT_MFMA ? mt : vt;
@@ -462,7 +470,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     //    range meet in one L2).
     //  * VALU items run one task per four KV heads, one wave per head, as part
     //    of continuous per-wave streams.  The lists are taken in groups of
-    //    ceil(Hkv / 4) consecutive lists ("stripes", all KV heads of an item);
+    //    ceil(Hkv / 4) lists on one XCD ("stripes", all KV heads of an item);
     //    the VALU token stream of the launch (every VALU range in order) is cut
     //    into pieces that fill every stripe up to one common level above its
     //    MFMA load.  The stripes then end together, and at most one cut per
