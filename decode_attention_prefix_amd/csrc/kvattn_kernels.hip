@@ -2,13 +2,15 @@
 //
 // Forward (PAT review, forward stage: multi-tile kernels picked per work item,
 // long KV split into chunks, no execution bubbles): one persistent launch;
-// workgroup w runs the static task list the planner built for it.  A task is
+// workgroup w runs task list w the planner built for it (and claims lists
+// past the grid at run time).  A task is
 // one item (a run of paged KV blocks and the query rows attending to it) on
 // one KV head (MFMA path) or four KV heads (VALU path); it yields either final
 // output rows or partial triples (m, l, acc), m in log2 units.
 //   * MFMA path -- packed groups (up to 128 rows per KV head): S^T = K Q^T and
 //                  O^T = V^T P^T on v_mfma_f32_16x16x32_bf16, K/V tiles staged
-//                  in LDS by direct global->LDS DMA, three stages deep.
+//                  in LDS by buffer->LDS DMA, three tiles in flight, V^T read
+//                  by transposing LDS reads.
 //   * VALU path -- at most 4 (D = 128) or 8 (D = 64) rows per KV head: a
 //                  query's GQA group or a few queries of a small pack.
 //                  Bandwidth bound: q K^T with v_dot2_f32_bf16, p V with fp32
@@ -16,7 +18,7 @@
 //                  runs across the list's tasks, 8-lane DPP reductions.
 // Merge (PAT review, merge stage: online-softmax combination of the per-
 // workgroup partial results of a query): one wave per 256 output floats of a
-// query, single pass over its partials.
+// query, single pass over its partials (consecutive slot blocks).
 //
 // Scores are kept in log2 units (q.k * scale * log2 e) so every exponential is
 // a single v_exp_f32.  The running max is refreshed lazily: a row is rescaled
@@ -217,7 +219,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // ============================================================================
 // VALU stream: a wave runs the VALU tasks of its workgroup's list for KV head
 // (task head + wave) as one continuous stream of 16-token blocks.  Its
-// four-deep register ring crosses task boundaries, so blocks of the next
+// kValuRing-deep register ring crosses task boundaries, so blocks of the next
 // task are in flight while the current one finishes and nothing drains
 // between tasks.  The list's descriptors sit in an LDS window; the q rows of a
 // task are copied into one of four per-wave LDS slots by DMA right before the
