@@ -61,6 +61,10 @@ def check_coverage(wl_bt, seq_lens, Hq, Hkv, ex):
             i = mq[b]
             listed = ex["merge_dest"][ex["merge_ptr"][i]:ex["merge_ptr"][i + 1]]
             assert sorted(listed.tolist()) == sorted(d)
+            # the merge locates a query's partials from its first slot and count:
+            # consecutive [Hq]-slot blocks
+            first = int(listed.min())
+            assert sorted(listed.tolist()) == [first + k * Hq for k in range(len(d))]
             for x in d:
                 for h in range(Hq):
                     assert (x + h) not in slots_used
