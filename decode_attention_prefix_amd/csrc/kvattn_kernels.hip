@@ -629,7 +629,7 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
     // vector-memory operation, or waits on it would also drain the tile DMA.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
 
-    // ---- loop-invariant DMA geometry: chunk u of this thread is token tok_u, row offset off_u
+    // ---- loop-invariant DMA geometry
     const size_t head_elems = size_t(16) * D;
     const size_t blk_elems = size_t(Hkv) * head_elems;
     const uint16_t* kh = kc + size_t(g) * head_elems;
@@ -689,11 +689,10 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
     {
         const int t = 4 * lg + (lr >> 2);
         const int sw = vswz<D>(t);
+        // vtr[j]: head dims 16j + 4 (lr mod 4) .. + 3 of token t, in V chunk 2j + (lr mod 4) / 2
 #pragma unroll
         for (int j = 0; j < NDT; ++j)
             vtr[j] = uint32_t(2 * (TT * D + t * D) + ((2 * j + ((lr & 3) >> 1)) ^ sw) * 16 + (lr & 1) * 8);
-        // vtr[j] reads head dims 16j + 4(lr mod 4) .. + 3 of token t
-
     }
 
     auto compute = [&](int i, const uint16_t* sb) {
