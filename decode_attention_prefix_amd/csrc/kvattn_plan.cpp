@@ -256,6 +256,80 @@ int32_t put_desc(kvattn_plan_s& P, const Task& t) {
     return words;
 }
 
+// Task descriptors of every launch, from the lists in P.tasks / P.list_ptr.
+// Everything a task reads before its KV stream sits in one contiguous record:
+// a 16-word header, the entries, the block ids.  A list's MFMA records lie back
+// to back (each header gives the next one's size), so a workgroup finds the next
+// record right after the current one and copies it into LDS while the current
+// task streams; its VALU records follow and are copied into LDS in one piece.
+// Returns false if a list's VALU records overflow the launch's LDS window.
+bool serialize_lists(kvattn_plan_s& P) {
+    const int n_lists = P.n_lists;
+    const int D = P.shape.head_dim;
+    P.desc.clear();
+    P.desc_list_ptr.assign(P.forward_launches.size() * size_t(n_lists) * 3, 0);
+    P.task_desc.assign(P.tasks.size(), 0);
+    for (const Launch& Lr : P.forward_launches) {
+        const int32_t window = valu_window_words(D, Lr.valu_rows);
+        for (int w = 0; w < n_lists; ++w) {
+            const int t0 = Lr.task_base + P.list_ptr[size_t(Lr.index) * (n_lists + 1) + w];
+            const int t1 = Lr.task_base + P.list_ptr[size_t(Lr.index) * (n_lists + 1) + w + 1];
+            int32_t* lp = P.desc_list_ptr.data() + (size_t(Lr.index) * n_lists + w) * 3;
+            lp[0] = int32_t(P.desc.size());
+            size_t prev = SIZE_MAX;
+            int t = t0;
+            for (; t < t1 && P.items[size_t(P.tasks[size_t(t)].item)].kind == KVATTN_VARIANT_MFMA; ++t) {
+                const size_t at = P.desc.size();
+                P.task_desc[size_t(t)] = int32_t(at);
+                const int32_t words = put_desc(P, P.tasks[size_t(t)]);
+                if (prev != SIZE_MAX) P.desc[prev + kDescNextWords] = words;
+                prev = at;
+            }
+            lp[1] = int32_t(P.desc.size());
+            for (; t < t1; ++t) {
+                P.task_desc[size_t(t)] = int32_t(P.desc.size());
+                put_desc(P, P.tasks[size_t(t)]);
+            }
+            lp[2] = int32_t(P.desc.size());
+            if (lp[2] - lp[1] > window) return false;
+        }
+    }
+    return true;
+}
+
+// Header and arrays of the device blob (the part kvattn_plan_upload copies);
+// the partial triples follow it in the workspace.
+void serialize_blob(kvattn_plan_s& P) {
+    BlobHeader& h = P.header;
+    std::memset(&h, 0, sizeof(h));
+    h.magic = kBlobMagic;
+    h.version = kBlobVersion;
+    h.n_desc_words = int32_t(P.desc.size());
+    h.n_merge_q = int32_t(P.merge_query.size());
+    h.n_slots = P.n_slots;
+    h.head_dim = P.shape.head_dim;
+    h.n_tasks = int32_t(P.tasks.size());
+    h.n_launches = int32_t(P.forward_launches.size());
+    h.n_lists = P.n_lists;
+    uint64_t off = align256(sizeof(BlobHeader));
+    h.off_desc = off;         off = align256(off + P.desc.size() * 4);
+    h.off_list_ptr = off;     off = align256(off + P.desc_list_ptr.size() * 4);
+    h.off_merge_rec = off;    off = align256(off + P.merge_rec.size() * 4);
+    h.off_claim = off;        off = align256(off + 4);
+    h.blob_bytes = off;
+    h.off_part_ml = off;      off = align256(off + uint64_t(P.n_slots) * 8);
+    h.off_part_acc = off;     off = align256(off + uint64_t(P.n_slots) * uint64_t(P.shape.head_dim) * 4);
+    h.total_bytes = off;
+    P.blob.assign(h.blob_bytes, 0);
+    std::memcpy(P.blob.data(), &h, sizeof(h));
+    auto put = [&](uint64_t at, const void* src, size_t n) {
+        if (n) std::memcpy(P.blob.data() + at, src, n);
+    };
+    put(h.off_desc, P.desc.data(), P.desc.size() * 4);
+    put(h.off_list_ptr, P.desc_list_ptr.data(), P.desc_list_ptr.size() * 4);
+    put(h.off_merge_rec, P.merge_rec.data(), P.merge_rec.size() * 4);
+}
+
 }  // namespace
 
 kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, const int32_t* seq_lens,
@@ -818,8 +892,6 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     P.list_ptr.assign(size_t(n_launch) * (n_lists + 1), 0);
     P.forward_launches.clear();
     P.n_lists = n_lists;
-    P.desc.clear();
-    P.desc_list_ptr.assign(size_t(n_launch) * n_lists * 3, 0);
     for (int L = 0; L < n_launch; ++L) {
         const int launch_valu_rows = L < int(vt.size()) ? vt[size_t(L)] : 1;
         const int32_t window = valu_window_words(D, launch_valu_rows);
@@ -865,58 +937,13 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         Lr.n_tasks = int(P.tasks.size()) - base;
         Lr.task_base = base;
         P.forward_launches.push_back(Lr);
-
-        // ---- task descriptors of this launch
-        // Everything a task reads before its KV stream, in one contiguous record:
-        // a 16-word header, the entries, the block ids.  A list's MFMA records
-        // lie back to back, so a workgroup finds the next record right after the
-        // current one and copies it into LDS while the current task streams; its
-        // VALU records follow and are copied into LDS in one piece.
-        for (int w = 0; w < n_lists; ++w) {
-            int32_t* lp = P.desc_list_ptr.data() + (size_t(L) * n_lists + w) * 3;
-            lp[0] = int32_t(P.desc.size());
-            size_t prev = SIZE_MAX;
-            for (const Task& t : mlist[size_t(w)]) {
-                const size_t at = P.desc.size();
-                const int32_t words = put_desc(P, t);
-                if (prev != SIZE_MAX) P.desc[prev + kDescNextWords] = words;
-                prev = at;
-            }
-            lp[1] = int32_t(P.desc.size());
-            for (const Task& t : vlist[size_t(w)]) put_desc(P, t);
-            lp[2] = int32_t(P.desc.size());
-        }
     }
+    if (!serialize_lists(P)) return set_error(KVATTN_EINVAL, "internal: VALU task descriptors exceed the LDS window");
 
     // ---- blob ------------------------------------------------------------------------------------
-    BlobHeader& h = P.header;
-    std::memset(&h, 0, sizeof(h));
-    h.magic = kBlobMagic;
-    h.version = kBlobVersion;
-    h.n_desc_words = int32_t(P.desc.size());
-    h.n_merge_q = int32_t(P.merge_query.size());
-    h.n_slots = slots_used;
-    h.head_dim = D;
-    h.n_tasks = int32_t(P.tasks.size());
-    h.n_launches = n_launch;
-    h.n_lists = n_lists;
-    uint64_t off = align256(sizeof(BlobHeader));
-    h.off_desc = off;         off = align256(off + P.desc.size() * 4);
-    h.off_list_ptr = off;     off = align256(off + P.desc_list_ptr.size() * 4);
-    h.off_merge_rec = off;    off = align256(off + P.merge_rec.size() * 4);
-    h.off_claim = off;        off = align256(off + 4);
-    h.blob_bytes = off;
-    h.off_part_ml = off;      off = align256(off + uint64_t(slots_used) * 8);
-    h.off_part_acc = off;     off = align256(off + uint64_t(slots_used) * D * 4);
-    h.total_bytes = off;
-    P.blob.assign(h.blob_bytes, 0);
-    std::memcpy(P.blob.data(), &h, sizeof(h));
-    auto put = [&](uint64_t at, const void* src, size_t n) {
-        if (n) std::memcpy(P.blob.data() + at, src, n);
-    };
-    put(h.off_desc, P.desc.data(), P.desc.size() * 4);
-    put(h.off_list_ptr, P.desc_list_ptr.data(), P.desc_list_ptr.size() * 4);
-    put(h.off_merge_rec, P.merge_rec.data(), P.merge_rec.size() * 4);
+    P.n_slots = slots_used;
+    serialize_blob(P);
+    const BlobHeader& h = P.header;
 
     // ---- statistics ------------------------------------------------------------------------------
     kvattn_stats& st = P.stats;

@@ -19,6 +19,7 @@ struct kvattn_plan_s {
     std::vector<kvattn::Task> tasks;
     std::vector<int32_t> list_ptr;          // [launch][n_lists + 1] task ranges of the static lists
     std::vector<int32_t> desc;              // device task descriptors
+    std::vector<int32_t> task_desc;         // [tasks] word offset of each task's descriptor in desc
     std::vector<int32_t> desc_list_ptr;     // [launch][n_lists][3] (MFMA begin, VALU begin, end) in words
     int32_t n_lists = 0;                    // static task lists per launch (one per persistent workgroup)
     std::vector<kvattn::Launch> forward_launches;
