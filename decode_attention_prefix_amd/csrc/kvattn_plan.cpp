@@ -64,6 +64,25 @@ struct Batch {
     int32_t id(int b, int j) const { return bt[size_t(b) * mb + j]; }
 };
 
+// Lengths within [1, max_blocks * 16] and block ids of every used block within
+// [0, num_physical_blocks).
+kvattn_status check_tables(const kvattn_shape& s, const int32_t* block_tables, const int32_t* seq_lens) {
+    for (int b = 0; b < s.num_queries; ++b) {
+        const int T = seq_lens[b];
+        if (T < 1 || int64_t(T) > int64_t(s.max_blocks_per_seq) * kBlock)
+            return set_error(KVATTN_EINVAL, "seq_lens[" + std::to_string(b) + "] = " + std::to_string(T) +
+                                                " outside [1, max_blocks_per_seq * 16]");
+        const int nb = (T + kBlock - 1) / kBlock;
+        for (int j = 0; j < nb; ++j) {
+            const int32_t id = block_tables[size_t(b) * s.max_blocks_per_seq + j];
+            if (id < 0 || id >= s.num_physical_blocks)
+                return set_error(KVATTN_EINVAL, "block_tables[" + std::to_string(b) + "][" + std::to_string(j) +
+                                                    "] = " + std::to_string(id) + " outside [0, num_physical_blocks)");
+        }
+    }
+    return KVATTN_OK;
+}
+
 // Maximal tree: a node is a maximal run of positions over which one fixed set
 // of queries holds the same (physical block, token count) keys.
 void derive_tree(const Batch& bt, std::vector<Node>& nodes, std::vector<int>& leaf) {
@@ -338,19 +357,8 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     const int B = s.num_queries, Hq = s.num_q_heads, Hkv = s.num_kv_heads, D = s.head_dim;
     const int G = Hq / Hkv;
     Batch bt{B, s.max_blocks_per_seq, block_tables, seq_lens, std::vector<int>(B)};
-    for (int b = 0; b < B; ++b) {
-        int T = seq_lens[b];
-        if (T < 1 || int64_t(T) > int64_t(s.max_blocks_per_seq) * kBlock)
-            return set_error(KVATTN_EINVAL, "seq_lens[" + std::to_string(b) + "] = " + std::to_string(T) +
-                                                " outside [1, max_blocks_per_seq * 16]");
-        bt.nb[b] = (T + kBlock - 1) / kBlock;
-        for (int j = 0; j < bt.nb[b]; ++j) {
-            int32_t id = bt.id(b, j);
-            if (id < 0 || id >= s.num_physical_blocks)
-                return set_error(KVATTN_EINVAL, "block_tables[" + std::to_string(b) + "][" + std::to_string(j) +
-                                                    "] = " + std::to_string(id) + " outside [0, num_physical_blocks)");
-        }
-    }
+    if (kvattn_status vs = check_tables(s, block_tables, seq_lens); vs != KVATTN_OK) return vs;
+    for (int b = 0; b < B; ++b) bt.nb[b] = (seq_lens[b] + kBlock - 1) / kBlock;
 
     // ---- prefix tree ---------------------------------------------------------
     std::vector<Node> nodes;
@@ -985,7 +993,194 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     st.blob_bytes = h.blob_bytes;
     st.workspace_bytes = h.total_bytes;
     st.plan_seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+
+    // ---- state for incremental updates --------------------------------------------------------
+    P.tables.assign(block_tables, block_tables + size_t(B) * s.max_blocks_per_seq);
+    P.lens.assign(seq_lens, seq_lens + B);
+    P.entry_item.assign(P.entries.size(), 0);
+    P.tail_entry.assign(size_t(B), -1);
+    for (size_t i = 0; i < P.items.size(); ++i) {
+        const Item& it = P.items[i];
+        for (int e = it.q_begin; e < it.q_begin + it.n_q; ++e) {
+            P.entry_item[size_t(e)] = int32_t(i);
+            const Entry& en = P.entries[size_t(e)];
+            if (int64_t(it.pos_begin) * kBlock + en.limit == seq_lens[en.query]) P.tail_entry[size_t(en.query)] = e;
+        }
+    }
     return KVATTN_OK;
+}
+
+// Extend the plan in place to longer sequences (PAT review, overhead analysis,
+// Fig 16: the pack scheduler's cost must stay negligible next to decoding).
+// A decode step appends tokens to each query; when every query's old blocks are
+// unchanged and its new tokens extend the item that holds its last token --
+// its own private item, or a shared item all of whose end queries grow alike
+// into the same new blocks -- only those items, their entries' limits and
+// their descriptors change: no tree, pack, split or list work.  Returns 1 when
+// the descriptors were patched in place, 2 when their sizes changed and the
+// lists were re-serialized, 0 (plan unchanged) when the step does not fit.
+int extend_plan(kvattn_plan_s& P, const int32_t* block_tables, const int32_t* seq_lens) {
+    const kvattn_shape& s = P.shape;
+    const int B = s.num_queries, MB = s.max_blocks_per_seq;
+    if (P.lens.size() != size_t(B) || P.tail_entry.size() != size_t(B)) return 0;
+    // the blocks the old lengths cover are unchanged
+    for (int b = 0; b < B; ++b) {
+        if (seq_lens[b] < P.lens[size_t(b)]) return 0;
+        const int nb = (P.lens[size_t(b)] + kBlock - 1) / kBlock;
+        const int32_t* a = block_tables + size_t(b) * MB;
+        const int32_t* o = P.tables.data() + size_t(b) * MB;
+        if (!std::equal(a, a + nb, o)) return 0;
+    }
+    // growth per item: the entries that grow are exactly those ending with the item
+    struct Grow {
+        int item, delta, growing, query;
+    };
+    std::vector<Grow> grow;
+    std::vector<int> slot(P.items.size(), -1);
+    for (int b = 0; b < B; ++b) {
+        const int d = seq_lens[b] - P.lens[size_t(b)];
+        if (d == 0) continue;
+        const int e = P.tail_entry[size_t(b)];
+        if (e < 0) return 0;
+        const int i = P.entry_item[size_t(e)];
+        const Item& it = P.items[size_t(i)];
+        if (P.entries[size_t(e)].limit != it.n_tokens) return 0;
+        if (slot[size_t(i)] < 0) {
+            slot[size_t(i)] = int(grow.size());
+            grow.push_back({i, d, 0, b});
+        }
+        Grow& g = grow[size_t(slot[size_t(i)])];
+        if (g.delta != d) return 0;
+        g.growing++;
+    }
+    if (grow.empty()) return 1;
+    int64_t uniq_add = 0, qc_add = 0;
+    for (int b = 0; b < B; ++b) qc_add += seq_lens[b] - P.lens[size_t(b)];
+    bool resize = false;
+    std::vector<std::vector<int32_t>> new_ids(grow.size());
+    for (size_t k = 0; k < grow.size(); ++k) {
+        const Grow& g = grow[k];
+        const Item& it = P.items[size_t(g.item)];
+        int at_end = 0;
+        for (int e = it.q_begin; e < it.q_begin + it.n_q; ++e) at_end += P.entries[size_t(e)].limit == it.n_tokens;
+        if (at_end != g.growing) return 0;
+        const int nt = it.n_tokens + g.delta;
+        const int nb0 = (it.n_tokens + kBlock - 1) / kBlock, nb1 = (nt + kBlock - 1) / kBlock;
+        if (nb1 > (it.kind == KVATTN_VARIANT_MFMA ? kMfmaMaxItemBlocks : kMaxItemBlocks)) return 0;
+        if (it.pos_begin + nb1 > MB) return 0;
+        // the new blocks, alike for every growing query
+        for (int j = nb0; j < nb1; ++j) new_ids[k].push_back(block_tables[size_t(g.query) * MB + it.pos_begin + j]);
+        for (int e = it.q_begin; e < it.q_begin + it.n_q; ++e) {
+            const int q = P.entries[size_t(e)].query;
+            if (P.entries[size_t(e)].limit != it.n_tokens || q == g.query) continue;
+            for (int j = nb0; j < nb1; ++j)
+                if (block_tables[size_t(q) * MB + it.pos_begin + j] != new_ids[k][size_t(j - nb0)]) return 0;
+        }
+        resize |= desc_words(it.n_q, nb1) != desc_words(it.n_q, nb0);
+    }
+    // unique tokens: the valid-token count each touched physical block gains
+    {
+        std::vector<std::pair<int32_t, int>> touched;   // (block id, valid tokens after the step)
+        for (int b = 0; b < B; ++b) {
+            const int T0 = P.lens[size_t(b)], T1 = seq_lens[b];
+            if (T1 == T0) continue;
+            for (int j = (T0 - 1) / kBlock; j < (T1 + kBlock - 1) / kBlock; ++j)
+                touched.emplace_back(block_tables[size_t(b) * MB + j], std::min(kBlock, T1 - j * kBlock));
+        }
+        std::sort(touched.begin(), touched.end());
+        for (size_t x = 0; x < touched.size(); ++x) {
+            if (x + 1 < touched.size() && touched[x + 1].first == touched[x].first) continue;   // keep the largest
+            const int32_t id = touched[x].first;
+            // tokens the block held before: the largest old valid count among the queries that hold it
+            int before = 0;
+            for (int b = 0; b < B; ++b) {
+                const int T0 = P.lens[size_t(b)];
+                const int j = (T0 - 1) / kBlock;
+                if (P.tables[size_t(b) * MB + j] == id) before = std::max(before, T0 - j * kBlock);
+            }
+            uniq_add += touched[x].second - before;
+        }
+    }
+    // apply: items, entries, block ids
+    std::vector<int32_t> old_ids;
+    std::vector<Item> old_items;
+    std::vector<Entry> old_entries;
+    if (resize) {
+        old_ids = P.block_ids;
+        old_items = P.items;
+        old_entries = P.entries;
+    }
+    bool new_blocks = false;
+    for (size_t k = 0; k < grow.size(); ++k) {
+        Item& it = P.items[size_t(grow[k].item)];
+        for (int e = it.q_begin; e < it.q_begin + it.n_q; ++e)
+            if (P.entries[size_t(e)].limit == it.n_tokens) P.entries[size_t(e)].limit += grow[k].delta;
+        it.n_tokens += grow[k].delta;
+        new_blocks |= !new_ids[k].empty();
+    }
+    if (new_blocks) {
+        std::vector<int32_t> ids;
+        ids.reserve(P.block_ids.size() + 64);
+        for (size_t i = 0; i < P.items.size(); ++i) {
+            Item& it = P.items[i];
+            const int nb = (it.n_tokens + kBlock - 1) / kBlock;
+            const int32_t begin = int32_t(ids.size());
+            const int have = slot[i] >= 0 ? nb - int(new_ids[size_t(slot[i])].size()) : nb;
+            ids.insert(ids.end(), P.block_ids.begin() + it.blk_begin, P.block_ids.begin() + it.blk_begin + have);
+            if (slot[i] >= 0) ids.insert(ids.end(), new_ids[size_t(slot[i])].begin(), new_ids[size_t(slot[i])].end());
+            it.blk_begin = begin;
+        }
+        P.block_ids.swap(ids);
+    }
+    // descriptors
+    int path = 1;
+    if (!resize) {
+        int32_t* blob_desc = reinterpret_cast<int32_t*>(P.blob.data() + P.header.off_desc);
+        for (size_t t = 0; t < P.tasks.size(); ++t) {
+            const int i = P.tasks[t].item;
+            if (slot[size_t(i)] < 0) continue;
+            const Item& it = P.items[size_t(i)];
+            const int nb = (it.n_tokens + kBlock - 1) / kBlock;
+            const size_t off = size_t(P.task_desc[t]);
+            int32_t* d = P.desc.data() + off;
+            int32_t lim_all = it.n_tokens;
+            for (int e = 0; e < it.n_q; ++e) {
+                const int32_t lim = P.entries[size_t(it.q_begin + e)].limit;
+                d[kDescHeader + 4 * e + 2] = lim;
+                lim_all = std::min(lim_all, lim);
+            }
+            d[kDescTokens] = it.n_tokens;
+            d[kDescBlocks] = nb;
+            d[kDescLimAll] = lim_all;
+            int32_t* blk = d + kDescHeader + 4 * it.n_q;
+            for (int j = 0; j < nb; ++j) blk[j] = P.block_ids[size_t(it.blk_begin + j)];
+            std::memcpy(blob_desc + off, d, size_t(d[kDescWords]) * 4);
+        }
+    } else {
+        if (!serialize_lists(P)) {
+            // a VALU window overflows: leave the plan as it was
+            P.block_ids.swap(old_ids);
+            P.items.swap(old_items);
+            P.entries.swap(old_entries);
+            if (!serialize_lists(P)) return 0;
+            serialize_blob(P);
+            return 0;
+        }
+        serialize_blob(P);
+        path = 2;
+    }
+    // state and statistics
+    std::copy(block_tables, block_tables + size_t(B) * MB, P.tables.begin());
+    std::copy(seq_lens, seq_lens + B, P.lens.begin());
+    const int64_t bpt = int64_t(2) * s.num_kv_heads * s.head_dim * 2;
+    P.stats.unique_kv_bytes += uniq_add * bpt;
+    P.stats.query_centric_kv_bytes += qc_add * bpt;
+    int64_t planned = 0;
+    for (const Item& it : P.items) planned += it.n_tokens;
+    P.stats.planned_kv_bytes = planned * bpt;
+    P.stats.blob_bytes = P.header.blob_bytes;
+    P.stats.workspace_bytes = P.header.total_bytes;
+    return path;
 }
 
 }  // namespace kvattn
@@ -1052,6 +1247,35 @@ kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables
                      x.unique_kv_bytes / 1e6, x.planned_kv_bytes / 1e6, x.partial_bytes / 1e6, x.plan_seconds * 1e3);
     }
     *out = P;
+    return KVATTN_OK;
+}
+
+kvattn_status kvattn_plan_update(kvattn_plan_t plan, const int32_t* block_tables, const int32_t* seq_lens) {
+    using namespace kvattn;
+    clear_error();
+    if (!plan || !block_tables || !seq_lens) return set_error(KVATTN_EINVAL, "plan, block_tables or seq_lens is NULL");
+    const auto t0 = std::chrono::steady_clock::now();
+    if (kvattn_status vs = check_tables(plan->shape, block_tables, seq_lens); vs != KVATTN_OK) return vs;
+    int path = 0;
+    try {
+        path = extend_plan(*plan, block_tables, seq_lens);
+        if (path == 0) {
+            // the step does not extend the plan's items: plan from scratch
+            kvattn_plan_t fresh = nullptr;
+            const kvattn_status st = kvattn_plan(&plan->shape, block_tables, seq_lens, nullptr, &plan->opts, &fresh);
+            if (st != KVATTN_OK) return st;
+            *plan = std::move(*fresh);
+            delete fresh;
+            path = 3;
+        }
+    } catch (const std::bad_alloc&) {
+        return set_error(KVATTN_ENOMEM, "host allocation failed while updating the plan");
+    }
+    // the device copy of the schedule is stale until the next upload
+    plan->dev_ws = nullptr;
+    plan->dev_bytes = 0;
+    plan->stats.update_path = path;
+    plan->stats.plan_seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
     return KVATTN_OK;
 }
 

@@ -26,6 +26,11 @@ struct kvattn_plan_s {
     std::vector<unsigned char> blob;        // serialised schedule: header + arrays + zero region
     kvattn::BlobHeader header{};
     kvattn_stats stats{};
+    // incremental updates (kvattn_plan_update)
+    std::vector<int32_t> tables;            // [B][max_blocks] block tables of the last plan or update
+    std::vector<int32_t> lens;              // [B] their sequence lengths
+    std::vector<int32_t> entry_item;        // [entries] item of each entry
+    std::vector<int32_t> tail_entry;        // [B] entry holding each query's last token
     void* dev_ws = nullptr;                 // bound device workspace (caller-owned)
     size_t dev_bytes = 0;
 };

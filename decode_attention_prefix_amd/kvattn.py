@@ -46,7 +46,7 @@ class kvattn_stats(ctypes.Structure):
                 ("partial_bytes", i64), ("num_nodes", i32), ("num_packed_nodes", i32), ("num_items", i32),
                 ("num_items_valu", i32), ("num_items_mfma", i32), ("num_folded_leaves", i32),
                 ("num_partial_slots", i32), ("num_merge_rows", i32), ("num_direct_rows", i32),
-                ("num_launches", i32), ("split_tokens", i32), ("num_queued_tasks", i32), ("plan_seconds", f64),
+                ("num_launches", i32), ("split_tokens", i32), ("update_path", i32), ("plan_seconds", f64),
                 ("blob_bytes", u64), ("workspace_bytes", u64)]
 
     def as_dict(self):
@@ -80,6 +80,8 @@ def _load():
     lib.kvattn_plan.argtypes = [ctypes.POINTER(kvattn_shape), P32, P32, ctypes.POINTER(kvattn_prefix_tree),
                                 ctypes.POINTER(kvattn_plan_options), ctypes.POINTER(vp)]
     lib.kvattn_plan.restype = ctypes.c_int
+    lib.kvattn_plan_update.argtypes = [vp, P32, P32]
+    lib.kvattn_plan_update.restype = ctypes.c_int
     lib.kvattn_plan_device_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
     lib.kvattn_plan_device_bytes.restype = ctypes.c_int
     lib.kvattn_plan_upload.argtypes = [vp, vp, ctypes.c_size_t, vp]
@@ -188,6 +190,13 @@ def kvattn_plan(shape, block_tables: np.ndarray, seq_lens: np.ndarray, tree=None
     return Plan(h.value, shape)
 
 
+def kvattn_plan_update(plan: Plan, block_tables: np.ndarray, seq_lens: np.ndarray):
+    """Bring the plan to longer sequences in place; upload it again before decoding."""
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    _check(_lib.kvattn_plan_update(plan.handle, bt.ctypes.data_as(P32), sl.ctypes.data_as(P32)), "kvattn_plan_update")
+
+
 def kvattn_plan_device_bytes(plan: Plan) -> int:
     n = ctypes.c_size_t()
     _check(_lib.kvattn_plan_device_bytes(plan.handle, ctypes.byref(n)), "kvattn_plan_device_bytes")
@@ -275,6 +284,16 @@ class Decoder:
 
     def stats(self):
         return kvattn_plan_stats(self.plan)
+
+    def update(self, block_tables, seq_lens, stream=None):
+        """Next decode step: update the plan in place and upload it (a larger workspace if it grew)."""
+        import torch
+        kvattn_plan_update(self.plan, block_tables, seq_lens)
+        n = kvattn_plan_device_bytes(self.plan)
+        if n > self.workspace.numel():
+            self.workspace = torch.empty(n, dtype=torch.uint8, device=self.workspace.device)
+        self.nbytes = n
+        kvattn_plan_upload(self.plan, self.workspace, self.workspace.numel(), stream)
 
     def decode(self, q, k_cache, v_cache, out, stream=None):
         kvattn_decode(q, k_cache, v_cache, self.plan, out, stream)

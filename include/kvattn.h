@@ -143,7 +143,9 @@ typedef struct {
     int32_t num_direct_rows;         /* rows written by exactly one forward item                */
     int32_t num_launches;            /* kernel launches per kvattn_decode                       */
     int32_t split_tokens;            /* longest chunk of a split KV range (0: nothing split)     */
-    int32_t num_queued_tasks;        /* forward tasks left to the dynamic queues (rest: static)  */
+    int32_t update_path;             /* last kvattn_plan / _update: 0 full plan, 1 descriptors
+                                        patched in place, 2 lists re-serialized, 3 update fell
+                                        back to a full plan                                      */
     double plan_seconds;             /* host wall time of kvattn_plan                            */
     uint64_t blob_bytes;             /* schedule bytes uploaded by kvattn_plan_upload            */
     uint64_t workspace_bytes;        /* = kvattn_plan_device_bytes                               */
@@ -219,6 +221,26 @@ void kvattn_plan_options_default(kvattn_plan_options* opts);
  */
 kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables, const int32_t* seq_lens,
                           const kvattn_prefix_tree* tree, const kvattn_plan_options* opts, kvattn_plan_t* out);
+
+/*
+ * Bring a plan to the next decode step in place (PAT review, overhead
+ * analysis, Fig 16: the pack scheduler's cost next to decoding).  block_tables
+ * and seq_lens describe the same queries (same shape) one or more steps later:
+ * each seq_len is at least the plan's, and the blocks the plan's lengths cover
+ * are unchanged.  When every query's new tokens extend the item that holds its
+ * last token -- its own private item, or a shared item whose end queries all
+ * grow alike into the same new blocks (a session's shared KV growing) -- only
+ * those items, their queries' limits and their descriptors change: nothing is
+ * re-planned, and the item-to-list schedule is kept.  Otherwise (a length
+ * shrinks, a block changes, a new private run starts, an item would exceed its
+ * block cap) the plan is rebuilt from scratch with its options, the tree derived.
+ * stats.update_path tells which happened.  The device copy of the schedule is
+ * stale afterwards: kvattn_plan_upload again before the next kvattn_decode (its
+ * size, kvattn_plan_device_bytes, changes only on a rebuild).
+ * Errors: EINVAL (NULL, seq_len or block id out of range; the plan is then
+ * unchanged), ENOMEM.
+ */
+kvattn_status kvattn_plan_update(kvattn_plan_t plan, const int32_t* block_tables, const int32_t* seq_lens);
 
 /* Device workspace bytes the plan needs: schedule blob + partial triples (256-B aligned). */
 kvattn_status kvattn_plan_device_bytes(kvattn_plan_t plan, size_t* bytes);

@@ -130,6 +130,51 @@ def test_parity_lists_claimed_past_the_grid(c, variant):
                      "%s claims variant %d decode %d" % (wl.name, variant, rep))
 
 
+def _cut_state(wl, cut):
+    import dataclasses
+    lens = (wl.seq_lens - np.asarray(cut, dtype=np.int32)).astype(np.int32)
+    bt = wl.block_tables.copy()
+    for b, T in enumerate(lens):
+        bt[b, (int(T) + 15) // 16:] = -1
+    return dataclasses.replace(wl, seq_lens=lens, block_tables=bt)
+
+
+@pytest.mark.parametrize("kind", ["private", "session"])
+def test_parity_across_plan_updates(kind):
+    """Plan at shortened lengths, then kvattn_plan_update one decode step at a
+    time (crossing block boundaries and descriptor growth); after every step
+    the decode matches the oracle at the current lengths."""
+    rng = np.random.default_rng(21)
+    if kind == "private":
+        segs = [[("root", 96), (("own", b), int(rng.integers(90, 160)))] for b in range(10)]
+        wl = W.from_segments("upd_gpu_private", segs, 8, 2, 128, 21, 721).materialize()
+    else:
+        segs = [[(("sess", s), 480)] for s in range(2) for _ in range(8)]
+        wl = W.from_segments("upd_gpu_session", segs, 16, 2, 128, 22, 722).materialize()
+    k = K()
+    steps = 70
+    cut = np.full(wl.num_queries, steps, dtype=np.int32)
+    cur = _cut_state(wl, cut)
+    print("case plan updates %s" % kind, flush=True)
+    dec = k.Decoder(wl.shape_tuple(), cur.block_tables, cur.seq_lens)
+    q, kc, vc = device_inputs(wl)
+    paths = []
+    for step in range(steps + 1):
+        if step:
+            cut -= 1
+            cur = _cut_state(wl, cut)
+            dec.update(cur.block_tables, cur.seq_lens)
+            paths.append(dec.stats()["update_path"])
+        if step % 7 == 0 or step == steps:
+            out = torch.full((wl.num_queries, wl.num_q_heads, wl.head_dim), float("nan"), dtype=torch.float32,
+                             device="cuda")
+            dec.decode(q, kc, vc, out)
+            torch.cuda.synchronize()
+            ref = oracle.decode_workload(cur)
+            assert_close(out.cpu().numpy().astype(np.float64), ref, "%s update step %d" % (kind, step))
+    assert set(paths) <= {1, 2} and 2 in paths, paths
+
+
 def valu_max_rows(D):
     """Rows per KV head the VALU forward holds (the planner's limit)."""
     return 4 if D == 128 else 8
