@@ -141,6 +141,21 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_bytes": n * 4, "dispatches": 3}))
 
 
+def plan_update_timing(K, wl, opts):
+    """Host time of kvattn_plan_update for one decode step: a plan at every
+    query's length minus one token, brought to the workload's lengths (the
+    path taken: 1 patched in place, 2 re-serialized, 3 rebuilt)."""
+    lens = (wl.seq_lens - 1).astype(np.int32)
+    bt = wl.block_tables.copy()
+    for b, T in enumerate(lens):
+        bt[b, (int(T) + 15) // 16:] = -1
+    plan = K.kvattn_plan(wl.shape_tuple(), bt, lens, None, opts)
+    t0 = time.perf_counter()
+    K.kvattn_plan_update(plan, wl.block_tables, wl.seq_lens)
+    ms = (time.perf_counter() - t0) * 1e3
+    return ms, int(K.kvattn_plan_stats(plan)["update_path"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +195,8 @@ def main():
     plan_upload_ms = (time.perf_counter() - t0) * 1e3
     st = dec.stats()
     log("bench: plan %s" % json.dumps(st))
+    upd_ms, upd_path = plan_update_timing(K, wl, opts)
+    log("bench: plan update (one decode step) %.3f ms, path %d" % (upd_ms, upd_path))
 
     pool_bytes = wl.k_pool.nbytes + wl.v_pool.nbytes
     copies = args.copies or max(1, min(8, math.ceil(3 * 256e6 / pool_bytes) + 1))
@@ -275,6 +292,7 @@ def main():
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "redundancy_fetch_over_unique": None if fetched is None else round(fetched / uniq, 4),
         "plan_ms": round(st["plan_seconds"] * 1e3, 3), "plan_upload_ms": round(plan_upload_ms, 3),
+        "plan_update_ms": round(upd_ms, 3), "plan_update_path": upd_path,
         "plan": {k: st[k] for k in ("num_items", "num_items_valu", "num_items_mfma", "num_packed_nodes",
                                     "num_folded_leaves", "num_merge_rows", "num_launches", "split_tokens",
                                     "planned_kv_bytes", "partial_bytes")},

@@ -1018,7 +1018,9 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
 // into the same new blocks -- only those items, their entries' limits and
 // their descriptors change: no tree, pack, split or list work.  Returns 1 when
 // the descriptors were patched in place, 2 when their sizes changed and the
-// lists were re-serialized, 0 (plan unchanged) when the step does not fit.
+// lists were re-serialized, 0 (plan unchanged) when the step does not fit, -1
+// (plan unchanged) when a new block id is out of range.  Lengths are checked
+// by the caller; old blocks are compared with the plan's, new ones range-checked.
 int extend_plan(kvattn_plan_s& P, const int32_t* block_tables, const int32_t* seq_lens) {
     const kvattn_shape& s = P.shape;
     const int B = s.num_queries, MB = s.max_blocks_per_seq;
@@ -1029,7 +1031,9 @@ int extend_plan(kvattn_plan_s& P, const int32_t* block_tables, const int32_t* se
         const int nb = (P.lens[size_t(b)] + kBlock - 1) / kBlock;
         const int32_t* a = block_tables + size_t(b) * MB;
         const int32_t* o = P.tables.data() + size_t(b) * MB;
-        if (!std::equal(a, a + nb, o)) return 0;
+        if (std::memcmp(a, o, size_t(nb) * 4) != 0) return 0;
+        for (int j = nb; j < (seq_lens[b] + kBlock - 1) / kBlock; ++j)
+            if (a[j] < 0 || a[j] >= s.num_physical_blocks) return -1;
     }
     // growth per item: the entries that grow are exactly those ending with the item
     struct Grow {
@@ -1135,26 +1139,30 @@ int extend_plan(kvattn_plan_s& P, const int32_t* block_tables, const int32_t* se
     // descriptors
     int path = 1;
     if (!resize) {
+        // same record sizes: rewrite the header words, the limits and the new
+        // block ids of the grown items' records, here and in the blob
         int32_t* blob_desc = reinterpret_cast<int32_t*>(P.blob.data() + P.header.off_desc);
         for (size_t t = 0; t < P.tasks.size(); ++t) {
             const int i = P.tasks[t].item;
             if (slot[size_t(i)] < 0) continue;
             const Item& it = P.items[size_t(i)];
+            const std::vector<int32_t>& add = new_ids[size_t(slot[size_t(i)])];
             const int nb = (it.n_tokens + kBlock - 1) / kBlock;
             const size_t off = size_t(P.task_desc[t]);
             int32_t* d = P.desc.data() + off;
+            int32_t* bd = blob_desc + off;
             int32_t lim_all = it.n_tokens;
             for (int e = 0; e < it.n_q; ++e) {
                 const int32_t lim = P.entries[size_t(it.q_begin + e)].limit;
-                d[kDescHeader + 4 * e + 2] = lim;
+                d[kDescHeader + 4 * e + 2] = bd[kDescHeader + 4 * e + 2] = lim;
                 lim_all = std::min(lim_all, lim);
             }
-            d[kDescTokens] = it.n_tokens;
-            d[kDescBlocks] = nb;
-            d[kDescLimAll] = lim_all;
-            int32_t* blk = d + kDescHeader + 4 * it.n_q;
-            for (int j = 0; j < nb; ++j) blk[j] = P.block_ids[size_t(it.blk_begin + j)];
-            std::memcpy(blob_desc + off, d, size_t(d[kDescWords]) * 4);
+            d[kDescTokens] = bd[kDescTokens] = it.n_tokens;
+            d[kDescBlocks] = bd[kDescBlocks] = nb;
+            d[kDescLimAll] = bd[kDescLimAll] = lim_all;
+            const int nb0 = nb - int(add.size());
+            for (size_t j = 0; j < add.size(); ++j)
+                d[kDescHeader + 4 * it.n_q + nb0 + int(j)] = bd[kDescHeader + 4 * it.n_q + nb0 + int(j)] = add[j];
         }
     } else {
         if (!serialize_lists(P)) {
@@ -1169,9 +1177,15 @@ int extend_plan(kvattn_plan_s& P, const int32_t* block_tables, const int32_t* se
         serialize_blob(P);
         path = 2;
     }
-    // state and statistics
-    std::copy(block_tables, block_tables + size_t(B) * MB, P.tables.begin());
-    std::copy(seq_lens, seq_lens + B, P.lens.begin());
+    // state and statistics (the old blocks are unchanged: copy the new ones)
+    for (int b = 0; b < B; ++b) {
+        const int T0 = P.lens[size_t(b)], T1 = seq_lens[b];
+        if (T1 == T0) continue;
+        const size_t row = size_t(b) * MB;
+        std::copy(block_tables + row + (T0 - 1) / kBlock, block_tables + row + (T1 + kBlock - 1) / kBlock,
+                  P.tables.begin() + std::ptrdiff_t(row + (T0 - 1) / kBlock));
+        P.lens[size_t(b)] = T1;
+    }
     const int64_t bpt = int64_t(2) * s.num_kv_heads * s.head_dim * 2;
     P.stats.unique_kv_bytes += uniq_add * bpt;
     P.stats.query_centric_kv_bytes += qc_add * bpt;
@@ -1255,14 +1269,19 @@ kvattn_status kvattn_plan_update(kvattn_plan_t plan, const int32_t* block_tables
     clear_error();
     if (!plan || !block_tables || !seq_lens) return set_error(KVATTN_EINVAL, "plan, block_tables or seq_lens is NULL");
     const auto t0 = std::chrono::steady_clock::now();
-    if (kvattn_status vs = check_tables(plan->shape, block_tables, seq_lens); vs != KVATTN_OK) return vs;
+    const kvattn_shape& s = plan->shape;
+    for (int b = 0; b < s.num_queries; ++b)
+        if (seq_lens[b] < 1 || int64_t(seq_lens[b]) > int64_t(s.max_blocks_per_seq) * kBlock)
+            return set_error(KVATTN_EINVAL, "seq_lens[" + std::to_string(b) + "] = " + std::to_string(seq_lens[b]) +
+                                                " outside [1, max_blocks_per_seq * 16]");
     int path = 0;
     try {
         path = extend_plan(*plan, block_tables, seq_lens);
+        if (path < 0) return check_tables(s, block_tables, seq_lens);   // names the bad block id
         if (path == 0) {
             // the step does not extend the plan's items: plan from scratch
             kvattn_plan_t fresh = nullptr;
-            const kvattn_status st = kvattn_plan(&plan->shape, block_tables, seq_lens, nullptr, &plan->opts, &fresh);
+            const kvattn_status st = kvattn_plan(&s, block_tables, seq_lens, nullptr, &plan->opts, &fresh);
             if (st != KVATTN_OK) return st;
             *plan = std::move(*fresh);
             delete fresh;
