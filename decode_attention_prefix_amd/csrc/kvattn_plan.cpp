@@ -1298,6 +1298,34 @@ kvattn_status kvattn_plan_update(kvattn_plan_t plan, const int32_t* block_tables
     return KVATTN_OK;
 }
 
+kvattn_status kvattn_expand_query_tokens(const kvattn_shape* shape, const int32_t* block_tables,
+                                         const int32_t* seq_lens, const int32_t* q_lens,
+                                         int32_t* out_block_tables, int32_t* out_seq_lens) {
+    using namespace kvattn;
+    clear_error();
+    if (!shape || !block_tables || !seq_lens || !q_lens || !out_block_tables || !out_seq_lens)
+        return set_error(KVATTN_EINVAL, "NULL argument");
+    const int B = shape->num_queries, MB = shape->max_blocks_per_seq;
+    for (int b = 0; b < B; ++b) {
+        if (seq_lens[b] < 1 || int64_t(seq_lens[b]) > int64_t(MB) * kBlock)
+            return set_error(KVATTN_EINVAL, "seq_lens[" + std::to_string(b) + "] outside [1, max_blocks_per_seq * 16]");
+        if (q_lens[b] < 1 || q_lens[b] > seq_lens[b])
+            return set_error(KVATTN_EINVAL, "q_lens[" + std::to_string(b) + "] outside [1, seq_lens[b]]");
+    }
+    size_t row = 0;
+    for (int b = 0; b < B; ++b) {
+        for (int i = 0; i < q_lens[b]; ++i, ++row) {
+            const int T = seq_lens[b] - q_lens[b] + i + 1;
+            const int nb = (T + kBlock - 1) / kBlock;
+            int32_t* dst = out_block_tables + row * size_t(MB);
+            std::copy(block_tables + size_t(b) * MB, block_tables + size_t(b) * MB + nb, dst);
+            std::fill(dst + nb, dst + MB, -1);
+            out_seq_lens[row] = T;
+        }
+    }
+    return KVATTN_OK;
+}
+
 kvattn_status kvattn_plan_device_bytes(kvattn_plan_t plan, size_t* bytes) {
     using namespace kvattn;
     clear_error();

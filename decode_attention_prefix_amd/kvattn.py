@@ -81,6 +81,8 @@ def _load():
                                 ctypes.POINTER(kvattn_plan_options), ctypes.POINTER(vp)]
     lib.kvattn_plan.restype = ctypes.c_int
     lib.kvattn_plan_update.argtypes = [vp, P32, P32]
+    lib.kvattn_expand_query_tokens.argtypes = [ctypes.POINTER(kvattn_shape), P32, P32, P32, P32, P32]
+    lib.kvattn_expand_query_tokens.restype = ctypes.c_int
     lib.kvattn_plan_update.restype = ctypes.c_int
     lib.kvattn_plan_device_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
     lib.kvattn_plan_device_bytes.restype = ctypes.c_int
@@ -195,6 +197,22 @@ def kvattn_plan_update(plan: Plan, block_tables: np.ndarray, seq_lens: np.ndarra
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
     sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
     _check(_lib.kvattn_plan_update(plan.handle, bt.ctypes.data_as(P32), sl.ctypes.data_as(P32)), "kvattn_plan_update")
+
+
+def kvattn_expand_query_tokens(shape, block_tables: np.ndarray, seq_lens: np.ndarray, q_lens: np.ndarray):
+    """One single-token row per new token of multi-token queries: (block_tables, seq_lens) of the rows."""
+    if not isinstance(shape, kvattn_shape):
+        shape = kvattn_shape(*[int(x) for x in shape])
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    ql = np.ascontiguousarray(q_lens, dtype=np.int32)
+    n = int(ql.astype(np.int64).sum()) if ql.size else 0
+    out_bt = np.empty((max(n, 1), shape.max_blocks_per_seq), dtype=np.int32)
+    out_sl = np.empty(max(n, 1), dtype=np.int32)
+    _check(_lib.kvattn_expand_query_tokens(ctypes.byref(shape), bt.ctypes.data_as(P32), sl.ctypes.data_as(P32),
+                                           ql.ctypes.data_as(P32), out_bt.ctypes.data_as(P32),
+                                           out_sl.ctypes.data_as(P32)), "kvattn_expand_query_tokens")
+    return out_bt[:n], out_sl[:n]
 
 
 def kvattn_plan_device_bytes(plan: Plan) -> int:

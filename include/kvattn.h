@@ -242,6 +242,25 @@ kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables
  */
 kvattn_status kvattn_plan_update(kvattn_plan_t plan, const int32_t* block_tables, const int32_t* seq_lens);
 
+/*
+ * Multi-token queries (stateful-streaming digest, method breakdown: a query of
+ * |q| tokens against a session's cached KV, prefix-aware grouped prefill).
+ * Query b brings q_lens[b] >= 1 new tokens: the last q_lens[b] of its
+ * seq_lens[b] tokens, their K/V already in the cache.  New token i of query b
+ * (0-based) attends causally to the first seq_lens[b] - q_lens[b] + i + 1
+ * tokens.  This writes one single-token row per new token, in query order:
+ * out_block_tables [sum q_lens][max_blocks_per_seq] (the query's table, -1
+ * past the row's blocks) and out_seq_lens [sum q_lens] (caller-allocated).
+ * A plan over these rows (num_queries = sum q_lens) packs the tokens of a query
+ * like the queries of a shared prefix, so their KV is fetched once; q and out
+ * then hold [sum q_lens][Hq][D] in the same row order.
+ * Errors: EINVAL (NULL, q_lens[b] outside [1, seq_lens[b]], seq_lens[b] outside
+ * [1, max_blocks_per_seq * 16]).
+ */
+kvattn_status kvattn_expand_query_tokens(const kvattn_shape* shape, const int32_t* block_tables,
+                                         const int32_t* seq_lens, const int32_t* q_lens,
+                                         int32_t* out_block_tables, int32_t* out_seq_lens);
+
 /* Device workspace bytes the plan needs: schedule blob + partial triples (256-B aligned). */
 kvattn_status kvattn_plan_device_bytes(kvattn_plan_t plan, size_t* bytes);
 

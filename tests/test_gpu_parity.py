@@ -175,6 +175,27 @@ def test_parity_across_plan_updates(kind):
     assert set(paths) <= {1, 2} and 2 in paths, paths
 
 
+@pytest.mark.parametrize("m", [3, 24])
+def test_parity_multi_token_queries(m):
+    """Queries of m new tokens, expanded to causal single-token rows by the
+    library and decoded as one packed batch, against the oracle per row."""
+    import dataclasses
+    rng = np.random.default_rng(31 + m)
+    segs = [[("sys", 48), (("sess", b), int(rng.integers(60, 400)))] for b in range(4)]
+    base = W.from_segments("multi_tok_gpu_%d" % m, segs, 16, 4, 128, 31, 731).materialize()
+    k = K()
+    q_lens = np.full(base.num_queries, m, dtype=np.int32)
+    bt, sl = k.kvattn_expand_query_tokens(base.shape_tuple(), base.block_tables, base.seq_lens, q_lens)
+    rows = len(sl)
+    q = W.normal_bf16(base.seed_values, W.TAG_Q, 0, rows * base.num_q_heads * base.head_dim).reshape(
+        rows, base.num_q_heads, base.head_dim)
+    wl = dataclasses.replace(base, name="multi_tok_rows_%d" % m, seq_lens=sl, block_tables=bt, q=q)
+    print("case multi-token m=%d rows %d" % (m, rows), flush=True)
+    got, dec = gpu_decode(wl)
+    assert dec.stats()["num_items_mfma"] > 0 or wl.group * m <= 4
+    assert_close(got, oracle.decode_workload(wl), "multi-token m=%d" % m)
+
+
 def valu_max_rows(D):
     """Rows per KV head the VALU forward holds (the planner's limit)."""
     return 4 if D == 128 else 8
