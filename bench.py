@@ -156,6 +156,73 @@ def plan_update_timing(K, wl, opts):
     return ms, int(K.kvattn_plan_stats(plan)["update_path"])
 
 
+def append_timing(K, torch, W, wl, dec, pools, q, outs, steps, warmup):
+    """The decode step with its KV append fused in (kvattn_decode_append over a
+    new-token plan) against the unfused step (the new K/V written with a torch
+    index_copy_ per cache, then kvattn_decode over the full lengths), both as
+    HIP-graph replays over the rotated KV copies.  Both write the same slots."""
+    try:
+        fused = K.Decoder(wl.shape_tuple(), wl.block_tables, wl.seq_lens, options=K.make_options(new_token=1))
+    except K.KvattnError as e:
+        return {"applicable": False, "reason": str(e)}
+    B, Hkv, D = wl.num_queries, wl.num_kv_heads, wl.head_dim
+    rng = np.random.default_rng(5)
+
+    def bf16_dev(shape):
+        return torch.from_numpy(W.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32)).view(np.int16)).cuda()
+
+    kn, vn = bf16_dev((B, Hkv, D)), bf16_dev((B, Hkv, D))
+    pos = wl.seq_lens.astype(np.int64) - 1
+    blk = wl.block_tables[np.arange(B), pos // 16].astype(np.int64)
+    rows = ((blk[:, None] * Hkv + np.arange(Hkv)[None, :]) * 16 + (pos % 16)[:, None]).reshape(-1)
+    rows = torch.from_numpy(rows).cuda()
+    copies = len(pools)
+
+    def fused_call(i):
+        kk, vv = pools[i % copies]
+        K.kvattn_decode_append(q, kn, vn, kk, vv, fused.plan, outs[i % copies])
+
+    def unfused_call(i):
+        kk, vv = pools[i % copies]
+        kk.view(-1, D).index_copy_(0, rows, kn.view(-1, D))
+        vv.view(-1, D).index_copy_(0, rows, vn.view(-1, D))
+        K.kvattn_decode(q, kk, vv, dec.plan, outs[i % copies])
+
+    # the two steps agree (same slots written, same attention)
+    fused_call(0)
+    torch.cuda.synchronize()
+    a = outs[0].clone()
+    unfused_call(0)
+    torch.cuda.synchronize()
+    agree = float((a - outs[0]).abs().max())
+    assert agree <= 2e-3, "fused and unfused append steps disagree: %.3e" % agree
+    res = {"applicable": True, "max_abs_diff_fused_vs_unfused": agree}
+    graphs = {}
+    for name, fn in (("fused", fused_call), ("unfused", unfused_call)):
+        graphs[name] = []
+        for i in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn(i)
+            graphs[name].append(g)
+    # two alternating rounds, best of each: launch-bound sizes are sensitive to what ran just before
+    best = {}
+    for _ in range(2):
+        for name, gs in graphs.items():
+            for i in range(warmup):
+                gs[i % copies].replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                gs[i % copies].replay()
+            torch.cuda.synchronize()
+            us = (time.perf_counter() - t0) / steps * 1e6
+            best[name] = min(best.get(name, us), us)
+    for name, us in best.items():
+        res[name + "_us_per_call"] = round(us, 2)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,6 +338,9 @@ def main():
     mrg_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(n_ev)])
     call_ms = fwd_ms + mrg_ms
 
+    append = append_timing(K, torch, W, wl, dec, pools, q, outs, min(args.steps, 100), args.warmup)
+    log("bench: decode step with KV append %s" % json.dumps(append))
+
     uniq = wl.unique_kv_bytes
     value = uniq / (ms_per_step * 1e-3) / 1e9
     fwd_avg = float(fwd_ms.mean())
@@ -293,6 +363,7 @@ def main():
         "redundancy_fetch_over_unique": None if fetched is None else round(fetched / uniq, 4),
         "plan_ms": round(st["plan_seconds"] * 1e3, 3), "plan_upload_ms": round(plan_upload_ms, 3),
         "plan_update_ms": round(upd_ms, 3), "plan_update_path": upd_path,
+        "decode_with_kv_append": append,
         "plan": {k: st[k] for k in ("num_items", "num_items_valu", "num_items_mfma", "num_packed_nodes",
                                     "num_folded_leaves", "num_merge_rows", "num_launches", "split_tokens",
                                     "planned_kv_bytes", "partial_bytes")},

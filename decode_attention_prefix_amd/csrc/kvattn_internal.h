@@ -120,9 +120,21 @@ struct Launch {
 };
 
 // Merge record of one query whose rows have several partials: partial k of
-// q head h sits in slot first + k * Hq + h.
+// q head h sits in slot first + k * Hq + h.  In new-token plans every query
+// has one (count may be 0 or 1) and new_slot = block * 16 + slot of its new
+// token's paged position; otherwise new_slot is 0.
 struct alignas(16) MergeRec {
-    int32_t query, first, count, pad;
+    int32_t query, first, count, new_slot;
+};
+constexpr int32_t kMaxNewTokenBlock = 1 << 27;   // block * 16 + slot fits int32
+
+// Inputs of the fused KV append (kvattn_decode_append).
+struct NewTokens {
+    const uint16_t* q;          // bf16 [B][Hq][D]
+    const uint16_t* k_new;      // bf16 [B][Hkv][D]
+    const uint16_t* v_new;
+    uint16_t* k_cache;          // bf16 [blocks][Hkv][16][D]
+    uint16_t* v_cache;
 };
 
 // Pointers the kernels take, resolved from the bound workspace.
@@ -145,6 +157,7 @@ struct Dims {
 int launch_forward(const DevPlan& p, const Dims& d, int valu_rows, int mfma_tiles, int n_tasks,
                    const uint16_t* q, const uint16_t* k, const uint16_t* v, float* out, void* stream);
 int launch_merge(const DevPlan& p, const Dims& d, int q_count, float* out, void* stream);
+int launch_merge_append(const DevPlan& p, const Dims& d, int q_count, const NewTokens& nt, float* out, void* stream);
 
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 

@@ -961,14 +961,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 // and writes A / L.  A query's partials are consecutive [Hq][D] blocks of
 // slots (partial k of q head h in slot first + k Hq + h), located from one
 // record.  Partials are read in batches of eight with every load in flight.
+//
+// With the fused KV append (NEW), the query's newest token, which the forward
+// did not read, starts the combination as one more partial: m = q.k_new in log2
+// units, l = 1, acc = v_new.  Its score is a dot product over the head's D/4
+// lanes (one aligned lane group of the wave); the lanes of the first q head of
+// each KV head also copy k_new / v_new into the token's paged slot.
 // ============================================================================
-template <int D>
-__global__ __launch_bounds__(64) void merge_kernel(DevPlan p, Dims dm, float* __restrict__ out) {
+template <int D, bool NEW>
+__global__ __launch_bounds__(64) void merge_kernel(DevPlan p, Dims dm, NewTokens nt, float* __restrict__ out) {
     constexpr int BATCH = 8;
     const int Hq = dm.num_q_heads;
     const int mq = blockIdx.x;
     const int col = int(blockIdx.y) * 256 + 4 * int(threadIdx.x);   // float index in [Hq][D]
-    if (col >= Hq * D) return;
+    if (col >= Hq * D) return;     // whole heads: a head's lanes leave together
     const int h = col / D;
     // the query, its first partial slot and its partial count (one scalar load)
     const KV_CONST MergeRec* rec = cptr(p.merge_rec) + mq;
@@ -976,6 +982,25 @@ __global__ __launch_bounds__(64) void merge_kernel(DevPlan p, Dims dm, float* __
     const size_t slot0 = size_t(rec->first) + h;
     float M = -INFINITY, L = 0.f;
     float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (NEW) {
+        const int hk = h / dm.group, e0 = col - h * D;
+        const size_t kv = (size_t(b) * dm.num_kv_heads + hk) * D + e0;
+        const uint2 qw = *reinterpret_cast<const uint2*>(nt.q + size_t(b) * Hq * D + col);
+        const uint2 kw = *reinterpret_cast<const uint2*>(nt.k_new + kv);
+        const uint2 vw = *reinterpret_cast<const uint2*>(nt.v_new + kv);
+        float dot = dot2_bf16(qw.y, kw.y, dot2_bf16(qw.x, kw.x, 0.f));
+#pragma unroll
+        for (int o = D / 8; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+        M = dot * dm.scale_log2;
+        L = 1.f;
+        A = make_float4(bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y));
+        if (h % dm.group == 0) {
+            const int code = rec->new_slot;   // block * 16 + slot
+            const size_t at = ((size_t(code >> 4) * dm.num_kv_heads + hk) * 16 + (code & 15)) * D + e0;
+            *reinterpret_cast<uint2*>(nt.k_cache + at) = kw;
+            *reinterpret_cast<uint2*>(nt.v_cache + at) = vw;
+        }
+    }
     for (int ib = 0; ib < n; ib += BATCH) {
         float2 ml[BATCH];
         float4 ac[BATCH];
@@ -1052,10 +1077,24 @@ int launch_merge(const DevPlan& p, const Dims& d, int q_count, float* out, void*
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (q_count <= 0) return 0;
     const unsigned ny = unsigned((d.num_q_heads * d.head_dim + 255) / 256);
+    const NewTokens none{};
     if (d.head_dim == 128)
-        hipLaunchKernelGGL((merge_kernel<128>), dim3(q_count, ny), dim3(64), 0, s, p, d, out);
+        hipLaunchKernelGGL((merge_kernel<128, false>), dim3(q_count, ny), dim3(64), 0, s, p, d, none, out);
     else if (d.head_dim == 64)
-        hipLaunchKernelGGL((merge_kernel<64>), dim3(q_count, ny), dim3(64), 0, s, p, d, out);
+        hipLaunchKernelGGL((merge_kernel<64, false>), dim3(q_count, ny), dim3(64), 0, s, p, d, none, out);
+    else
+        return int(hipErrorInvalidValue);
+    return int(hipGetLastError());
+}
+
+int launch_merge_append(const DevPlan& p, const Dims& d, int q_count, const NewTokens& nt, float* out, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (q_count <= 0) return 0;
+    const unsigned ny = unsigned((d.num_q_heads * d.head_dim + 255) / 256);
+    if (d.head_dim == 128)
+        hipLaunchKernelGGL((merge_kernel<128, true>), dim3(q_count, ny), dim3(64), 0, s, p, d, nt, out);
+    else if (d.head_dim == 64)
+        hipLaunchKernelGGL((merge_kernel<64, true>), dim3(q_count, ny), dim3(64), 0, s, p, d, nt, out);
     else
         return int(hipErrorInvalidValue);
     return int(hipGetLastError());

@@ -83,6 +83,53 @@ kvattn_status check_tables(const kvattn_shape& s, const int32_t* block_tables, c
     return KVATTN_OK;
 }
 
+// Per physical block, the most tokens any query's first lens[b] tokens read from it.
+std::vector<int32_t> block_reads(const kvattn_shape& s, const int32_t* block_tables, const int32_t* lens) {
+    std::vector<int32_t> r(size_t(s.num_physical_blocks), 0);
+    for (int b = 0; b < s.num_queries; ++b) {
+        const int T = lens[b];
+        for (int j = 0; j * kBlock < T; ++j) {
+            int32_t& x = r[size_t(block_tables[size_t(b) * s.max_blocks_per_seq + j])];
+            x = std::max(x, int32_t(std::min(kBlock, T - j * kBlock)));
+        }
+    }
+    return r;
+}
+
+// New-token plans: query b's new token goes to position cached[b], slot
+// cached[b] % 16 of block block_tables[b][cached[b] / 16] (ids range-checked by
+// the caller).  Its slot must be the query's alone: no two queries' new tokens
+// in one block (one slot: two writers; two slots: the later one's cached part
+// reads the earlier one's new slot), and no cached read covering a new slot
+// (reads_of(id) = most tokens any cached part reads from block id).  Writes
+// block * 16 + slot per query into code.
+template <typename Reads>
+kvattn_status check_new_slots(const kvattn_shape& s, const int32_t* block_tables, const int32_t* cached,
+                              Reads reads_of, std::vector<int32_t>& code) {
+    const int B = s.num_queries;
+    std::vector<std::pair<int32_t, int>> owner(static_cast<size_t>(B));
+    code.resize(size_t(B));
+    for (int b = 0; b < B; ++b) {
+        const int32_t id = block_tables[size_t(b) * s.max_blocks_per_seq + cached[b] / kBlock];
+        if (id >= kMaxNewTokenBlock)
+            return set_error(KVATTN_EUNSUPPORTED, "new token of query " + std::to_string(b) + " in block " +
+                                                      std::to_string(id) + " >= 2^27");
+        const int slot = cached[b] % kBlock;
+        if (reads_of(id) > slot)
+            return set_error(KVATTN_EINVAL, "new token slot " + std::to_string(slot) + " of block " + std::to_string(id) +
+                                                " (query " + std::to_string(b) + ") is read by a cached part");
+        owner[size_t(b)] = {id, b};
+        code[size_t(b)] = id * kBlock + slot;
+    }
+    std::sort(owner.begin(), owner.end());
+    for (int b = 1; b < B; ++b)
+        if (owner[size_t(b)].first == owner[size_t(b) - 1].first)
+            return set_error(KVATTN_EINVAL, "queries " + std::to_string(owner[size_t(b) - 1].second) + " and " +
+                                                std::to_string(owner[size_t(b)].second) + " put their new tokens in block " +
+                                                std::to_string(owner[size_t(b)].first));
+    return KVATTN_OK;
+}
+
 // Maximal tree: a node is a maximal run of positions over which one fixed set
 // of queries holds the same (physical block, token count) keys.
 void derive_tree(const Batch& bt, std::vector<Node>& nodes, std::vector<int>& leaf) {
@@ -110,9 +157,10 @@ void derive_tree(const Batch& bt, std::vector<Node>& nodes, std::vector<int>& le
             for (int c : created) nodes[parent].children.push_back(c);
         for (auto it = created.rbegin(); it != created.rend(); ++it) stack.push_back(*it);
     };
-    std::vector<int> all(bt.B);
-    std::iota(all.begin(), all.end(), 0);
-    make_children(all, 0, -1);
+    std::vector<int> all;               // queries with a cached part
+    for (int b = 0; b < bt.B; ++b)
+        if (bt.nb[b] > 0) all.push_back(b);
+    if (!all.empty()) make_children(all, 0, -1);
     while (!stack.empty()) {
         int n = stack.back();
         stack.pop_back();
@@ -169,6 +217,7 @@ kvattn_status adopt_tree(const Batch& bt, const kvattn_prefix_tree& t, std::vect
     }
     for (int b = 0; b < bt.B; ++b) {
         int lf = t.query_leaf[b];
+        if (bt.nb[b] == 0 && lf == -1) continue;   // no cached part (new-token plans)
         if (lf < 0 || lf >= N) return set_error(KVATTN_EINVAL, "prefix tree: bad leaf of query " + std::to_string(b));
         if (nodes[lf].pos_end != bt.nb[b])
             return set_error(KVATTN_EINVAL, "prefix tree: leaf of query " + std::to_string(b) + " does not end at its last block");
@@ -356,8 +405,21 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     const auto t0 = std::chrono::steady_clock::now();
     const int B = s.num_queries, Hq = s.num_q_heads, Hkv = s.num_kv_heads, D = s.head_dim;
     const int G = Hq / Hkv;
-    Batch bt{B, s.max_blocks_per_seq, block_tables, seq_lens, std::vector<int>(B)};
     if (kvattn_status vs = check_tables(s, block_tables, seq_lens); vs != KVATTN_OK) return vs;
+    // New-token plans cover each query's cached part, its first seq_len - 1
+    // tokens; the last one comes with the call and joins in the merge.
+    std::vector<int32_t> cached;
+    std::vector<int32_t> new_slot;
+    if (o.new_token) {
+        cached.resize(size_t(B));
+        for (int b = 0; b < B; ++b) cached[size_t(b)] = seq_lens[b] - 1;
+        seq_lens = cached.data();
+        P.reads = block_reads(s, block_tables, seq_lens);
+        kvattn_status ns = check_new_slots(s, block_tables, seq_lens, [&](int32_t id) { return P.reads[size_t(id)]; },
+                                           new_slot);
+        if (ns != KVATTN_OK) return ns;
+    }
+    Batch bt{B, s.max_blocks_per_seq, block_tables, seq_lens, std::vector<int>(B)};
     for (int b = 0; b < B; ++b) bt.nb[b] = (seq_lens[b] + kBlock - 1) / kBlock;
 
     // ---- prefix tree ---------------------------------------------------------
@@ -855,8 +917,10 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     std::vector<int32_t> slot_base(B, -1);
     std::vector<int> item_proto;
     int32_t slots_used = 0;
+    // rows with one partial write out directly, unless the new token joins them in the merge
+    const int min_merged = o.new_token ? 1 : 2;
     for (int b = 0; b < B; ++b)
-        if (count[b] > 1) {
+        if (count[b] >= min_merged) {
             slot_base[b] = slots_used;
             slots_used += count[b] * Hq;
         }
@@ -865,7 +929,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         p.it.q_begin = int32_t(P.entries.size());
         p.it.blk_begin = int32_t(P.block_ids.size());
         for (Entry e : p.entries) {
-            if (count[e.query] > 1) {
+            if (count[e.query] >= min_merged) {
                 e.dest = slot_base[e.query] + int32_t(dests[e.query].size()) * Hq;
                 dests[e.query].push_back(e.dest);
             }
@@ -882,11 +946,11 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     P.merge_rec.clear();
     int direct_rows = 0;
     for (int b = 0; b < B; ++b) {
-        if (count[b] == 1) {
+        if (count[b] < min_merged && !o.new_token) {
             direct_rows += Hq;
             continue;
         }
-        P.merge_rec.insert(P.merge_rec.end(), {b, slot_base[b], count[b], 0});
+        P.merge_rec.insert(P.merge_rec.end(), {b, std::max(slot_base[b], 0), count[b], o.new_token ? new_slot[size_t(b)] : 0});
         P.merge_query.push_back(b);
         P.merge_dest.insert(P.merge_dest.end(), dests[b].begin(), dests[b].end());
         P.merge_ptr.push_back(int32_t(P.merge_dest.size()));
@@ -957,15 +1021,9 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     kvattn_stats& st = P.stats;
     std::memset(&st, 0, sizeof(st));
     {
-        std::vector<int32_t> maxv(size_t(s.num_physical_blocks), 0);
         int64_t qc = 0;
-        for (int b = 0; b < B; ++b) {
-            qc += seq_lens[b];
-            for (int j = 0; j < bt.nb[b]; ++j) {
-                int32_t id = bt.id(b, j);
-                maxv[id] = std::max(maxv[id], int32_t(bt.valid(b, j)));
-            }
-        }
+        for (int b = 0; b < B; ++b) qc += seq_lens[b];
+        const std::vector<int32_t> maxv = o.new_token ? P.reads : block_reads(s, block_tables, seq_lens);
         int64_t uniq = 0;
         for (int32_t v : maxv) uniq += v;
         st.unique_kv_bytes = uniq * bpt;
@@ -1021,7 +1079,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
 // lists were re-serialized, 0 (plan unchanged) when the step does not fit, -1
 // (plan unchanged) when a new block id is out of range.  Lengths are checked
 // by the caller; old blocks are compared with the plan's, new ones range-checked.
-int extend_plan(kvattn_plan_s& P, const int32_t* block_tables, const int32_t* seq_lens) {
+int extend_plan(kvattn_plan_s& P, const int32_t* block_tables, const int32_t* seq_lens, kvattn_status& err) {
     const kvattn_shape& s = P.shape;
     const int B = s.num_queries, MB = s.max_blocks_per_seq;
     if (P.lens.size() != size_t(B) || P.tail_entry.size() != size_t(B)) return 0;
@@ -1057,7 +1115,8 @@ int extend_plan(kvattn_plan_s& P, const int32_t* block_tables, const int32_t* se
         if (g.delta != d) return 0;
         g.growing++;
     }
-    if (grow.empty()) return 1;
+    // (new-token plans go on: the new tokens' slots move even when nothing grows)
+    if (grow.empty() && !P.opts.new_token) return 1;
     int64_t uniq_add = 0, qc_add = 0;
     for (int b = 0; b < B; ++b) qc_add += seq_lens[b] - P.lens[size_t(b)];
     bool resize = false;
@@ -1083,8 +1142,8 @@ int extend_plan(kvattn_plan_s& P, const int32_t* block_tables, const int32_t* se
         resize |= desc_words(it.n_q, nb1) != desc_words(it.n_q, nb0);
     }
     // unique tokens: the valid-token count each touched physical block gains
+    std::vector<std::pair<int32_t, int>> touched;   // (block id, valid tokens after the step), sorted
     {
-        std::vector<std::pair<int32_t, int>> touched;   // (block id, valid tokens after the step)
         for (int b = 0; b < B; ++b) {
             const int T0 = P.lens[size_t(b)], T1 = seq_lens[b];
             if (T1 == T0) continue;
@@ -1104,6 +1163,18 @@ int extend_plan(kvattn_plan_s& P, const int32_t* block_tables, const int32_t* se
             }
             uniq_add += touched[x].second - before;
         }
+    }
+    // new-token plans: the new tokens' slots, checked against the reads after the step
+    std::vector<int32_t> new_slot;
+    if (P.opts.new_token) {
+        auto reads_of = [&](int32_t id) {
+            int32_t r = P.reads[size_t(id)];
+            auto it = std::upper_bound(touched.begin(), touched.end(), std::make_pair(id, std::numeric_limits<int>::max()));
+            if (it != touched.begin() && std::prev(it)->first == id) r = std::max(r, int32_t(std::prev(it)->second));
+            return r;
+        };
+        err = check_new_slots(s, block_tables, seq_lens, reads_of, new_slot);
+        if (err != KVATTN_OK) return -2;
     }
     // apply: items, entries, block ids
     std::vector<int32_t> old_ids;
@@ -1186,6 +1257,12 @@ int extend_plan(kvattn_plan_s& P, const int32_t* block_tables, const int32_t* se
                   P.tables.begin() + std::ptrdiff_t(row + (T0 - 1) / kBlock));
         P.lens[size_t(b)] = T1;
     }
+    if (P.opts.new_token) {
+        for (const auto& t : touched) P.reads[size_t(t.first)] = std::max(P.reads[size_t(t.first)], int32_t(t.second));
+        int32_t* blob_rec = reinterpret_cast<int32_t*>(P.blob.data() + P.header.off_merge_rec);
+        for (size_t r = 0; r < P.merge_rec.size() / 4; ++r)
+            P.merge_rec[4 * r + 3] = blob_rec[4 * r + 3] = new_slot[size_t(P.merge_rec[4 * r])];
+    }
     const int64_t bpt = int64_t(2) * s.num_kv_heads * s.head_dim * 2;
     P.stats.unique_kv_bytes += uniq_add * bpt;
     P.stats.query_centric_kv_bytes += qc_add * bpt;
@@ -1212,6 +1289,7 @@ void kvattn_plan_options_default(kvattn_plan_options* o) {
     o->force_variant = KVATTN_VARIANT_AUTO;
     o->split_tokens = 0;
     o->num_cus = 0;
+    o->new_token = 0;
 }
 
 kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables, const int32_t* seq_lens,
@@ -1234,7 +1312,8 @@ kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables
     kvattn_plan_options_default(&o);
     if (opts) o = *opts;
     if (o.pack_mode < 0 || o.pack_mode > 2 || o.scheme < 0 || o.scheme > 2 || o.force_variant < -1 ||
-        o.force_variant > 1 || o.split_tokens < 0 || o.num_cus < 0 || !(o.scale >= 0.f) || std::isinf(o.scale))
+        o.force_variant > 1 || o.split_tokens < 0 || o.num_cus < 0 || !(o.scale >= 0.f) || std::isinf(o.scale) ||
+        o.new_token < 0 || o.new_token > 1)
         return set_error(KVATTN_EINVAL, "bad option value");
     kvattn_plan_s* P = new (std::nothrow) kvattn_plan_s();
     if (!P) return set_error(KVATTN_ENOMEM, "plan allocation failed");
@@ -1274,9 +1353,23 @@ kvattn_status kvattn_plan_update(kvattn_plan_t plan, const int32_t* block_tables
         if (seq_lens[b] < 1 || int64_t(seq_lens[b]) > int64_t(s.max_blocks_per_seq) * kBlock)
             return set_error(KVATTN_EINVAL, "seq_lens[" + std::to_string(b) + "] = " + std::to_string(seq_lens[b]) +
                                                 " outside [1, max_blocks_per_seq * 16]");
+    // new-token plans extend over the cached parts; their new tokens' blocks are range-checked here
+    const int32_t* lens = seq_lens;
+    std::vector<int32_t> cached;
+    if (plan->opts.new_token) {
+        cached.resize(size_t(s.num_queries));
+        for (int b = 0; b < s.num_queries; ++b) {
+            cached[size_t(b)] = seq_lens[b] - 1;
+            const int32_t id = block_tables[size_t(b) * s.max_blocks_per_seq + cached[size_t(b)] / kBlock];
+            if (id < 0 || id >= s.num_physical_blocks) return check_tables(s, block_tables, seq_lens);
+        }
+        lens = cached.data();
+    }
     int path = 0;
     try {
-        path = extend_plan(*plan, block_tables, seq_lens);
+        kvattn_status err = KVATTN_OK;
+        path = extend_plan(*plan, block_tables, lens, err);
+        if (path == -2) return err;                                       // new-token slot conflict
         if (path < 0) return check_tables(s, block_tables, seq_lens);   // names the bad block id
         if (path == 0) {
             // the step does not extend the plan's items: plan from scratch
@@ -1365,6 +1458,7 @@ kvattn_status kvattn_plan_export(kvattn_plan_t plan, kvattn_export* out) {
     out->num_desc_words = int32_t(plan->desc.size());
     out->desc = plan->desc.data();
     out->list_ptr = plan->desc_list_ptr.data();
+    out->merge_rec = plan->merge_rec.data();
     return KVATTN_OK;
 }
 

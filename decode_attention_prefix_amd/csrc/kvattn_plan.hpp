@@ -14,7 +14,7 @@ struct kvattn_plan_s {
     std::vector<kvattn::Entry> entries;
     std::vector<int32_t> block_ids;
     std::vector<int32_t> merge_query, merge_ptr, merge_dest;   // host copy (export)
-    std::vector<int32_t> merge_rec;                            // device: (b, slot base, partials, 0) per merged query
+    std::vector<int32_t> merge_rec;                            // device: (b, slot base, partials, new-token slot) per merged query
     int32_t n_slots = 0;
     std::vector<kvattn::Task> tasks;
     std::vector<int32_t> list_ptr;          // [launch][n_lists + 1] task ranges of the static lists
@@ -31,6 +31,7 @@ struct kvattn_plan_s {
     std::vector<int32_t> lens;              // [B] their sequence lengths
     std::vector<int32_t> entry_item;        // [entries] item of each entry
     std::vector<int32_t> tail_entry;        // [B] entry holding each query's last token
+    std::vector<int32_t> reads;             // new-token plans: [num_physical_blocks] most tokens a cached part reads
     void* dev_ws = nullptr;                 // bound device workspace (caller-owned)
     size_t dev_bytes = 0;
 };

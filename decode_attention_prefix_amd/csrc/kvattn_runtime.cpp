@@ -64,6 +64,8 @@ kvattn_status run_forward(const void* q, const void* k, const void* v, kvattn_pl
 
 kvattn_status run_merge(kvattn_plan_t plan, float* out, void* stream) {
     if (!out) return set_error(KVATTN_EINVAL, "out is NULL");
+    if (plan->opts.new_token)
+        return set_error(KVATTN_EINVAL, "the plan takes each query's newest token from the call: use kvattn_decode_append");
     const DevPlan dp = resolve(*plan, -1);
     const Dims d = dims(*plan);
     const int rc = launch_merge(dp, d, int(plan->merge_query.size()), out, stream);
@@ -116,9 +118,36 @@ kvattn_status kvattn_decode(const void* q, const void* k_cache, const void* v_ca
     clear_error();
     kvattn_status s = check_bound(plan);
     if (s != KVATTN_OK) return s;
+    if (plan->opts.new_token)
+        return set_error(KVATTN_EINVAL, "the plan takes each query's newest token from the call: use kvattn_decode_append");
     s = run_forward(q, k_cache, v_cache, plan, out, stream);
     if (s != KVATTN_OK) return s;
     return run_merge(plan, out, stream);
+}
+
+kvattn_status kvattn_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                   kvattn_plan_t plan, float* out, void* stream) {
+    using namespace kvattn;
+    clear_error();
+    kvattn_status s = check_bound(plan);
+    if (s != KVATTN_OK) return s;
+    if (!plan->opts.new_token) return set_error(KVATTN_EINVAL, "the plan was made without new_token: use kvattn_decode");
+    if (!k_new || !v_new) return set_error(KVATTN_EINVAL, "k_new or v_new is NULL");
+    if (!aligned16(k_new) || !aligned16(v_new)) return set_error(KVATTN_EINVAL, "k_new and v_new must be 16-byte aligned");
+    // the forward reads the cached parts only; the merge adds the new tokens and writes them into the cache
+    s = run_forward(q, k_cache, v_cache, plan, out, stream);
+    if (s != KVATTN_OK) return s;
+    const DevPlan dp = resolve(*plan, -1);
+    const Dims d = dims(*plan);
+    NewTokens nt;
+    nt.q = static_cast<const uint16_t*>(q);
+    nt.k_new = static_cast<const uint16_t*>(k_new);
+    nt.v_new = static_cast<const uint16_t*>(v_new);
+    nt.k_cache = static_cast<uint16_t*>(k_cache);
+    nt.v_cache = static_cast<uint16_t*>(v_cache);
+    const int rc = launch_merge_append(dp, d, int(plan->merge_query.size()), nt, out, stream);
+    if (rc != 0) return set_error(KVATTN_EHIP, std::string("merge launch failed: ") + hipGetErrorString(hipError_t(rc)));
+    return KVATTN_OK;
 }
 
 }  // extern "C"

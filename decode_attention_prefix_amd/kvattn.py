@@ -38,7 +38,7 @@ class kvattn_prefix_tree(ctypes.Structure):
 
 class kvattn_plan_options(ctypes.Structure):
     _fields_ = [("scale", f32), ("pack_mode", i32), ("scheme", i32), ("force_variant", i32), ("split_tokens", i32),
-                ("num_cus", i32)]
+                ("num_cus", i32), ("new_token", i32)]
 
 
 class kvattn_stats(ctypes.Structure):
@@ -68,7 +68,7 @@ class kvattn_export(ctypes.Structure):
                 ("num_merge_queries", i32), ("merge_query", P32), ("merge_ptr", P32), ("merge_dest", P32),
                 ("num_partial_slots", i32), ("head_dim", i32), ("num_tasks", i32), ("tasks", P32),
                 ("num_launches", i32), ("num_lists", i32), ("num_desc_words", i32), ("desc", P32),
-                ("list_ptr", P32)]
+                ("list_ptr", P32), ("merge_rec", P32)]
 
 
 def _load():
@@ -91,6 +91,8 @@ def _load():
     for name in ("kvattn_decode", "kvattn_forward"):
         getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, vp]
         getattr(lib, name).restype = ctypes.c_int
+    lib.kvattn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.kvattn_decode_append.restype = ctypes.c_int
     lib.kvattn_merge.argtypes = [vp, vp, vp]
     lib.kvattn_merge.restype = ctypes.c_int
     lib.kvattn_plan_stats.argtypes = [vp, ctypes.POINTER(kvattn_stats)]
@@ -234,6 +236,11 @@ def kvattn_decode(q, k_cache, v_cache, plan: Plan, out, stream=None):
            "kvattn_decode")
 
 
+def kvattn_decode_append(q, k_new, v_new, k_cache, v_cache, plan: Plan, out, stream=None):
+    _check(_lib.kvattn_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), plan.handle,
+                                     _ptr(out), _stream(stream)), "kvattn_decode_append")
+
+
 def kvattn_forward(q, k_cache, v_cache, plan: Plan, out, stream=None):
     _check(_lib.kvattn_forward(_ptr(q), _ptr(k_cache), _ptr(v_cache), plan.handle, _ptr(out), _stream(stream)),
            "kvattn_forward")
@@ -275,6 +282,7 @@ def kvattn_plan_export(plan: Plan) -> dict:
         "num_lists": e.num_lists,
         "desc": arr(e.desc, e.num_desc_words, 1).reshape(-1),
         "list_ptr": arr(e.list_ptr, e.num_launches * e.num_lists * 3, 1).reshape(e.num_launches, e.num_lists, 3),
+        "merge_rec": arr(e.merge_rec, e.num_merge_queries, 4),
     }
 
 
@@ -315,4 +323,9 @@ class Decoder:
 
     def decode(self, q, k_cache, v_cache, out, stream=None):
         kvattn_decode(q, k_cache, v_cache, self.plan, out, stream)
+        return out
+
+    def decode_append(self, q, k_new, v_new, k_cache, v_cache, out, stream=None):
+        """Plans made with new_token=1: write each query's new K/V into the cache and attend."""
+        kvattn_decode_append(q, k_new, v_new, k_cache, v_cache, self.plan, out, stream)
         return out

@@ -116,6 +116,16 @@ enum { KVATTN_VARIANT_AUTO = -1, KVATTN_VARIANT_VALU = 0, KVATTN_VARIANT_MFMA = 
  *   split_tokens   0 auto; otherwise the KV chunk length of split items, rounded
  *                  up to a multiple of 16 (long-KV splitting).
  *   num_cus        compute units the split model balances over; 0 means 256.
+ *   new_token      0: seq_lens count tokens already in the cache (kvattn_decode).
+ *                  1: the last token of each query, position seq_len - 1, comes
+ *                  with the call as k_new / v_new (kvattn_decode_append), which
+ *                  writes it into its paged slot and attends to it; the plan
+ *                  covers the first seq_len - 1 tokens, read from the cache
+ *                  (short-term-memory page, technical principles, the KV cache
+ *                  in autoregressive generation: a step appends its token's K
+ *                  and V, then attends to all of them).  The new token's slot
+ *                  must belong to its query alone: no other query reads it
+ *                  (copy-on-write paging), else kvattn_plan returns EINVAL.
  */
 typedef struct {
     float scale;
@@ -124,6 +134,7 @@ typedef struct {
     int32_t force_variant;
     int32_t split_tokens;
     int32_t num_cus;
+    int32_t new_token;
 } kvattn_plan_options;
 
 /* Statistics of a plan (bytes are per decode call, all KV heads). */
@@ -201,6 +212,9 @@ typedef struct {
     int32_t num_desc_words;
     const int32_t* desc;
     const int32_t* list_ptr;      /* [num_launches][num_lists][3]              */
+    const int32_t* merge_rec;     /* [num_merge_queries][4] as uploaded: b, first partial slot,
+                                     partial count, and in new-token plans block * 16 + slot
+                                     of the query's new token (else 0)                        */
 } kvattn_export;
 
 /* Fill *opts with the defaults (AUTO packing, scheme auto, auto variant and split). */
@@ -216,8 +230,12 @@ void kvattn_plan_options_default(kvattn_plan_options* opts);
  *   *out receives a plan owned by the caller until kvattn_plan_destroy.
  * Errors: EINVAL (NULL pointer, B/H/D <= 0, Hq % Hkv, seq_len outside
  * [1, max_blocks*16], block id outside [0, num_physical_blocks), bad tree or
- * option), EUNSUPPORTED (head_dim not 64/128, block_size != 16, Hq/Hkv > 64),
- * ENOMEM.  Reentrant; plans are independent.
+ * option; with new_token: two queries' new tokens in one block, or a query
+ * reading another's new-token slot), EUNSUPPORTED (head_dim not 64/128,
+ * block_size != 16, Hq/Hkv > 64; with new_token, a new-token block id >= 2^27),
+ * ENOMEM.  Reentrant; plans are independent.  With new_token, a tree (if
+ * given) describes the cached part, the first seq_len - 1 tokens of each query;
+ * a query with seq_len 1 has no cached part and query_leaf -1.
  */
 kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables, const int32_t* seq_lens,
                           const kvattn_prefix_tree* tree, const kvattn_plan_options* opts, kvattn_plan_t* out);
@@ -237,8 +255,11 @@ kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables
  * stats.update_path tells which happened.  The device copy of the schedule is
  * stale afterwards: kvattn_plan_upload again before the next kvattn_decode (its
  * size, kvattn_plan_device_bytes, changes only on a rebuild).
- * Errors: EINVAL (NULL, seq_len or block id out of range; the plan is then
- * unchanged), ENOMEM.
+ * New-token plans (options.new_token) take seq_lens with each query's new
+ * token, as kvattn_plan does: the cached parts are extended, each merge record
+ * gets its query's new slot, and the slot-ownership rule is checked again.
+ * Errors: EINVAL (NULL, seq_len or block id out of range, a new-token slot
+ * that another query reads or shares; the plan is then unchanged), ENOMEM.
  */
 kvattn_status kvattn_plan_update(kvattn_plan_t plan, const int32_t* block_tables, const int32_t* seq_lens);
 
@@ -281,17 +302,39 @@ kvattn_status kvattn_plan_upload(kvattn_plan_t plan, void* dev_workspace, size_t
  * The bound workspace holds the partial triples, so at most one decode per
  * workspace may be in flight.  One plan serves any number of calls (e.g. every
  * layer of a decode step) with different q / caches of the same shape.
- * Errors: EINVAL (NULL), ESTATE (no workspace bound), EHIP (launch failed).
+ * Errors: EINVAL (NULL, plan made with new_token: use kvattn_decode_append),
+ * ESTATE (no workspace bound), EHIP (launch failed).
  */
 kvattn_status kvattn_decode(const void* q, const void* k_cache, const void* v_cache, kvattn_plan_t plan,
                             float* out, void* stream);
+
+/*
+ * One decode step with the KV append fused in (short-term-memory page,
+ * technical principles, the KV cache in autoregressive generation: append the
+ * step's K and V to the cache, then attend over all cached tokens).  The plan
+ * must have been made with options.new_token = 1.  k_new, v_new: device bf16
+ * [B][Hkv][D], the K and V of each query's newest token (position
+ * seq_len[b] - 1).  The forward kernels read the first seq_len[b] - 1 tokens
+ * from the cache; the merge kernel scores the new token against q, folds it
+ * into each row's online softmax as one more partial, and copies k_new / v_new
+ * (bit-exact) into slot (seq_len[b] - 1) % 16 of block
+ * block_tables[b][(seq_len[b] - 1) / 16] of k_cache / v_cache.  No kernel of
+ * the call reads that slot, so out equals attention over the cache after the
+ * append.  Two launches, as kvattn_decode; every row goes through the merge.
+ * Calling it again with the same inputs rewrites the same bytes.
+ * Errors: EINVAL (NULL or misaligned pointer, plan made without new_token),
+ * ESTATE (no workspace bound), EHIP (launch failed).
+ */
+kvattn_status kvattn_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                   void* v_cache, kvattn_plan_t plan, float* out, void* stream);
 
 /* The forward stage of kvattn_decode alone (PAT review, forward stage). */
 kvattn_status kvattn_forward(const void* q, const void* k_cache, const void* v_cache, kvattn_plan_t plan,
                              float* out, void* stream);
 
 /* The merge stage of kvattn_decode alone (PAT review, merge stage); reads the
- * partial triples the last kvattn_forward on this workspace wrote. */
+ * partial triples the last kvattn_forward on this workspace wrote.  EINVAL for
+ * a plan made with new_token (its merge needs the new token's inputs). */
 kvattn_status kvattn_merge(kvattn_plan_t plan, float* out, void* stream);
 
 /* Plan statistics (host only). */

@@ -5,7 +5,9 @@ import this package.  The library (decode_attention_prefix_amd) never does,
 and this package imports nothing from it.
 
 The arithmetic lives in kvattn_oracle.c (plain C, double precision, compiled
-with gcc); this file only marshals numpy arrays through ctypes.
+with gcc); this file marshals numpy arrays through ctypes and holds the one
+step without arithmetic, the append of a decode step's new token to the paged
+cache (numpy indexing).
 """
 from __future__ import annotations
 
@@ -80,6 +82,28 @@ def decode_all(q, k_pool, v_pool, block_tables, seq_lens, num_q_heads, num_kv_he
     rows = np.arange(B * num_q_heads, dtype=np.int64)
     return decode_rows(q, k_pool, v_pool, block_tables, seq_lens, num_q_heads, num_kv_heads, rows, scale,
                        block_size).reshape(B, num_q_heads, D)
+
+
+def append_tokens(k_pool, v_pool, block_tables, seq_lens, k_new, v_new, block_size=16):
+    """The KV pools after one decode step's append -> new (k_pool, v_pool) arrays.
+
+    Short-term-memory page, technical principles (the KV cache in
+    autoregressive generation): a step computes its token's K and V and adds
+    them to the cache before attending over every cached token.  With paging
+    (PagedAttention section) query b's newest token, position seq_lens[b] - 1,
+    sits in block block_tables[b][pos // block_size], slot pos % block_size;
+    each KV head's row of that slot receives k_new[b][head] (likewise V).
+    Pools: uint16 bf16 bits [n_blocks][Hkv][block_size][D]; k_new, v_new:
+    uint16 [B][Hkv][D].  The inputs are not modified.
+    """
+    k = np.array(k_pool, dtype=np.uint16, copy=True)
+    v = np.array(v_pool, dtype=np.uint16, copy=True)
+    for b, T in enumerate(np.asarray(seq_lens).tolist()):
+        pos = int(T) - 1
+        blk = int(block_tables[b][pos // block_size])
+        k[blk, :, pos % block_size, :] = k_new[b]
+        v[blk, :, pos % block_size, :] = v_new[b]
+    return k, v
 
 
 def decode_workload(wl, rows=None, scale=0.0):

@@ -262,3 +262,44 @@ def test_explicit_scale_and_rejects_bad_input():
         run_oracle(q, kp, vp, bt, bad, 2, 2, 16)
     with pytest.raises(ValueError):
         run_oracle(q, kp, vp, bt, sl, 3, 2, 16)
+
+
+@pytest.mark.parametrize("seed,B,Hq,Hkv,D,L,bs", [
+    (20, 2, 4, 2, 16, 37, 16),
+    (21, 3, 2, 1, 8, 11, 4),
+])
+def test_append_then_attend_steps_equal_causal_attention(seed, B, Hq, Hkv, D, L, bs):
+    """Decoding token by token into an empty paged cache equals causal attention over the sequence.
+
+    Step t appends K_t, V_t with append_tokens (seq_len t + 1) and attends with
+    the oracle; torch's float64 scaled_dot_product_attention with a causal mask
+    over all L positions at once is the reference.  After the last step the
+    pools equal the dense sequences packed directly into the same blocks.
+    """
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(seed)
+    q = bf16(rng.standard_normal((B, L, Hq, D)))
+    dk = [bf16(rng.standard_normal((L, Hkv, D))) for _ in range(B)]
+    dv = [bf16(rng.standard_normal((L, Hkv, D))) for _ in range(B)]
+    kp_full, vp_full, bt, _ = paged(dk, dv, bs, rng)
+    kp = np.full_like(kp_full, 0x7FC0)       # NaN everywhere: only appended slots are ever read
+    vp = np.full_like(vp_full, 0x7FC0)
+    G = Hq // Hkv
+    for t in range(L):
+        lens = np.full(B, t + 1, dtype=np.int32)
+        k_new = np.stack([dk[b][t] for b in range(B)])
+        v_new = np.stack([dv[b][t] for b in range(B)])
+        kp2, vp2 = oracle.append_tokens(kp, vp, bt, lens, k_new, v_new, block_size=bs)
+        assert np.isnan(bf16_bits_to_f32(kp)).sum() - np.isnan(bf16_bits_to_f32(kp2)).sum() == B * Hkv * D
+        kp, vp = kp2, vp2
+        got = oracle.decode_all(q[:, t], kp, vp, bt, lens, Hq, Hkv, block_size=bs)
+        for b in range(B):
+            qt = torch.from_numpy(bf16_bits_to_f32(q[b]).astype(np.float64)).permute(1, 0, 2).unsqueeze(0)
+            kt = torch.from_numpy(bf16_bits_to_f32(dk[b]).astype(np.float64)).permute(1, 0, 2)
+            vt = torch.from_numpy(bf16_bits_to_f32(dv[b]).astype(np.float64)).permute(1, 0, 2)
+            kt = kt.repeat_interleave(G, dim=0).unsqueeze(0).contiguous()
+            vt = vt.repeat_interleave(G, dim=0).unsqueeze(0).contiguous()
+            ref = torch.nn.functional.scaled_dot_product_attention(qt.contiguous(), kt, vt, is_causal=True)
+            np.testing.assert_allclose(got[b], ref[0, :, t, :].numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(kp, kp_full)
+    np.testing.assert_array_equal(vp, vp_full)

@@ -16,7 +16,12 @@ import workloads as W
 K = pytest.importorskip("decode_attention_prefix_amd.kvattn")
 
 
-def check_coverage(wl_bt, seq_lens, Hq, Hkv, ex):
+def check_coverage(wl_bt, seq_lens, Hq, Hkv, ex, all_merged=False):
+    """Every token of every query read exactly once; destinations and merge map consistent.
+
+    all_merged: every query's rows go through the merge (new-token plans), even
+    with one partial or none.
+    """
     B = len(seq_lens)
     G = Hq // Hkv
     it, en, ids = ex["items"], ex["entries"], ex["block_ids"]
@@ -54,13 +59,18 @@ def check_coverage(wl_bt, seq_lens, Hq, Hkv, ex):
     mq = {int(b): i for i, b in enumerate(ex["merge_query"])}
     for b in range(B):
         d = per_query[b]
-        if len(d) == 1:
+        if len(d) == 1 and not all_merged:
             assert d[0] == -1 and b not in mq
         else:
             assert all(x >= 0 for x in d) and b in mq
             i = mq[b]
             listed = ex["merge_dest"][ex["merge_ptr"][i]:ex["merge_ptr"][i + 1]]
             assert sorted(listed.tolist()) == sorted(d)
+            rec = ex["merge_rec"][i]
+            assert rec[0] == b and rec[2] == len(d)
+            if not d:
+                continue
+            assert rec[1] == int(listed.min())
             # the merge locates a query's partials from its first slot and count:
             # consecutive [Hq]-slot blocks
             first = int(listed.min())
