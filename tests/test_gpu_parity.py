@@ -234,6 +234,22 @@ def test_parity_boundary_lengths(D, G, Hkv, variant):
         np.testing.assert_allclose(got[0, h], vf[blk, h // G, 0], rtol=0, atol=1e-6)
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(1, 1, 64), (3, 1, 64), (6, 2, 128), (16, 1, 128), (32, 32, 128),
+                                       (64, 2, 128), (64, 1, 64), (128, 8, 128)])
+@pytest.mark.parametrize("variant", [-1, 0, 1])
+def test_parity_head_shapes(Hq, Hkv, D, variant):
+    """Head counts off the configs' 32/8 and 4/4: one head, odd groups, MHA with 32 KV heads,
+    the widest GQA group (64 q heads per KV head) and 128 q heads, over a shared prefix
+    with ragged suffixes."""
+    G = Hq // Hkv
+    if variant == 0 and G > valu_max_rows(D):
+        pytest.skip("the VALU forward holds at most %d rows per KV head at head_dim %d" % (valu_max_rows(D), D))
+    lengths = [1, 17, 33, 40, 64, 90, 129]
+    wl = edge_workload(lengths, 32, Hq, Hkv, D, 60 + Hq + Hkv + D)
+    got, dec = gpu_decode(wl, force_variant=variant)
+    assert_close(got, oracle_out(wl), "heads %d/%d D%d v%d" % (Hq, Hkv, D, variant))
+
+
 @pytest.mark.parametrize("variant", [-1, 0, 1])
 @pytest.mark.parametrize("shared", [16, 32, 48])
 def test_parity_shared_prefix_ragged(variant, shared):

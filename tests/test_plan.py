@@ -361,6 +361,12 @@ def test_validation_errors():
     s = list(shp)
     s[4] = 32
     expect(K.KVATTN_EUNSUPPORTED, shape=s)
+    s = list(shp)
+    s[1], s[2] = 128, 1                       # 128 q heads on one KV head: wider than 64
+    expect(K.KVATTN_EUNSUPPORTED, shape=s)
+    s = list(shp)
+    s[1], s[2] = 32, 4                        # 8 rows per KV head: more than VALU holds at head_dim 128
+    expect(K.KVATTN_EUNSUPPORTED, shape=s, force_variant=0)
     expect(K.KVATTN_EINVAL, pack_mode=7)
     expect(K.KVATTN_EINVAL, split_tokens=-1)
     # unused block-table entries are never read, whatever they hold
