@@ -338,6 +338,20 @@ def main():
     mrg_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(n_ev)])
     call_ms = fwd_ms + mrg_ms
 
+    # a plain streaming read of the same pools (same bytes, same grid) for context beside the peak
+    grid = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+    for i in range(3):
+        K.kvattn_read_probe(pools[i % copies][0], pools[i % copies][1], sink, grid, stream)
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
+    for i in range(n_ev):
+        pev[i][0].record(stream)
+        K.kvattn_read_probe(pools[i % copies][0], pools[i % copies][1], sink, grid, stream)
+        pev[i][1].record(stream)
+    torch.cuda.synchronize()
+    probe_us = float(np.median([e[0].elapsed_time(e[1]) for e in pev])) * 1e3
+    attainable = pool_bytes / (probe_us * 1e-6) / 1e9
+
     append = append_timing(K, torch, W, wl, dec, pools, q, outs, min(args.steps, 100), args.warmup)
     log("bench: decode step with KV append %s" % json.dumps(append))
 
@@ -351,7 +365,11 @@ def main():
                 "kernel": "fwd_kernel (persistent; %d MFMA + %d VALU items)" % (st["num_items_mfma"],
                                                                                  st["num_items_valu"]),
                 "algorithmic_bytes_per_launch": int(uniq),
-                "avg_forward_us": round(fwd_avg * 1e3, 2), "avg_merge_us": round(float(mrg_ms.mean()) * 1e3, 2)}
+                "avg_forward_us": round(fwd_avg * 1e3, 2), "avg_merge_us": round(float(mrg_ms.mean()) * 1e3, 2),
+                "plain_read": {"GB/s": round(attainable, 1), "bytes": int(pool_bytes), "us": round(probe_us, 2),
+                               "grid": grid, "forward_over_plain_read": round(achieved / attainable, 4),
+                               "what": "kvattn_read_probe: one contiguous share per workgroup of the K and V "
+                                       "pools, median of HIP-event timed launches"}}
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",

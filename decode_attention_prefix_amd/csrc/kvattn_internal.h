@@ -157,6 +157,8 @@ struct Dims {
 int launch_forward(const DevPlan& p, const Dims& d, int valu_rows, int mfma_tiles, int n_tasks,
                    const uint16_t* q, const uint16_t* k, const uint16_t* v, float* out, void* stream);
 int launch_merge(const DevPlan& p, const Dims& d, int q_count, float* out, void* stream);
+int launch_read_probe(const void* a, size_t a_bytes, const void* b, size_t b_bytes, uint32_t* sink, int grid,
+                      void* stream);
 int launch_merge_append(const DevPlan& p, const Dims& d, int q_count, const NewTokens& nt, float* out, void* stream);
 
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }

@@ -1056,7 +1056,45 @@ int launch_fwd_t(const DevPlan& p, const Dims& d, int n_tasks, const uint16_t* q
     return int(hipGetLastError());
 }
 
+// Measurement helper, not part of the attention path: a plain streaming read
+// of two buffers (the K and V pools), split into one contiguous share per
+// workgroup, four 16-byte loads per lane in flight, XOR-folded into one word
+// per thread so the loads are not removed.  It gives the bandwidth the memory
+// system delivers for the pools' bytes at the same size and grid.
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict__ a, size_t na,
+                                                         const u32x4* __restrict__ b, size_t nb, uint32_t* sink) {
+    constexpr int DEPTH = 4;
+    const size_t n = na + nb;
+    const size_t per = (n + gridDim.x - 1) / gridDim.x;
+    const size_t s0 = per * blockIdx.x, s1 = min(n, s0 + per);
+    uint32_t x = 0;
+    for (size_t i = s0 + threadIdx.x; i < s1; i += size_t(256) * DEPTH) {
+        // addresses are selected, never the loads: all DEPTH loads stay in flight
+        u32x4 v[DEPTH];
+        bool ok[DEPTH];
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const size_t j = i + size_t(d) * 256;
+            ok[d] = j < s1;
+            const size_t jj = ok[d] ? j : i;          // i < s1: a valid element
+            const u32x4* src = jj < na ? a + jj : b + (jj - na);
+            v[d] = *src;
+        }
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d)
+            if (ok[d]) x ^= v[d].x ^ v[d].y ^ v[d].z ^ v[d].w;
+    }
+    sink[size_t(blockIdx.x) * 256 + threadIdx.x] = x;
+}
+
 }  // namespace
+
+int launch_read_probe(const void* a, size_t a_bytes, const void* b, size_t b_bytes, uint32_t* sink, int grid,
+                      void* stream) {
+    hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4*>(a), a_bytes / 16, static_cast<const u32x4*>(b), b_bytes / 16, sink);
+    return int(hipGetLastError());
+}
 
 int launch_forward(const DevPlan& p, const Dims& d, int valu_rows, int mfma_tiles, int n_tasks,
                    const uint16_t* q, const uint16_t* k, const uint16_t* v, float* out, void* stream) {

@@ -150,4 +150,20 @@ kvattn_status kvattn_decode_append(const void* q, const void* k_new, const void*
     return KVATTN_OK;
 }
 
+kvattn_status kvattn_read_probe(const void* a, size_t a_bytes, const void* b, size_t b_bytes, void* sink,
+                                size_t sink_bytes, int32_t grid, void* stream) {
+    using namespace kvattn;
+    clear_error();
+    if (!a || !b || !sink) return set_error(KVATTN_EINVAL, "a, b or sink is NULL");
+    if (!aligned16(a) || !aligned16(b) || !aligned16(sink) || (a_bytes & 15u) || (b_bytes & 15u))
+        return set_error(KVATTN_EINVAL, "buffers must be 16-byte aligned and multiples of 16 bytes");
+    if (grid < 1) return set_error(KVATTN_EINVAL, "grid must be >= 1");
+    if (sink_bytes < size_t(grid) * 256 * 4)
+        return set_error(KVATTN_EINVAL, "sink holds " + std::to_string(sink_bytes) + " bytes, the probe writes " +
+                                            std::to_string(size_t(grid) * 256 * 4));
+    const int rc = launch_read_probe(a, a_bytes, b, b_bytes, static_cast<uint32_t*>(sink), grid, stream);
+    if (rc != 0) return set_error(KVATTN_EHIP, std::string("probe launch failed: ") + hipGetErrorString(hipError_t(rc)));
+    return KVATTN_OK;
+}
+
 }  // extern "C"

@@ -93,6 +93,8 @@ def _load():
         getattr(lib, name).restype = ctypes.c_int
     lib.kvattn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kvattn_decode_append.restype = ctypes.c_int
+    lib.kvattn_read_probe.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp, ctypes.c_size_t, i32, vp]
+    lib.kvattn_read_probe.restype = ctypes.c_int
     lib.kvattn_merge.argtypes = [vp, vp, vp]
     lib.kvattn_merge.restype = ctypes.c_int
     lib.kvattn_plan_stats.argtypes = [vp, ctypes.POINTER(kvattn_stats)]
@@ -110,8 +112,9 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("kvattn_plan_options_default", "kvattn_plan", "kvattn_plan_device_bytes", "kvattn_plan_upload",
-            "kvattn_decode", "kvattn_forward", "kvattn_merge", "kvattn_plan_stats", "kvattn_plan_export",
-            "kvattn_plan_destroy", "kvattn_status_string", "kvattn_last_error")
+            "kvattn_decode", "kvattn_decode_append", "kvattn_forward", "kvattn_merge", "kvattn_plan_update",
+            "kvattn_expand_query_tokens", "kvattn_plan_stats", "kvattn_plan_export", "kvattn_plan_destroy",
+            "kvattn_read_probe", "kvattn_status_string", "kvattn_last_error")
 
 
 class KvattnError(RuntimeError):
@@ -239,6 +242,13 @@ def kvattn_decode(q, k_cache, v_cache, plan: Plan, out, stream=None):
 def kvattn_decode_append(q, k_new, v_new, k_cache, v_cache, plan: Plan, out, stream=None):
     _check(_lib.kvattn_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), plan.handle,
                                      _ptr(out), _stream(stream)), "kvattn_decode_append")
+
+
+def kvattn_read_probe(a, b, sink, grid, stream=None):
+    """Plain streaming read of tensors a and b (measurement helper; see kvattn.h)."""
+    _check(_lib.kvattn_read_probe(_ptr(a), a.numel() * a.element_size(), _ptr(b), b.numel() * b.element_size(),
+                                  _ptr(sink), sink.numel() * sink.element_size(), int(grid), _stream(stream)),
+           "kvattn_read_probe")
 
 
 def kvattn_forward(q, k_cache, v_cache, plan: Plan, out, stream=None):

@@ -337,6 +337,18 @@ kvattn_status kvattn_forward(const void* q, const void* k_cache, const void* v_c
  * a plan made with new_token (its merge needs the new token's inputs). */
 kvattn_status kvattn_merge(kvattn_plan_t plan, float* out, void* stream);
 
+/*
+ * Measurement helper, not part of the attention path.  One launch of `grid`
+ * workgroups that reads a_bytes of a then b_bytes of b (device buffers,
+ * 16-byte aligned, sizes multiples of 16), each workgroup one contiguous share,
+ * and writes one word per thread into sink (device, >= grid * 1024 bytes).  It
+ * times what the memory system delivers for a plain streaming read of the same
+ * bytes, e.g. the K and V pools a decode reads, beside the decode's own rate.
+ * Errors: EINVAL (NULL, misaligned, sink too small, grid < 1), EHIP.
+ */
+kvattn_status kvattn_read_probe(const void* a, size_t a_bytes, const void* b, size_t b_bytes, void* sink,
+                                size_t sink_bytes, int32_t grid, void* stream);
+
 /* Plan statistics (host only). */
 kvattn_status kvattn_plan_stats(kvattn_plan_t plan, kvattn_stats* stats);
 

@@ -350,3 +350,21 @@ def test_graph_replay_matches_eager():
         k.kvattn_decode(q, kc, vc, dec.plan, other)   # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(other, eager)
+
+
+def test_read_probe_reads_every_word():
+    """The measurement helper reads every 32-bit word of both buffers once: the XOR of its sink
+    equals the XOR of all words (sizes not multiples of the grid's shares)."""
+    k = K()
+    rng = np.random.default_rng(5)
+    a = rng.integers(0, 2 ** 31, size=(1000 * 4 + 4,), dtype=np.int64).astype(np.int32)
+    b = rng.integers(0, 2 ** 31, size=(777 * 4,), dtype=np.int64).astype(np.int32)
+    grid = 7
+    sink = torch.zeros(grid * 256, dtype=torch.int32, device="cuda")
+    k.kvattn_read_probe(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), sink, grid)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    want = np.bitwise_xor.reduce(np.concatenate([a, b]).view(np.uint32))
+    assert got == want
+    with pytest.raises(k.KvattnError):
+        k.kvattn_read_probe(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), sink[:10], grid)
