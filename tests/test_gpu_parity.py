@@ -368,3 +368,25 @@ def test_read_probe_reads_every_word():
     assert got == want
     with pytest.raises(k.KvattnError):
         k.kvattn_read_probe(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), sink[:10], grid)
+
+
+def test_two_plans_in_flight_on_two_streams():
+    """Two plans, each with its own workspace, decode at the same time on two non-default streams
+    (default priority); both match the oracle, twice in a row."""
+    k = K()
+    a, b = small(2), small(5)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    da = k.Decoder(a.shape_tuple(), a.block_tables, a.seq_lens, options=k.make_options(num_cus=1024))
+    db = k.Decoder(b.shape_tuple(), b.block_tables, b.seq_lens)
+    qa, ka, va = [torch.from_numpy(x.view(np.int16)).cuda() for x in (a.q, a.k_pool, a.v_pool)]
+    qb, kb, vb = [torch.from_numpy(x.view(np.int16)).cuda() for x in (b.q, b.k_pool, b.v_pool)]
+    torch.cuda.synchronize()
+    for rep in range(2):
+        oa = torch.full((a.num_queries, a.num_q_heads, a.head_dim), float("nan"), device="cuda")
+        ob = torch.full((b.num_queries, b.num_q_heads, b.head_dim), float("nan"), device="cuda")
+        torch.cuda.synchronize()
+        da.decode(qa, ka, va, oa, stream=s1.cuda_stream)
+        db.decode(qb, kb, vb, ob, stream=s2.cuda_stream)
+        torch.cuda.synchronize()
+        assert_close(oa.cpu().numpy().astype(np.float64), oracle_out(a), "stream 1 rep %d" % rep)
+        assert_close(ob.cpu().numpy().astype(np.float64), oracle_out(b), "stream 2 rep %d" % rep)

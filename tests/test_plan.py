@@ -361,6 +361,11 @@ def test_validation_errors():
     s = list(shp)
     s[4] = 32
     expect(K.KVATTN_EUNSUPPORTED, shape=s)
+    for field in range(7):                    # every shape field must be >= 1 (an empty batch included)
+        s = list(shp)
+        s[field] = 0
+        expect(K.KVATTN_EUNSUPPORTED if field == 4 else K.KVATTN_EINVAL,
+               shape=s)
     s = list(shp)
     s[1], s[2] = 128, 1                       # 128 q heads on one KV head: wider than 64
     expect(K.KVATTN_EUNSUPPORTED, shape=s)
@@ -388,3 +393,40 @@ def test_device_calls_report_state_errors_without_gpu():
         K.kvattn_plan_upload(p, 257, 1 << 30, stream=0)
     assert e.value.status == K.KVATTN_EWORKSPACE
     assert K.kvattn_plan_device_bytes(p) >= K.kvattn_plan_stats(p)["blob_bytes"]
+
+
+def test_planning_is_reentrant_across_threads():
+    """kvattn_plan from several threads at once (ctypes releases the GIL) gives the plans of a serial run."""
+    from concurrent.futures import ThreadPoolExecutor
+    wls = [W.small(c) for c in (1, 2, 3, 5)] * 3
+
+    def plan_desc(wl):
+        p = K.kvattn_plan(wl.shape_tuple(), wl.block_tables, wl.seq_lens)
+        ex = K.kvattn_plan_export(p)
+        return ex["desc"].copy(), ex["block_ids"].copy()
+
+    serial = [plan_desc(wl) for wl in wls]
+    with ThreadPoolExecutor(max_workers=6) as pool:
+        parallel = list(pool.map(plan_desc, wls))
+    for (d0, b0), (d1, b1) in zip(serial, parallel):
+        assert np.array_equal(d0, d1) and np.array_equal(b0, b1)
+    # a failing call on one thread leaves the other threads' error strings alone
+    bad = W.small(2)
+    sl = bad.seq_lens.copy()
+    sl[0] = 0
+
+    def fail():
+        try:
+            K.kvattn_plan(bad.shape_tuple(), bad.block_tables, sl)
+        except K.KvattnError:
+            return K.kvattn_last_error()
+        return ""
+
+    def ok():
+        K.kvattn_plan(bad.shape_tuple(), bad.block_tables, bad.seq_lens)
+        return K.kvattn_last_error()
+
+    with ThreadPoolExecutor(max_workers=2) as pool:
+        f1, f2 = pool.submit(fail), pool.submit(ok)
+        assert "seq_lens[0]" in f1.result()
+        assert f2.result() == ""
