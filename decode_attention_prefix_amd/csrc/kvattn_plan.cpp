@@ -1077,8 +1077,12 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
 // their descriptors change: no tree, pack, split or list work.  Returns 1 when
 // the descriptors were patched in place, 2 when their sizes changed and the
 // lists were re-serialized, 0 (plan unchanged) when the step does not fit, -1
-// (plan unchanged) when a new block id is out of range.  Lengths are checked
-// by the caller; old blocks are compared with the plan's, new ones range-checked.
+// (plan unchanged) when a new block id is out of range, -2 (plan unchanged, err
+// set) when a new-token plan's new token would land in a slot that is not its
+// query's alone.  Lengths are checked by the caller (for new-token plans they
+// are the cached parts); old blocks are compared with the plan's, new ones
+// range-checked.  New-token plans also move every merge record's new-token
+// slot, in the host copy and in the blob.
 int extend_plan(kvattn_plan_s& P, const int32_t* block_tables, const int32_t* seq_lens, kvattn_status& err) {
     const kvattn_shape& s = P.shape;
     const int B = s.num_queries, MB = s.max_blocks_per_seq;
