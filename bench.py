@@ -68,19 +68,21 @@ def traffic_from_counters(c):
 
     Each counter (KiB per dispatch) is scaled by what the same counter reads for a
     plain device copy of known size (fetch_scale, write_scale in the summary).
-    Returns (read + written bytes, read bytes), both None when no summary exists
-    for this workload or the kernel source changed since the counters were taken.
+    Returns (read + written bytes, read bytes, bytes the merge launch reads), all
+    None when no summary exists for this workload or the kernel source changed
+    since the counters were taken.
     """
     path = os.path.join(PROFILES, "counters_c%d.json" % c)
     if not os.path.exists(path):
-        return None, None
+        return None, None, None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_src_sha") != kernel_src_sha():
-        return None, None
+        return None, None, None
     fetch = rec["forward_fetch_kib"] * 1024.0 * rec["fetch_scale"]
     write = rec["forward_write_kib"] * 1024.0 * rec["write_scale"]
-    return fetch + write, fetch
+    merge_fetch = (rec.get("merge_fetch_kib") or 0.0) * 1024.0 * rec["fetch_scale"]
+    return fetch + write, fetch, merge_fetch
 
 
 def cpu_baseline(wl, budget_s=12.0):
@@ -108,7 +110,7 @@ def cpu_baseline(wl, budget_s=12.0):
         while True:
             oracle.decode_workload(wl, rows=rows)
             reps += 1
-            if time.perf_counter() - t0 >= budget_s or reps >= 1000:
+            if time.perf_counter() - t0 >= budget_s:
                 break
         dt = time.perf_counter() - t0
         full_s = dt / reps
@@ -125,8 +127,15 @@ def cpu_baseline(wl, budget_s=12.0):
         sample = ("%d of %d (query, head) rows chosen at random (%.1f%% of the token-row work), %.2f s wall on %d "
                   "OpenMP threads; the full batch extrapolates to %.1f s" % (n, B * Hq, 100 * frac, dt, threads,
                                                                              full_s))
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((line.split(":", 1)[1].strip() for line in f if line.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": round(wl.unique_kv_bytes / full_s / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "sample": sample, "full_batch_seconds": round(full_s, 4)}
+            "kind": "oracle", "sample": sample, "full_batch_seconds": float("%.4g" % full_s), "cpu_model": cpu,
+            "host_cpus": os.cpu_count()}
 
 
 def copy_calibration(nbytes):
@@ -375,7 +384,7 @@ def main():
     value = uniq / (ms_per_step * 1e-3) / 1e9
     fwd_avg = float(fwd_ms.mean())
     achieved = uniq / (fwd_avg * 1e-3) / 1e9
-    traffic, fetched = traffic_from_counters(args.config)
+    traffic, fetched, merge_fetched = traffic_from_counters(args.config)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None if traffic is None else int(traffic),
                 "kernel": "fwd_kernel (persistent; %d MFMA + %d VALU items)" % (st["num_items_mfma"],
@@ -393,6 +402,7 @@ def main():
         "us_per_call_gpu_events_median": round(float(np.median(call_ms)) * 1e3, 2),
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "redundancy_fetch_over_unique": None if fetched is None else round(fetched / uniq, 4),
+        "redundancy_fetch_over_unique_with_merge": None if fetched is None else round((fetched + merge_fetched) / uniq, 4),
         "plan_ms": round(st["plan_seconds"] * 1e3, 3), "plan_upload_ms": round(plan_upload_ms, 3),
         "plan_update_ms": round(upd_ms, 3), "plan_update_path": upd_path,
         "decode_with_kv_append": append,
