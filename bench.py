@@ -206,15 +206,24 @@ def append_timing(K, torch, W, wl, dec, pools, q, outs, steps, warmup):
     agree = float((a - outs[0]).abs().max())
     assert agree <= 2e-3, "fused and unfused append steps disagree: %.3e" % agree
     res = {"applicable": True, "max_abs_diff_fused_vs_unfused": agree}
+    best = graph_best_us(torch, {"fused": fused_call, "unfused": unfused_call}, copies, steps, warmup)
+    for name, us in best.items():
+        res[name + "_us_per_call"] = us
+    return res
+
+
+def graph_best_us(torch, fns, copies, steps, warmup):
+    """HIP-graph replays of each step function (one graph per KV copy), timed in two
+    alternating rounds; the best round of each.  Launch-bound sizes are sensitive to
+    what ran just before, hence the alternation."""
     graphs = {}
-    for name, fn in (("fused", fused_call), ("unfused", unfused_call)):
+    for name, fn in fns.items():
         graphs[name] = []
         for i in range(copies):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 fn(i)
             graphs[name].append(g)
-    # two alternating rounds, best of each: launch-bound sizes are sensitive to what ran just before
     best = {}
     for _ in range(2):
         for name, gs in graphs.items():
@@ -227,9 +236,34 @@ def append_timing(K, torch, W, wl, dec, pools, q, outs, steps, warmup):
             torch.cuda.synchronize()
             us = (time.perf_counter() - t0) / steps * 1e6
             best[name] = min(best.get(name, us), us)
-    for name, us in best.items():
-        res[name + "_us_per_call"] = round(us, 2)
-    return res
+    return {name: round(us, 2) for name, us in best.items()}
+
+
+def multi_stream_timing(K, torch, wl, dec, pools, q, outs, steps, warmup):
+    """The PAT review's multi-stream forward (MFMA launches on a side stream,
+    kvattn_decode_streams over a multi_stream plan) against the single-launch
+    plan of the main measurement, both as graph replays."""
+    ms = K.Decoder(wl.shape_tuple(), wl.block_tables, wl.seq_lens, options=K.make_options(multi_stream=1))
+    side = torch.cuda.Stream()
+    copies = len(pools)
+
+    def single(i):
+        K.kvattn_decode(q, pools[i % copies][0], pools[i % copies][1], dec.plan, outs[i % copies])
+
+    def multi(i):
+        K.kvattn_decode_streams(q, pools[i % copies][0], pools[i % copies][1], ms.plan, outs[i % copies], side)
+
+    multi(0)
+    torch.cuda.synchronize()
+    a = outs[0].clone()
+    single(0)
+    torch.cuda.synchronize()
+    diff = float((a - outs[0]).abs().max())
+    assert diff <= 2e-3, "multi-stream and single-launch decodes disagree: %.3e" % diff
+    best = graph_best_us(torch, {"single_launch": single, "multi_stream": multi}, copies, steps, warmup)
+    st = ms.stats()
+    return {"us_per_call_single_launch": best["single_launch"], "us_per_call_multi_stream": best["multi_stream"],
+            "multi_stream_launches": st["num_launches"], "max_abs_diff": diff}
 
 
 def extras(K, torch, W, wl, dec, pools, q, outs, stream, n_ev, pool_bytes, args):
@@ -251,10 +285,12 @@ def extras(K, torch, W, wl, dec, pools, q, outs, stream, n_ev, pool_bytes, args)
 
     append = append_timing(K, torch, W, wl, dec, pools, q, outs, min(args.steps, 100), args.warmup)
     log("bench: decode step with KV append %s" % json.dumps(append))
+    multi = multi_stream_timing(K, torch, wl, dec, pools, q, outs, min(args.steps, 100), args.warmup)
+    log("bench: multi-stream forward %s" % json.dumps(multi))
     plain = {"GB/s": round(attainable, 1), "bytes": int(pool_bytes), "us": round(probe_us, 2), "grid": grid,
                      "what": "kvattn_read_probe: one contiguous share per workgroup of the K and V pools, "
                              "median of HIP-event timed launches"}
-    return plain, append
+    return plain, append, multi
 
 
 def main():
@@ -375,10 +411,9 @@ def main():
     call_ms = fwd_ms + mrg_ms
 
     # a plain streaming read of the same pools (same bytes, same grid) for context beside the peak
-    plain_read = None
-    append = None
+    plain_read = append = multi = None
     if not args.no_extras:
-        plain_read, append = extras(K, torch, W, wl, dec, pools, q, outs, stream, n_ev, pool_bytes, args)
+        plain_read, append, multi = extras(K, torch, W, wl, dec, pools, q, outs, stream, n_ev, pool_bytes, args)
 
     uniq = wl.unique_kv_bytes
     value = uniq / (ms_per_step * 1e-3) / 1e9
@@ -406,6 +441,7 @@ def main():
         "plan_ms": round(st["plan_seconds"] * 1e3, 3), "plan_upload_ms": round(plan_upload_ms, 3),
         "plan_update_ms": round(upd_ms, 3), "plan_update_path": upd_path,
         "decode_with_kv_append": append,
+        "multi_stream_forward": multi,
         "plan": {k: st[k] for k in ("num_items", "num_items_valu", "num_items_mfma", "num_packed_nodes",
                                     "num_folded_leaves", "num_merge_rows", "num_launches", "split_tokens",
                                     "planned_kv_bytes", "partial_bytes")},

@@ -117,6 +117,7 @@ struct Launch {
     int index;         // list set
     int n_tasks;
     int task_base;     // first task of the launch in the host schedule
+    int side;          // multi-stream plans: 1 for the MFMA launches (side stream); also the claim counter
 };
 
 // Merge record of one query whose rows have several partials: partial k of

@@ -383,7 +383,7 @@ void serialize_blob(kvattn_plan_s& P) {
     h.off_desc = off;         off = align256(off + P.desc.size() * 4);
     h.off_list_ptr = off;     off = align256(off + P.desc_list_ptr.size() * 4);
     h.off_merge_rec = off;    off = align256(off + P.merge_rec.size() * 4);
-    h.off_claim = off;        off = align256(off + 4);
+    h.off_claim = off;        off = align256(off + 2 * 4);   // one counter per stream
     h.blob_bytes = off;
     h.off_part_ml = off;      off = align256(off + uint64_t(P.n_slots) * 8);
     h.off_part_acc = off;     off = align256(off + uint64_t(P.n_slots) * uint64_t(P.shape.head_dim) * 4);
@@ -729,6 +729,8 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         // the stripes' common fill level for the VALU work above their MFMA loads
         auto stripe_base = [&](const std::vector<double>& load) {
             std::vector<double> base(size_t(n_stripes), 0.0);
+            // multi-stream plans run the MFMA lists in a launch of their own, beside the VALU one
+            if (o.multi_stream) return base;
             for (int s = 0; s < n_stripes; ++s)
                 for (int q = 0; q < quads; ++q) base[size_t(s)] = std::max(base[size_t(s)], load[size_t(stripe_list(s, q))]);
             return base;
@@ -961,7 +963,10 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     // continuous per-wave streams (in stream order), whose descriptors must fit
     // the LDS window.
     P.tasks.clear();
-    P.list_ptr.assign(size_t(n_launch) * (n_lists + 1), 0);
+    // Multi-stream plans split every launch into an MFMA-only launch (side
+    // stream) and a VALU-only launch, each with its own list set.
+    const int sets_per_launch = o.multi_stream ? 2 : 1;
+    P.list_ptr.assign(size_t(n_launch) * sets_per_launch * (n_lists + 1), 0);
     P.forward_launches.clear();
     P.n_lists = n_lists;
     for (int L = 0; L < n_launch; ++L) {
@@ -994,21 +999,33 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
                 }
             }
         }
-        const int base = int(P.tasks.size());
-        for (int w = 0; w < n_lists; ++w) {
-            P.list_ptr[size_t(L) * (n_lists + 1) + w] = int32_t(P.tasks.size()) - base;
-            for (const Task& t : mlist[size_t(w)]) P.tasks.push_back(t);
-            for (const Task& t : vlist[size_t(w)]) P.tasks.push_back(t);
+        for (int part = 0; part < sets_per_launch; ++part) {
+            // part 0 of a multi-stream plan holds the MFMA tasks, part 1 the VALU tasks
+            const bool take_m = !o.multi_stream || part == 0, take_v = !o.multi_stream || part == 1;
+            size_t n_part = 0;
+            for (int w = 0; w < n_lists; ++w)
+                n_part += (take_m ? mlist[size_t(w)].size() : 0) + (take_v ? vlist[size_t(w)].size() : 0);
+            if (o.multi_stream && n_part == 0) continue;   // an empty part is not launched
+            const int set = int(P.forward_launches.size());   // list sets stay contiguous
+            const int base = int(P.tasks.size());
+            for (int w = 0; w < n_lists; ++w) {
+                P.list_ptr[size_t(set) * (n_lists + 1) + w] = int32_t(P.tasks.size()) - base;
+                if (take_m)
+                    for (const Task& t : mlist[size_t(w)]) P.tasks.push_back(t);
+                if (take_v)
+                    for (const Task& t : vlist[size_t(w)]) P.tasks.push_back(t);
+            }
+            P.list_ptr[size_t(set) * (n_lists + 1) + n_lists] = int32_t(P.tasks.size()) - base;
+            Launch Lr;
+            // a kind without tasks in this launch takes the smallest instantiation
+            Lr.valu_rows = launch_valu_rows;
+            Lr.mfma_tiles = L < int(mt.size()) ? mt[size_t(L)] : 1;
+            Lr.index = set;
+            Lr.n_tasks = int(P.tasks.size()) - base;
+            Lr.task_base = base;
+            Lr.side = o.multi_stream && part == 0 ? 1 : 0;
+            P.forward_launches.push_back(Lr);
         }
-        P.list_ptr[size_t(L) * (n_lists + 1) + n_lists] = int32_t(P.tasks.size()) - base;
-        Launch Lr;
-        // a kind without tasks in this launch takes the smallest instantiation
-        Lr.valu_rows = launch_valu_rows;
-        Lr.mfma_tiles = L < int(mt.size()) ? mt[size_t(L)] : 1;
-        Lr.index = L;
-        Lr.n_tasks = int(P.tasks.size()) - base;
-        Lr.task_base = base;
-        P.forward_launches.push_back(Lr);
     }
     if (!serialize_lists(P)) return set_error(KVATTN_EINVAL, "internal: VALU task descriptors exceed the LDS window");
 
@@ -1294,6 +1311,7 @@ void kvattn_plan_options_default(kvattn_plan_options* o) {
     o->split_tokens = 0;
     o->num_cus = 0;
     o->new_token = 0;
+    o->multi_stream = 0;
 }
 
 kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables, const int32_t* seq_lens,
@@ -1317,7 +1335,7 @@ kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables
     if (opts) o = *opts;
     if (o.pack_mode < 0 || o.pack_mode > 2 || o.scheme < 0 || o.scheme > 2 || o.force_variant < -1 ||
         o.force_variant > 1 || o.split_tokens < 0 || o.num_cus < 0 || !(o.scale >= 0.f) || std::isinf(o.scale) ||
-        o.new_token < 0 || o.new_token > 1)
+        o.new_token < 0 || o.new_token > 1 || o.multi_stream < 0 || o.multi_stream > 1)
         return set_error(KVATTN_EINVAL, "bad option value");
     kvattn_plan_s* P = new (std::nothrow) kvattn_plan_s();
     if (!P) return set_error(KVATTN_ENOMEM, "plan allocation failed");
@@ -1380,7 +1398,12 @@ kvattn_status kvattn_plan_update(kvattn_plan_t plan, const int32_t* block_tables
             kvattn_plan_t fresh = nullptr;
             const kvattn_status st = kvattn_plan(&s, block_tables, seq_lens, nullptr, &plan->opts, &fresh);
             if (st != KVATTN_OK) return st;
+            // the plan keeps its stream events (owned by the runtime) across the rebuild
+            void* fork_event = plan->fork_event;
+            void* join_event = plan->join_event;
             *plan = std::move(*fresh);
+            plan->fork_event = fork_event;
+            plan->join_event = join_event;
             delete fresh;
             path = 3;
         }
@@ -1466,7 +1489,6 @@ kvattn_status kvattn_plan_export(kvattn_plan_t plan, kvattn_export* out) {
     return KVATTN_OK;
 }
 
-void kvattn_plan_destroy(kvattn_plan_t plan) { delete plan; }
 
 const char* kvattn_status_string(kvattn_status s) {
     switch (s) {

@@ -32,6 +32,8 @@ struct kvattn_plan_s {
     std::vector<int32_t> entry_item;        // [entries] item of each entry
     std::vector<int32_t> tail_entry;        // [B] entry holding each query's last token
     std::vector<int32_t> reads;             // new-token plans: [num_physical_blocks] most tokens a cached part reads
+    void* fork_event = nullptr;             // multi-stream decode: hipEvent_t pair, created on first use
+    void* join_event = nullptr;
     void* dev_ws = nullptr;                 // bound device workspace (caller-owned)
     size_t dev_bytes = 0;
 };

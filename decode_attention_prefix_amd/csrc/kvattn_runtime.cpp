@@ -21,6 +21,7 @@ DevPlan resolve(const kvattn_plan_s& P, int launch) {
     if (launch >= 0) d.list_ptr += size_t(launch) * size_t(P.n_lists) * 3;
     d.merge_rec = reinterpret_cast<const MergeRec*>(base + h.off_merge_rec);
     d.claim = reinterpret_cast<int32_t*>(base + h.off_claim);
+    if (launch >= 0) d.claim += P.forward_launches[size_t(launch)].side;   // concurrent launches count apart
     d.part_ml = reinterpret_cast<float*>(base + h.off_part_ml);
     d.part_acc = reinterpret_cast<float*>(base + h.off_part_acc);
     return d;
@@ -45,7 +46,7 @@ kvattn_status check_bound(kvattn_plan_t plan) {
 }
 
 kvattn_status run_forward(const void* q, const void* k, const void* v, kvattn_plan_t plan, float* out,
-                          void* stream) {
+                          void* stream, void* side_stream = nullptr) {
     if (!q || !k || !v || !out) return set_error(KVATTN_EINVAL, "q, k_cache, v_cache or out is NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return set_error(KVATTN_EINVAL, "q, k_cache, v_cache and out must be 16-byte aligned");
@@ -54,8 +55,9 @@ kvattn_status run_forward(const void* q, const void* k, const void* v, kvattn_pl
     // one) follow each other on `stream`.
     for (const Launch& L : plan->forward_launches) {
         const DevPlan dp = resolve(*plan, L.index);
+        void* s = L.side && side_stream ? side_stream : stream;
         const int rc = launch_forward(dp, d, L.valu_rows, L.mfma_tiles, L.n_tasks, static_cast<const uint16_t*>(q),
-                                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), out, stream);
+                                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), out, s);
         if (rc != 0)
             return set_error(KVATTN_EHIP, std::string("forward launch failed: ") + hipGetErrorString(hipError_t(rc)));
     }
@@ -164,6 +166,47 @@ kvattn_status kvattn_read_probe(const void* a, size_t a_bytes, const void* b, si
     const int rc = launch_read_probe(a, a_bytes, b, b_bytes, static_cast<uint32_t*>(sink), grid, stream);
     if (rc != 0) return set_error(KVATTN_EHIP, std::string("probe launch failed: ") + hipGetErrorString(hipError_t(rc)));
     return KVATTN_OK;
+}
+
+kvattn_status kvattn_decode_streams(const void* q, const void* k_cache, const void* v_cache, kvattn_plan_t plan,
+                                    float* out, void* stream, void* side_stream) {
+    using namespace kvattn;
+    clear_error();
+    kvattn_status s = check_bound(plan);
+    if (s != KVATTN_OK) return s;
+    if (!plan->opts.multi_stream)
+        return set_error(KVATTN_EINVAL, "the plan was made without multi_stream: use kvattn_decode");
+    if (plan->opts.new_token)
+        return set_error(KVATTN_EINVAL, "the plan takes each query's newest token from the call: use kvattn_decode_append");
+    if (side_stream == stream) return set_error(KVATTN_EINVAL, "side_stream must differ from stream");
+    for (void** ev : {&plan->fork_event, &plan->join_event}) {
+        if (*ev) continue;
+        hipEvent_t e = nullptr;
+        const hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+        if (err != hipSuccess) return set_error(KVATTN_EHIP, std::string("event creation failed: ") + hipGetErrorString(err));
+        *ev = e;
+    }
+    hipStream_t main_s = static_cast<hipStream_t>(stream), side_s = static_cast<hipStream_t>(side_stream);
+    hipEvent_t fork = static_cast<hipEvent_t>(plan->fork_event), join = static_cast<hipEvent_t>(plan->join_event);
+    // the side stream starts after the work already on the main stream (the caller's inputs)
+    hipError_t e = hipEventRecord(fork, main_s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side_s, fork, 0);
+    if (e != hipSuccess) return set_error(KVATTN_EHIP, std::string("stream fork failed: ") + hipGetErrorString(e));
+    s = run_forward(q, k_cache, v_cache, plan, out, stream, side_stream);
+    // join before any error return, so the side stream never runs past the call
+    e = hipEventRecord(join, side_s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(main_s, join, 0);
+    if (s != KVATTN_OK) return s;
+    if (e != hipSuccess) return set_error(KVATTN_EHIP, std::string("stream join failed: ") + hipGetErrorString(e));
+    return run_merge(plan, out, stream);
+}
+
+void kvattn_plan_destroy(kvattn_plan_t plan) {
+    if (!plan) return;
+    // events exist only if kvattn_decode_streams ran, i.e. on a host with the HIP runtime
+    if (plan->fork_event) (void)hipEventDestroy(static_cast<hipEvent_t>(plan->fork_event));
+    if (plan->join_event) (void)hipEventDestroy(static_cast<hipEvent_t>(plan->join_event));
+    delete plan;
 }
 
 }  // extern "C"

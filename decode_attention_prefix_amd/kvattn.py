@@ -38,7 +38,7 @@ class kvattn_prefix_tree(ctypes.Structure):
 
 class kvattn_plan_options(ctypes.Structure):
     _fields_ = [("scale", f32), ("pack_mode", i32), ("scheme", i32), ("force_variant", i32), ("split_tokens", i32),
-                ("num_cus", i32), ("new_token", i32)]
+                ("num_cus", i32), ("new_token", i32), ("multi_stream", i32)]
 
 
 class kvattn_stats(ctypes.Structure):
@@ -91,6 +91,8 @@ def _load():
     for name in ("kvattn_decode", "kvattn_forward"):
         getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, vp]
         getattr(lib, name).restype = ctypes.c_int
+    lib.kvattn_decode_streams.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    lib.kvattn_decode_streams.restype = ctypes.c_int
     lib.kvattn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kvattn_decode_append.restype = ctypes.c_int
     lib.kvattn_read_probe.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp, ctypes.c_size_t, i32, vp]
@@ -112,7 +114,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("kvattn_plan_options_default", "kvattn_plan", "kvattn_plan_device_bytes", "kvattn_plan_upload",
-            "kvattn_decode", "kvattn_decode_append", "kvattn_forward", "kvattn_merge", "kvattn_plan_update",
+            "kvattn_decode", "kvattn_decode_append", "kvattn_decode_streams", "kvattn_forward", "kvattn_merge", "kvattn_plan_update",
             "kvattn_expand_query_tokens", "kvattn_plan_stats", "kvattn_plan_export", "kvattn_plan_destroy",
             "kvattn_read_probe", "kvattn_status_string", "kvattn_last_error")
 
@@ -239,6 +241,12 @@ def kvattn_decode(q, k_cache, v_cache, plan: Plan, out, stream=None):
            "kvattn_decode")
 
 
+def kvattn_decode_streams(q, k_cache, v_cache, plan: Plan, out, side_stream, stream=None):
+    """Multi-stream plans: MFMA launches on side_stream beside the VALU ones on stream."""
+    _check(_lib.kvattn_decode_streams(_ptr(q), _ptr(k_cache), _ptr(v_cache), plan.handle, _ptr(out), _stream(stream),
+                                      _stream(side_stream)), "kvattn_decode_streams")
+
+
 def kvattn_decode_append(q, k_new, v_new, k_cache, v_cache, plan: Plan, out, stream=None):
     _check(_lib.kvattn_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), plan.handle,
                                      _ptr(out), _stream(stream)), "kvattn_decode_append")
@@ -333,6 +341,11 @@ class Decoder:
 
     def decode(self, q, k_cache, v_cache, out, stream=None):
         kvattn_decode(q, k_cache, v_cache, self.plan, out, stream)
+        return out
+
+    def decode_streams(self, q, k_cache, v_cache, out, side_stream, stream=None):
+        """Plans made with multi_stream=1: MFMA launches on side_stream, VALU launches on stream."""
+        kvattn_decode_streams(q, k_cache, v_cache, self.plan, out, side_stream, stream)
         return out
 
     def decode_append(self, q, k_new, v_new, k_cache, v_cache, out, stream=None):

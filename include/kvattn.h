@@ -126,6 +126,13 @@ enum { KVATTN_VARIANT_AUTO = -1, KVATTN_VARIANT_VALU = 0, KVATTN_VARIANT_MFMA = 
  *                  and V, then attends to all of them).  The new token's slot
  *                  must belong to its query alone: no other query reads it
  *                  (copy-on-write paging), else kvattn_plan returns EINVAL.
+ *   multi_stream   0: MFMA and VALU tasks share each forward launch.  1: each
+ *                  launch is split into an MFMA-only launch and a VALU-only
+ *                  launch with lists of their own (the PAT review's multi-stream
+ *                  forward: kernel variants on separate streams, implementation
+ *                  details); kvattn_decode_streams runs the MFMA launches on a
+ *                  side stream beside the VALU ones.  kvattn_decode runs all
+ *                  launches in turn on one stream.
  */
 typedef struct {
     float scale;
@@ -135,6 +142,7 @@ typedef struct {
     int32_t split_tokens;
     int32_t num_cus;
     int32_t new_token;
+    int32_t multi_stream;
 } kvattn_plan_options;
 
 /* Statistics of a plan (bytes are per decode call, all KV heads). */
@@ -327,6 +335,22 @@ kvattn_status kvattn_decode(const void* q, const void* k_cache, const void* v_ca
  */
 kvattn_status kvattn_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
                                    void* v_cache, kvattn_plan_t plan, float* out, void* stream);
+
+/*
+ * kvattn_decode with the PAT review's multi-stream forward (implementation
+ * details: variants launched on separate streams so their kernels overlap).
+ * For plans made with options.multi_stream = 1: the MFMA-only launches go on
+ * side_stream, the VALU-only launches on stream; side_stream first waits for
+ * the work already on stream, and stream waits for side_stream before the
+ * merge launch, so the call is ordered on `stream` like kvattn_decode.  The
+ * plan owns two HIP events for the fork and join (created on first use,
+ * destroyed with the plan): calls with one plan must not overlap.  Works under
+ * stream capture (the side stream joins the capture).
+ * Errors: EINVAL (NULL or misaligned pointer, plan made without multi_stream,
+ * side_stream equal to stream), ESTATE (no workspace bound), EHIP.
+ */
+kvattn_status kvattn_decode_streams(const void* q, const void* k_cache, const void* v_cache, kvattn_plan_t plan,
+                                    float* out, void* stream, void* side_stream);
 
 /* The forward stage of kvattn_decode alone (PAT review, forward stage). */
 kvattn_status kvattn_forward(const void* q, const void* k_cache, const void* v_cache, kvattn_plan_t plan,

@@ -19,7 +19,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("kvattn_plan", "kvattn_decode", "kvattn_plan_upload", "kvattn_plan_device_bytes",
                      "kvattn_forward", "kvattn_merge", "kvattn_plan_stats", "kvattn_plan_export",
-                     "kvattn_decode_append", "kvattn_plan_update", "kvattn_expand_query_tokens",
+                     "kvattn_decode_append", "kvattn_decode_streams", "kvattn_plan_update", "kvattn_expand_query_tokens",
                      "kvattn_plan_destroy", "kvattn_status_string", "kvattn_last_error"):
         assert required in names
 

@@ -390,3 +390,56 @@ def test_two_plans_in_flight_on_two_streams():
         torch.cuda.synchronize()
         assert_close(oa.cpu().numpy().astype(np.float64), oracle_out(a), "stream 1 rep %d" % rep)
         assert_close(ob.cpu().numpy().astype(np.float64), oracle_out(b), "stream 2 rep %d" % rep)
+
+
+@pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
+def test_parity_multi_stream_forward(c):
+    """Multi-stream plans: MFMA launches on a side stream beside the VALU launches (kvattn_decode_streams),
+    and the same plan through kvattn_decode (launches in turn), against the oracle."""
+    k = K()
+    wl = small(c)
+    print("case multi-stream %s" % wl.name, flush=True)
+    dec = k.Decoder(wl.shape_tuple(), wl.block_tables, wl.seq_lens, options=k.make_options(multi_stream=1))
+    q, kc, vc = device_inputs(wl)
+    main, side = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        out = torch.full((wl.num_queries, wl.num_q_heads, wl.head_dim), float("nan"), device="cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(main):
+            dec.decode_streams(q, kc, vc, out, side_stream=side)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy().astype(np.float64), oracle_out(wl), "multi-stream %s rep %d" % (wl.name, rep))
+    out = torch.full((wl.num_queries, wl.num_q_heads, wl.head_dim), float("nan"), device="cuda")
+    dec.decode(q, kc, vc, out)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy().astype(np.float64), oracle_out(wl), "multi-stream plan, one stream")
+    with pytest.raises(k.KvattnError):
+        dec.decode_streams(q, kc, vc, out, side_stream=torch.cuda.current_stream())
+    plain = k.Decoder(wl.shape_tuple(), wl.block_tables, wl.seq_lens)
+    with pytest.raises(k.KvattnError):
+        plain.decode_streams(q, kc, vc, out, side_stream=side)
+    torch.cuda.synchronize()
+
+
+def test_multi_stream_graph_replay_matches_eager():
+    """The fork and join of kvattn_decode_streams under stream capture: replays match the eager result."""
+    k = K()
+    wl = small(3)
+    dec = k.Decoder(wl.shape_tuple(), wl.block_tables, wl.seq_lens, options=k.make_options(multi_stream=1))
+    q, kc, vc = device_inputs(wl)
+    shape = (wl.num_queries, wl.num_q_heads, wl.head_dim)
+    side = torch.cuda.Stream()
+    eager = torch.zeros(shape, dtype=torch.float32, device="cuda")
+    dec.decode_streams(q, kc, vc, eager, side_stream=side)
+    torch.cuda.synchronize()
+    out = torch.zeros(shape, dtype=torch.float32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        k.kvattn_decode_streams(q, kc, vc, dec.plan, out, side)
+    for rep in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), "replay %d" % rep
+    assert_close(eager.cpu().numpy().astype(np.float64), oracle_out(wl), "multi-stream eager")

@@ -430,3 +430,27 @@ def test_planning_is_reentrant_across_threads():
         f1, f2 = pool.submit(fail), pool.submit(ok)
         assert "seq_lens[0]" in f1.result()
         assert f2.result() == ""
+
+
+@pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
+def test_multi_stream_plans_split_launches_by_kind(c):
+    """multi_stream: every forward launch holds one kernel family; coverage and the byte model are unchanged."""
+    wl = W.small(c)
+    single = plan_of(wl)
+    multi = plan_of(wl, multi_stream=1)
+    ex = K.kvattn_plan_export(multi)
+    check_coverage(wl.block_tables, wl.seq_lens, wl.num_q_heads, wl.num_kv_heads, ex)
+    kinds = set(int(k) for k in ex["items"]["kind"])
+    lp = ex["list_ptr"]
+    launch_kinds = []
+    for L in range(lp.shape[0]):
+        m0, v0, e0 = lp[L, :, 0], lp[L, :, 1], lp[L, :, 2]
+        has_m, has_v = bool((v0 > m0).any()), bool((e0 > v0).any())
+        assert has_m != has_v, "launch %d mixes MFMA and VALU lists" % L
+        launch_kinds.append(K.KVATTN_VARIANT_MFMA if has_m else K.KVATTN_VARIANT_VALU)
+    assert set(launch_kinds) == kinds
+    s1, s2 = K.kvattn_plan_stats(single), K.kvattn_plan_stats(multi)
+    assert s2["planned_kv_bytes"] >= s2["unique_kv_bytes"]
+    assert s2["num_launches"] == lp.shape[0] + (1 if len(ex["merge_query"]) else 0)
+    if len(kinds) == 2:
+        assert s2["num_launches"] > s1["num_launches"]
