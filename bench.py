@@ -324,7 +324,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     t_gen = time.perf_counter()
-    wl = W.CONFIGS[args.config]().materialize()
+    wl = W.WORKLOADS[args.config]().materialize()
     log("bench: %s generated in %.1f s; unique KV %.1f MB" % (wl.name, time.perf_counter() - t_gen,
                                                               wl.unique_kv_bytes / 1e6))
     opts = K.make_options(pack_mode=args.pack_mode, split_tokens=args.split_tokens)

@@ -112,7 +112,7 @@ def test_append_every_query_alone():
 
 def test_append_full_size_llama3_8b_layer_sampled():
     """The Llama-3-8B layer workload (64 queries, shared prefix, private tails) at full size."""
-    wl = W.CONFIGS[2]().materialize()
+    wl = W.WORKLOADS[2]().materialize()
     rows = sampled_rows(wl, 192, 2)
     got, ref, _ = run_append(wl, 72, rows=rows)
     assert_close(got, ref, "append full config 2")

@@ -316,7 +316,7 @@ def sampled_rows(wl, n, seed):
 @pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
 def test_parity_full_size_sampled(c):
     """Full-size configs in the launch configuration the bench times (default plan)."""
-    wl = W.CONFIGS[c]().materialize()
+    wl = W.WORKLOADS[c]().materialize()
     got, dec = gpu_decode(wl)
     assert np.all(np.isfinite(got))
     rows = sampled_rows(wl, 96 if c >= 4 else 192, c)

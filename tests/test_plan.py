@@ -165,7 +165,7 @@ def plan_of(wl, **opts):
 @pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("mode", [K.KVATTN_PACK_AUTO, K.KVATTN_PACK_QUERY, K.KVATTN_PACK_FULL])
 def test_coverage_full_size_configs(c, mode):
-    wl = W.CONFIGS[c]()
+    wl = W.WORKLOADS[c]()
     p = plan_of(wl, pack_mode=mode)
     check_coverage(wl.block_tables, wl.seq_lens, wl.num_q_heads, wl.num_kv_heads, K.kvattn_plan_export(p))
     s = K.kvattn_plan_stats(p)

@@ -40,7 +40,7 @@ def test_kv_cache_size_formula_matches_page_example():
 
 @pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
 def test_config_structure(c):
-    wl = W.CONFIGS[c]()
+    wl = W.WORKLOADS[c]()
     B = wl.num_queries
     assert wl.block_tables.shape[0] == B
     nb = (wl.seq_lens + 15) // 16

@@ -285,7 +285,7 @@ def config5() -> Workload:
     return _no_sharing("c5_no_sharing", 512, 32, 8, 128, 16, 32768, 5)
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+WORKLOADS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
 # Reduced shapes of the same five structures, for element-by-element parity
