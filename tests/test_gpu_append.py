@@ -6,8 +6,6 @@ match the output within 2e-3 and leave both caches bit-identical to the
 oracle's.  Before the call the new tokens' slots hold NaN, so a kernel that
 reads a slot before writing it, or fails to write it, fails the check.
 """
-import dataclasses
-
 import numpy as np
 import pytest
 
