@@ -42,3 +42,13 @@ def test_header_compiles_as_c():
         f.write(src)
     subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), "-c", cfile,
                            "-o", os.path.join(tmp, "hdr_check.o")])
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No CPU fallback: the binding, loaded where no libkvattn.so was built, refuses to import."""
+    import shutil
+    import sys
+    shutil.copy(os.path.join(ROOT, "decode_attention_prefix_amd", "kvattn.py"), str(tmp_path / "kvattn.py"))
+    r = subprocess.run([sys.executable, "-c", "import kvattn"], cwd=str(tmp_path), capture_output=True, text=True)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libkvattn.so is not built" in r.stderr
