@@ -198,3 +198,33 @@ def test_append_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(out, eager), "replay %d" % rep
         assert np.array_equal(host(kc), ref_k) and np.array_equal(host(vc), ref_v)
+
+
+def random_forest_private_leaves(seed):
+    """Random prefix forests (1-3 roots, optional children, random head shapes) where every
+    query ends in a private leaf of 1-90 tokens, so its new token's block is its own."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 24))
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    n_roots = int(rng.integers(1, 4))
+    segs = []
+    for b in range(B):
+        r = int(rng.integers(0, n_roots))
+        s = [(("root", r), 16 * int(1 + (r * 7) % 5))]
+        if rng.random() < 0.6:
+            c = int(rng.integers(0, 3))
+            s.append((("child", r, c), 16 * int(1 + c)))
+        s.append((("leaf", b), int(rng.integers(1, 90))))
+        segs.append(s)
+    return W.from_segments("forest%d" % seed, segs, G * Hkv, Hkv, D, seed, seed + 1, extra_blocks=3)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_append_random_forests(seed):
+    """The fused append on random prefix forests with private leaves, against the oracle."""
+    wl = random_forest_private_leaves(2000 + seed).materialize()
+    got, ref, _ = run_append(wl, 3000 + seed)
+    assert_close(got, ref, "append %s" % wl.name)
+

@@ -443,3 +443,30 @@ def test_multi_stream_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(out, eager), "replay %d" % rep
     assert_close(eager.cpu().numpy().astype(np.float64), oracle_out(wl), "multi-stream eager")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_parity_random_trees(seed):
+    """Random prefix forests (1-3 roots, optional children and private leaves, random head
+    shapes and head_dim) under auto, forced-variant and full-pack plans, plus the
+    multi-stream forward, against the oracle."""
+    from test_plan import random_tree_workload
+    wl = random_tree_workload(1000 + seed).materialize()
+    ref = oracle_out(wl)
+    k = K()
+    cases = [{}, {"pack_mode": 2}, {"force_variant": 1, "split_tokens": 32}, {"multi_stream": 1}]
+    if wl.group <= valu_max_rows(wl.head_dim):
+        cases.append({"force_variant": 0, "pack_mode": 2, "scheme": 2})
+    for opts in cases:
+        if opts.get("multi_stream"):
+            print("case %s opts %s" % (wl.name, opts), flush=True)
+            dec = k.Decoder(wl.shape_tuple(), wl.block_tables, wl.seq_lens, options=k.make_options(**opts))
+            q, kc, vc = device_inputs(wl)
+            out = torch.full((wl.num_queries, wl.num_q_heads, wl.head_dim), float("nan"), device="cuda")
+            side = torch.cuda.Stream()
+            dec.decode_streams(q, kc, vc, out, side_stream=side)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy().astype(np.float64)
+        else:
+            got, _ = gpu_decode(wl, **opts)
+        assert_close(got, ref, "%s %s" % (wl.name, opts))
