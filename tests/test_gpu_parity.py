@@ -470,3 +470,24 @@ def test_parity_random_trees(seed):
         else:
             got, _ = gpu_decode(wl, **opts)
         assert_close(got, ref, "%s %s" % (wl.name, opts))
+
+
+def test_parity_full_size_after_plan_update():
+    """The Llama-3-8B layer workload at full size: a plan made one decode step earlier
+    (every query one token shorter) and brought forward by kvattn_plan_update decodes
+    like the oracle on sampled rows."""
+    k = K()
+    wl = W.WORKLOADS[2]().materialize()
+    prev = _cut_state(wl, np.ones(wl.num_queries, dtype=np.int32))
+    print("case full-size update", flush=True)
+    dec = k.Decoder(wl.shape_tuple(), prev.block_tables, prev.seq_lens)
+    dec.update(wl.block_tables, wl.seq_lens)
+    assert dec.stats()["update_path"] in (1, 2)
+    q, kc, vc = device_inputs(wl)
+    out = torch.full((wl.num_queries, wl.num_q_heads, wl.head_dim), float("nan"), device="cuda")
+    dec.decode(q, kc, vc, out)
+    torch.cuda.synchronize()
+    rows = sampled_rows(wl, 192, 22)
+    ref = oracle.decode_workload(wl, rows=rows)
+    assert_close(out.cpu().numpy().astype(np.float64).reshape(-1, wl.head_dim)[rows], ref, "full size after update")
+    _dev_cache.clear()
