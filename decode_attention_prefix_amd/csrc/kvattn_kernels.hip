@@ -18,7 +18,12 @@
 //                  runs across the list's tasks, 8-lane DPP reductions.
 // Merge (PAT review, merge stage: online-softmax combination of the per-
 // workgroup partial results of a query): one wave per 256 output floats of a
-// query, single pass over its partials (consecutive slot blocks).
+// query, single pass over its partials (consecutive slot blocks).  Its
+// fused-append form also scores each query's new token and writes the token's
+// K/V into its paged slot (short-term-memory page: the decode step appends
+// K_t, V_t, then attends).
+// A measurement helper, a plain streaming read of two buffers, sits before
+// the launchers; it is not part of the attention path.
 //
 // Scores are kept in log2 units (q.k * scale * log2 e) so every exponential is
 // a single v_exp_f32.  The running max is refreshed lazily: a row is rescaled
