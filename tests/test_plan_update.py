@@ -179,3 +179,56 @@ def test_invalid_update_leaves_plan_unchanged():
     after = K.kvattn_plan_export(plan)
     assert np.array_equal(before["desc"], after["desc"])
     assert np.array_equal(before["block_ids"], after["block_ids"])
+
+
+def random_forest(seed, extra=6):
+    """Random prefix forest with private leaves long enough to grow into."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(2, 20))
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    n_roots = int(rng.integers(1, 4))
+    segs = []
+    for b in range(B):
+        r = int(rng.integers(0, n_roots))
+        s = [(("root", r), 16 * int(1 + (r * 7) % 5))]
+        if rng.random() < 0.6:
+            c = int(rng.integers(0, 3))
+            s.append((("child", r, c), 16 * int(1 + c)))
+        s.append((("leaf", b), int(rng.integers(30, 120))))
+        segs.append(s)
+    return W.from_segments("fuzz%d" % seed, segs, G * Hkv, Hkv, D, seed, seed + 1, extra_blocks=extra)
+
+
+@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("new_token", [0, 1])
+def test_update_fuzz_random_forests(seed, new_token):
+    """Random forests, random per-step growth (0-3 tokens per query, sometimes none at all):
+    after every update the plan satisfies the invariants at the current lengths."""
+    wl = random_forest(500 + seed)
+    rng = np.random.default_rng(seed)
+    cut = rng.integers(8, 28, wl.num_queries).astype(np.int32)
+    bt, lens = state(wl, cut)
+    opts = K.make_options(new_token=new_token)
+    plan = K.kvattn_plan(wl.shape_tuple(), bt, lens, None, opts)
+    paths = []
+    while cut.any():
+        step = np.minimum(cut, rng.integers(0, 4, wl.num_queries)).astype(np.int32)
+        if rng.random() < 0.1:
+            step[:] = 0
+        cut -= step
+        bt, lens = state(wl, cut)
+        K.kvattn_plan_update(plan, bt, lens)
+        st = K.kvattn_plan_stats(plan)
+        paths.append(st["update_path"])
+        ex = K.kvattn_plan_export(plan)
+        cached = lens - 1 if new_token else lens
+        check_coverage(bt, cached, wl.num_q_heads, wl.num_kv_heads, ex, all_merged=bool(new_token))
+        check_descriptors(ex)
+        if new_token:
+            codes = [int(bt[b, (int(T) - 1) // 16]) * 16 + (int(T) - 1) % 16 for b, T in enumerate(lens)]
+            for i, b in enumerate(ex["merge_query"]):
+                assert ex["merge_rec"][i, 3] == codes[b]
+        assert st["unique_kv_bytes"] == unique_tokens(bt, cached) * wl.bytes_per_token
+    assert paths and set(paths) <= {1, 2, 3}
