@@ -491,3 +491,30 @@ def test_parity_full_size_after_plan_update():
     ref = oracle.decode_workload(wl, rows=rows)
     assert_close(out.cpu().numpy().astype(np.float64).reshape(-1, wl.head_dim)[rows], ref, "full size after update")
     _dev_cache.clear()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_parity_random_forest_updates(seed):
+    """Random forests brought forward by kvattn_plan_update with uneven steps; the decode
+    after every fourth update matches the oracle at the current lengths."""
+    from test_plan_update import random_forest
+    k = K()
+    wl = random_forest(700 + seed).materialize()
+    rng = np.random.default_rng(seed)
+    cut = rng.integers(8, 28, wl.num_queries).astype(np.int32)
+    cur = _cut_state(wl, cut)
+    print("case random-forest updates %s" % wl.name, flush=True)
+    dec = k.Decoder(wl.shape_tuple(), cur.block_tables, cur.seq_lens)
+    q, kc, vc = device_inputs(wl)
+    n = 0
+    while cut.any():
+        cut -= np.minimum(cut, rng.integers(0, 4, wl.num_queries)).astype(np.int32)
+        cur = _cut_state(wl, cut)
+        dec.update(cur.block_tables, cur.seq_lens)
+        n += 1
+        if n % 4 == 0 or not cut.any():
+            out = torch.full((wl.num_queries, wl.num_q_heads, wl.head_dim), float("nan"), device="cuda")
+            dec.decode(q, kc, vc, out)
+            torch.cuda.synchronize()
+            assert_close(out.cpu().numpy().astype(np.float64), oracle.decode_workload(cur),
+                         "%s after %d updates" % (wl.name, n))
