@@ -921,6 +921,11 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     int32_t slots_used = 0;
     // rows with one partial write out directly, unless the new token joins them in the merge
     const int min_merged = o.new_token ? 1 : 2;
+    int64_t slots_wide = 0;
+    for (int b = 0; b < B; ++b)
+        if (count[b] >= min_merged) slots_wide += int64_t(count[b]) * Hq;
+    if (slots_wide > std::numeric_limits<int32_t>::max())
+        return set_error(KVATTN_EUNSUPPORTED, "more than 2^31 - 1 partial slots: split the batch");
     for (int b = 0; b < B; ++b)
         if (count[b] >= min_merged) {
             slot_base[b] = slots_used;
@@ -1330,6 +1335,9 @@ kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables
     if (s.head_dim != 64 && s.head_dim != 128) return set_error(KVATTN_EUNSUPPORTED, "head_dim must be 64 or 128");
     if (s.num_q_heads / s.num_kv_heads > kMaxGroup)
         return set_error(KVATTN_EUNSUPPORTED, "more than 64 q heads per KV head");
+    // the kernels index q (and out) rows with 32-bit element offsets
+    if (int64_t(s.num_queries) * s.num_q_heads * s.head_dim >= (int64_t(1) << 31))
+        return set_error(KVATTN_EUNSUPPORTED, "num_queries * num_q_heads * head_dim must stay below 2^31");
     kvattn_plan_options o;
     kvattn_plan_options_default(&o);
     if (opts) o = *opts;

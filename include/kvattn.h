@@ -240,7 +240,8 @@ void kvattn_plan_options_default(kvattn_plan_options* opts);
  * [1, max_blocks*16], block id outside [0, num_physical_blocks), bad tree or
  * option; with new_token: two queries' new tokens in one block, or a query
  * reading another's new-token slot), EUNSUPPORTED (head_dim not 64/128,
- * block_size != 16, Hq/Hkv > 64; with new_token, a new-token block id >= 2^27),
+ * block_size != 16, Hq/Hkv > 64, num_queries * Hq * head_dim >= 2^31, more
+ * than 2^31 - 1 partial slots; with new_token, a new-token block id >= 2^27),
  * ENOMEM.  Reentrant; plans are independent.  With new_token, a tree (if
  * given) describes the cached part, the first seq_len - 1 tokens of each query;
  * a query with seq_len 1 has no cached part and query_leaf -1.

@@ -366,6 +366,12 @@ def test_validation_errors():
         s[field] = 0
         expect(K.KVATTN_EUNSUPPORTED if field == 4 else K.KVATTN_EINVAL,
                shape=s)
+    big = 1 << 17                             # 2^17 queries x 128 q heads x 128 dims = 2^31 q elements
+    s = list(shp)
+    s[0], s[1], s[2], s[3] = big, 128, 8, 128
+    with pytest.raises(K.KvattnError) as e:
+        K.kvattn_plan(tuple(s), np.zeros((big, s[5]), dtype=np.int32), np.ones(big, dtype=np.int32))
+    assert e.value.status == K.KVATTN_EUNSUPPORTED and "2^31" in K.kvattn_last_error()
     s = list(shp)
     s[1], s[2] = 128, 1                       # 128 q heads on one KV head: wider than 64
     expect(K.KVATTN_EUNSUPPORTED, shape=s)
