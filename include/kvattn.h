@@ -115,7 +115,12 @@ enum { KVATTN_VARIANT_AUTO = -1, KVATTN_VARIANT_VALU = 0, KVATTN_VARIANT_MFMA = 
  *                  split into several items; a wider GQA group is EUNSUPPORTED).
  *   split_tokens   0 auto; otherwise the KV chunk length of split items, rounded
  *                  up to a multiple of 16 (long-KV splitting).
- *   num_cus        compute units the split model balances over; 0 means 256.
+ *   num_cus        compute units the split model balances over; 0 means 256
+ *                  (a whole MI355X).  The plan makes 2 * num_cus static lists,
+ *                  two workgroups per CU; set it to the device's CU count when
+ *                  the GPU is partitioned or smaller.  Lists beyond what the
+ *                  device holds at once are claimed at run time (correct, but
+ *                  slower than a matching count).
  *   new_token      0: seq_lens count tokens already in the cache (kvattn_decode).
  *                  1: the last token of each query, position seq_len - 1, comes
  *                  with the call as k_new / v_new (kvattn_decode_append), which
