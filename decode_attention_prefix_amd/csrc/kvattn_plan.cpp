@@ -293,6 +293,13 @@ constexpr double kPartialWriteCostMfma = 2.0;
 // slower than on even ones, whatever the KV heads they read; VALU stripes on
 // odd XCDs are filled to 0.9 of the common level.
 constexpr double kOddXcdRate = 0.9;
+// A list that runs MFMA tasks starts its VALU stream late and from cold: the
+// descriptor window, the q rows and the first blocks each take a round trip
+// under full load (per-task traces on MI355X: a 16-token VALU remainder after
+// a C2 prefix task ended ~8 us after it).  A stripe with MFMA load is filled
+// only above that load plus this start cost, so no such list gets a remainder
+// too small to pay for its start.
+constexpr double kValuRestartCost = 40.0;
 
 // Append the descriptor of task t (see kDesc*) to P.desc; returns its words.
 int32_t put_desc(kvattn_plan_s& P, const Task& t) {
@@ -731,8 +738,10 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             std::vector<double> base(size_t(n_stripes), 0.0);
             // multi-stream plans run the MFMA lists in a launch of their own, beside the VALU one
             if (o.multi_stream) return base;
-            for (int s = 0; s < n_stripes; ++s)
+            for (int s = 0; s < n_stripes; ++s) {
                 for (int q = 0; q < quads; ++q) base[size_t(s)] = std::max(base[size_t(s)], load[size_t(stripe_list(s, q))]);
+                if (base[size_t(s)] > 0.0) base[size_t(s)] += kValuRestartCost;
+            }
             return base;
         };
         // the level at which the stripes, each filled from its base, hold `work`
