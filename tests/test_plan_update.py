@@ -202,15 +202,15 @@ def random_forest(seed, extra=6):
 
 
 @pytest.mark.parametrize("seed", range(16))
-@pytest.mark.parametrize("new_token", [0, 1])
-def test_update_fuzz_random_forests(seed, new_token):
+@pytest.mark.parametrize("new_token,multi_stream", [(0, 0), (1, 0), (0, 1)])
+def test_update_fuzz_random_forests(seed, new_token, multi_stream):
     """Random forests, random per-step growth (0-3 tokens per query, sometimes none at all):
     after every update the plan satisfies the invariants at the current lengths."""
     wl = random_forest(500 + seed)
     rng = np.random.default_rng(seed)
     cut = rng.integers(8, 28, wl.num_queries).astype(np.int32)
     bt, lens = state(wl, cut)
-    opts = K.make_options(new_token=new_token)
+    opts = K.make_options(new_token=new_token, multi_stream=multi_stream)
     plan = K.kvattn_plan(wl.shape_tuple(), bt, lens, None, opts)
     paths = []
     while cut.any():
@@ -226,6 +226,10 @@ def test_update_fuzz_random_forests(seed, new_token):
         cached = lens - 1 if new_token else lens
         check_coverage(bt, cached, wl.num_q_heads, wl.num_kv_heads, ex, all_merged=bool(new_token))
         check_descriptors(ex)
+        if multi_stream:   # every launch still holds one kernel family
+            lp = ex["list_ptr"]
+            for L in range(lp.shape[0]):
+                assert ((lp[L, :, 1] > lp[L, :, 0]).any()) != ((lp[L, :, 2] > lp[L, :, 1]).any())
         if new_token:
             codes = [int(bt[b, (int(T) - 1) // 16]) * 16 + (int(T) - 1) % 16 for b, T in enumerate(lens)]
             for i, b in enumerate(ex["merge_query"]):
