@@ -13,7 +13,10 @@ in the softmax, a transposed operand -- fails at least one of them:
   * invariants: token order, a common score shift, linearity in V, GQA equal
     to MHA with repeated KV, outputs inside the convex hull of the V rows;
   * the merge rule: merging the partial triples of two halves equals the
-    attention over the whole sequence.
+    attention over the whole sequence;
+  * the row-subset path (decode_rows with an arbitrary list of b * Hq + h
+    rows: permuted, repeated, single, last) against torch float64 SDPA of
+    each listed row, and bit for bit against the same rows of decode_all.
 """
 import json
 import os
@@ -303,3 +306,53 @@ def test_append_then_attend_steps_equal_causal_attention(seed, B, Hq, Hkv, D, L,
             np.testing.assert_allclose(got[b], ref[0, :, t, :].numpy(), rtol=0, atol=1e-12)
     np.testing.assert_array_equal(kp, kp_full)
     np.testing.assert_array_equal(vp, vp_full)
+
+
+def _sdpa_rows(q, dk, dv, Hq, Hkv, rows):
+    """torch float64 SDPA of each listed row b * Hq + h over query b's own dense K/V."""
+    import torch
+    G = Hq // Hkv
+    D = q.shape[-1]
+    out = np.empty((len(rows), D))
+    for i, r in enumerate(rows):
+        b, h = divmod(int(r), Hq)
+        qt = torch.from_numpy(bf16_bits_to_f32(q[b, h]).astype(np.float64)).reshape(1, 1, 1, D)
+        kt = torch.from_numpy(bf16_bits_to_f32(dk[b][:, h // G]).astype(np.float64)).reshape(1, 1, -1, D)
+        vt = torch.from_numpy(bf16_bits_to_f32(dv[b][:, h // G]).astype(np.float64)).reshape(1, 1, -1, D)
+        out[i] = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).reshape(D).numpy()
+    return out
+
+
+@pytest.mark.parametrize("seed,B,Hq,Hkv,D,Tmax,bs", [
+    (40, 5, 8, 2, 64, 70, 16),
+    (41, 3, 6, 3, 32, 45, 4),
+])
+def test_row_subset_path(seed, B, Hq, Hkv, D, Tmax, bs):
+    """decode_rows writes row r of its output from (b, h) = divmod(rows[r], Hq), for any row list.
+
+    Every full-size parity check goes through this path with a row list other
+    than arange, so it is pinned on its own: permuted, repeated, single and
+    last rows against torch float64 SDPA of each listed row, and bit for bit
+    against the same rows of decode_all.  A row index taken from r instead of
+    rows[r], a swapped (b, h) split or an output offset of rows[r] * D fails
+    it.
+    """
+    pytest.importorskip("torch")
+    rng = np.random.default_rng(seed)
+    q, dk, dv, kp, vp, bt, sl = rand_case(rng, B, Hq, Hkv, D, Tmax, bs)
+    full = run_oracle(q, kp, vp, bt, sl, Hq, Hkv, bs).reshape(B * Hq, D)
+    n = B * Hq
+    perm = rng.permutation(n)
+    subsets = [
+        perm,                                              # every row, permuted
+        perm[: n // 3],                                    # a permuted strict subset
+        np.array([n - 1]),                                 # the last row alone
+        np.array([3, 3, 0, n - 1, 3, 1]),                  # repeats and out-of-order rows
+        rng.integers(0, n, size=2 * n),                    # random rows with repeats
+    ]
+    for rows in subsets:
+        rows = np.asarray(rows, dtype=np.int64)
+        got = oracle.decode_rows(q, kp, vp, bt, sl, Hq, Hkv, rows, block_size=bs)
+        assert got.shape == (len(rows), D)
+        np.testing.assert_allclose(got, _sdpa_rows(q, dk, dv, Hq, Hkv, rows), rtol=0, atol=1e-12)
+        assert np.array_equal(got, full[rows])
