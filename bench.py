@@ -7,6 +7,12 @@ already resident in HBM.  The plan (host pack scheduler) is built and uploaded
 once before timing: one plan serves every layer of a decode step, and its host
 time is reported separately as plan_ms.
 
+A default run measures all five workloads, one after the other, and prints one
+JSON line: the headline fields are those of the largest single-GPU workload,
+the stateful streaming sessions (16 sessions x 131072 tokens, 8 registered
+queries each, 64/8 heads, d 128); "per_config" holds the same measurements for
+every workload.  --config N measures workload N alone (profiler runs).
+
 So that the 256 MB Infinity Cache cannot serve a whole batch from a previous
 step, the steps rotate over enough HBM-resident copies of the KV pools that
 each step reads data last touched several hundred MB earlier.
@@ -14,8 +20,10 @@ each step reads data last touched several hundred MB earlier.
 Metric: effective HBM GB/s counting unique KV bytes (each physical block of the
 paged cache once, K and V, all KV heads), and microseconds per call.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config all|1..5]
        python bench.py --copy-calibration BYTES   (plain device copy, for counter scaling)
+       python bench.py --summarize-trace DIR --config N        (rocprofv3 kernel-trace summary)
+       python bench.py --summarize-counters FETCH_DIR WRITE_DIR CAL_FETCH_DIR CAL_WRITE_DIR --config N
 """
 from __future__ import annotations
 
@@ -85,15 +93,26 @@ def traffic_from_counters(c):
     return fetch + write, fetch, merge_fetch
 
 
-def cpu_baseline(wl, budget_s=12.0):
+def cpu_baseline(wl, budget_s=8.0, threads=None):
     """The fp64 oracle on the host cores, on a bounded sample of (query, head) rows.
 
     When the whole batch costs less than the budget, the sample is the whole
     batch, repeated until the budget is spent; otherwise it is a random subset
     of rows sized to the budget, and the full-batch time is extrapolated by the
-    subset's share of the token-row work.
+    subset's share of the token-row work.  threads: OpenMP threads (None: all
+    the host's cores, the oracle's default).
     """
     import oracle
+    default_threads = oracle.threads()
+    if threads is not None:
+        oracle.set_threads(threads)
+    try:
+        return _cpu_baseline(oracle, wl, budget_s)
+    finally:
+        oracle.set_threads(default_threads)
+
+
+def _cpu_baseline(oracle, wl, budget_s):
     B, Hq = wl.num_queries, wl.num_q_heads
     rng = np.random.default_rng(1234)
     rows = rng.permutation(B * Hq).astype(np.int64)
@@ -266,9 +285,10 @@ def multi_stream_timing(K, torch, wl, dec, pools, q, outs, steps, warmup):
             "multi_stream_launches": st["num_launches"], "max_abs_diff": diff}
 
 
-def extras(K, torch, W, wl, dec, pools, q, outs, stream, n_ev, pool_bytes, args):
-    """Context beside the roofline: a plain streaming read of the same K/V pools
-    (kvattn_read_probe, same grid), and the decode step with its KV append fused in."""
+def plain_read(K, torch, pools, stream, n_ev):
+    """A plain streaming read of the same K/V pools (kvattn_read_probe, one contiguous
+    share per workgroup), median of HIP-event timed launches: what the memory system
+    delivers for those bytes at that size, as context beside the peak."""
     copies = len(pools)
     grid = 2 * torch.cuda.get_device_properties(0).multi_processor_count
     sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
@@ -280,56 +300,111 @@ def extras(K, torch, W, wl, dec, pools, q, outs, stream, n_ev, pool_bytes, args)
         K.kvattn_read_probe(pools[i % copies][0], pools[i % copies][1], sink, grid, stream)
         pev[i][1].record(stream)
     torch.cuda.synchronize()
-    probe_us = float(np.median([e[0].elapsed_time(e[1]) for e in pev])) * 1e3
-    attainable = pool_bytes / (probe_us * 1e-6) / 1e9
-
-    append = append_timing(K, torch, W, wl, dec, pools, q, outs, min(args.steps, 100), args.warmup)
-    log("bench: decode step with KV append %s" % json.dumps(append))
-    multi = multi_stream_timing(K, torch, wl, dec, pools, q, outs, min(args.steps, 100), args.warmup)
-    log("bench: multi-stream forward %s" % json.dumps(multi))
-    plain = {"GB/s": round(attainable, 1), "bytes": int(pool_bytes), "us": round(probe_us, 2), "grid": grid,
-                     "what": "kvattn_read_probe: one contiguous share per workgroup of the K and V pools, "
-                             "median of HIP-event timed launches"}
-    return plain, append, multi
+    us = float(np.median([e[0].elapsed_time(e[1]) for e in pev])) * 1e3
+    nbytes = pools[0][0].numel() * 2 + pools[0][1].numel() * 2
+    return {"GB/s": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": int(nbytes), "us": round(us, 2), "grid": grid,
+            "what": "kvattn_read_probe: one contiguous share per workgroup of the K and V pools, "
+                    "median of HIP-event timed launches"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--pack-mode", type=int, default=0)
-    ap.add_argument("--split-tokens", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-check", action="store_true")
-    ap.add_argument("--copies", type=int, default=0)
-    ap.add_argument("--copy-calibration", type=int, default=0)
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
-    ap.add_argument("--prewarm-s", type=float, default=0.2,
-                    help="seconds of untimed calls before the counted warm-up steps (GPU clocks settle)")
-    ap.add_argument("--no-extras", action="store_true",
-                    help="skip the plain-read probe and the fused-append timing (profiler runs of the decode alone)")
-    args = ap.parse_args()
+# ---- rocprofv3 summaries (profiles/) -------------------------------------------------------------
+WORKLOAD_NAMES = {1: "c1_tiny", 2: "c2_llama3_8b_layer", 3: "c3_two_level_tree", 4: "c4_streaming_sessions",
+                  5: "c5_no_sharing"}
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this decode-attention library has no multi-GPU path "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
 
-    import torch
+def _csv_rows(directory, suffix):
+    """Rows of every rocprofv3 CSV file named *<suffix> under directory (any depth)."""
+    import csv
+    rows = []
+    for root, _, files in os.walk(directory):
+        for name in sorted(files):
+            if name.endswith(suffix):
+                with open(os.path.join(root, name), newline="") as f:
+                    rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit("no *%s under %s" % (suffix, directory))
+    return rows
+
+
+def _short(name):
+    name = name.replace("void kvattn::(anonymous namespace)::", "")
+    return name[:60]
+
+
+def trace_summary(directory, c, command):
+    """Text summary of a rocprofv3 --kernel-trace --stats run: calls and durations per kernel."""
+    rows = _csv_rows(directory, "kernel_stats.csv")
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["rocprofv3 kernel-trace summary: %s" % WORKLOAD_NAMES[c],
+             "command: %s" % command,
+             "kernel source sha256[:16]: %s" % kernel_src_sha(), "",
+             "%-60s %8s %12s %10s %10s %8s" % ("kernel", "calls", "avg_ns", "min_ns", "max_ns", "pct")]
+    for r in rows:
+        lines.append("%-60s %8s %12.1f %10s %10s %8.2f" % (_short(r["Name"]), r["Calls"], float(r["AverageNs"]),
+                                                             r["MinNs"], r["MaxNs"], float(r["Percentage"])))
+    return "\n".join(lines)
+
+
+def _counter_by_kernel(directory, counter):
+    """Mean counter value per dispatch, by kernel name (first dispatch of each kernel dropped when
+    several exist: it runs cold)."""
+    per = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r.get("Counter_Name", counter) != counter:
+            continue
+        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (float(np.mean(v[1:])) if len(v) > 2 else float(np.mean(v)), len(v)) for k, v in per.items()}
+
+
+def counters_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, c, command):
+    """profiles/counters_c<c>.json from four rocprofv3 --pmc runs: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) of the decode, and of a plain 1 GiB device copy that scales each counter to bytes."""
     import workloads as W
-    from decode_attention_prefix_amd import kvattn as K
+    fetch = _counter_by_kernel(fetch_dir, "FETCH_SIZE")
+    write = _counter_by_kernel(write_dir, "WRITE_SIZE")
+    cal_f = max(v for v, _ in _counter_by_kernel(cal_fetch_dir, "FETCH_SIZE").values())
+    cal_w = max(v for v, _ in _counter_by_kernel(cal_write_dir, "WRITE_SIZE").values())
+    copy_kib = 1024.0 * 1024.0
+    fwd = next(k for k in fetch if "fwd_kernel" in k)
+    mrg = next((k for k in fetch if "merge_kernel" in k), None)
+    wl = W.WORKLOADS[c]()
+    uniq = wl.unique_kv_bytes
+    rec = {
+        "workload": wl.name, "kernel": fwd, "kernel_src_sha": kernel_src_sha(),
+        "forward_fetch_kib": fetch[fwd][0], "forward_write_kib": write[fwd][0],
+        "merge_fetch_kib": fetch[mrg][0] if mrg else None, "merge_write_kib": write[mrg][0] if mrg else None,
+        "fetch_scale": round(copy_kib / cal_f, 6), "write_scale": round(copy_kib / cal_w, 6),
+        "dispatches_averaged": fetch[fwd][1] - (1 if fetch[fwd][1] > 2 else 0),
+        "unique_kv_bytes": int(uniq),
+    }
+    rec["forward_fetch_bytes"] = int(rec["forward_fetch_kib"] * 1024 * rec["fetch_scale"])
+    rec["forward_write_bytes"] = int(rec["forward_write_kib"] * 1024 * rec["write_scale"])
+    rec["fetch_over_unique"] = round(rec["forward_fetch_bytes"] / uniq, 4)
+    rec["commands"] = command
+    rec["scale_note"] = ("a 1 GiB device copy reads %.1f KiB by FETCH_SIZE and writes %.1f KiB by WRITE_SIZE per "
+                         "dispatch; scale = 1 GiB / counter" % (cal_f, cal_w))
+    path = os.path.join(PROFILES, "counters_c%d.json" % c)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+# timed steps of the workloads that are not the headline (the headline takes --steps exactly)
+OTHER_STEPS = {1: 400, 2: 200, 3: 100, 4: 30, 5: 30}
+HEADLINE = 4
+SINGLE_CORE_CONFIGS = (1, 2, 3)
+
+
+def measure(c, args, torch, K, W, steps, warmup, extras_on):
+    """Every measurement of workload c; returns (record, workload description)."""
     t_gen = time.perf_counter()
-    wl = W.WORKLOADS[args.config]().materialize()
+    wl = W.WORKLOADS[c]().materialize()
     log("bench: %s generated in %.1f s; unique KV %.1f MB" % (wl.name, time.perf_counter() - t_gen,
                                                               wl.unique_kv_bytes / 1e6))
     opts = K.make_options(pack_mode=args.pack_mode, split_tokens=args.split_tokens)
+    # the device is initialised before this point: plan_upload_ms covers planning,
+    # the workspace allocation and the upload copy only
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     dec = K.Decoder(wl.shape_tuple(), wl.block_tables, wl.seq_lens, options=opts)
     torch.cuda.synchronize()
@@ -349,6 +424,7 @@ def main():
             for _ in range(copies)]
     stream = torch.cuda.current_stream()
 
+    parity = None
     if not args.no_check:
         import oracle
         K.kvattn_decode(q, k0, v0, dec.plan, outs[0], stream)
@@ -361,12 +437,13 @@ def main():
         err = float(np.abs(got - ref).max())
         log("bench: parity on %d sampled rows: max abs err %.3e" % (len(rows), err))
         assert err <= 2e-3, "parity check failed"
+        parity = {"rows_checked": int(len(rows)), "max_abs_err": float("%.3g" % err), "tolerance": 2e-3}
 
     def eager_step(i):
         kk, vv = pools[i % copies]
         K.kvattn_decode(q, kk, vv, dec.plan, outs[i % copies], stream)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         eager_step(i)
     torch.cuda.synchronize()
 
@@ -378,7 +455,7 @@ def main():
             with torch.cuda.graph(g):
                 K.kvattn_decode(q, pools[i][0], pools[i][1], dec.plan, outs[i])
             graphs.append(g)
-        for i in range(args.warmup):
+        for i in range(warmup):
             graphs[i % copies].replay()
         torch.cuda.synchronize()
 
@@ -398,21 +475,21 @@ def main():
             step(i)
             i += 1
         torch.cuda.synchronize()
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, synchronised on both sides
+    # timed region: exactly `steps` steps, synchronised on both sides
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall / args.steps * 1e3
+    ms_per_step = wall / steps * 1e3
 
     # per-stage GPU time with HIP events on the launch stream
-    n_ev = min(args.steps, 100)
+    n_ev = min(max(steps, 30), 100)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
     for i in range(n_ev):
         kk, vv = pools[i % copies]
@@ -426,36 +503,38 @@ def main():
     mrg_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(n_ev)])
     call_ms = fwd_ms + mrg_ms
 
-    # a plain streaming read of the same pools (same bytes, same grid) for context beside the peak
-    plain_read = append = multi = None
-    if not args.no_extras:
-        plain_read, append, multi = extras(K, torch, W, wl, dec, pools, q, outs, stream, n_ev, pool_bytes, args)
+    plain = plain_read(K, torch, pools, stream, n_ev)
+    append = multi = None
+    if extras_on:
+        append = append_timing(K, torch, W, wl, dec, pools, q, outs, min(steps, 100), warmup)
+        log("bench: decode step with KV append %s" % json.dumps(append))
+        multi = multi_stream_timing(K, torch, wl, dec, pools, q, outs, min(steps, 100), warmup)
+        log("bench: multi-stream forward %s" % json.dumps(multi))
 
     uniq = wl.unique_kv_bytes
     value = uniq / (ms_per_step * 1e-3) / 1e9
     fwd_avg = float(fwd_ms.mean())
     achieved = uniq / (fwd_avg * 1e-3) / 1e9
-    traffic, fetched, merge_fetched = traffic_from_counters(args.config)
+    traffic, fetched, merge_fetched = traffic_from_counters(c)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None if traffic is None else int(traffic),
                 "kernel": "fwd_kernel (persistent; %d MFMA + %d VALU items)" % (st["num_items_mfma"],
                                                                                  st["num_items_valu"]),
                 "algorithmic_bytes_per_launch": int(uniq),
                 "avg_forward_us": round(fwd_avg * 1e3, 2), "avg_merge_us": round(float(mrg_ms.mean()) * 1e3, 2),
-                "plain_read": None if plain_read is None else
-                dict(plain_read, forward_over_plain_read=round(achieved / plain_read["GB/s"], 4))}
-    result = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": describe(args.config, wl),
+                "plain_read": dict(plain, forward_over_plain_read=round(achieved / plain["GB/s"], 4))}
+    rec = {
+        "value": round(value, 1), "unit": "GB/s", "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
         "us_per_call": round(ms_per_step * 1e3, 2),
         "us_per_call_gpu_events_median": round(float(np.median(call_ms)) * 1e3, 2),
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "redundancy_fetch_over_unique": None if fetched is None else round(fetched / uniq, 4),
-        "redundancy_fetch_over_unique_with_merge": None if fetched is None else round((fetched + merge_fetched) / uniq, 4),
+        "redundancy_fetch_over_unique_with_merge": None if fetched is None else round((fetched + merge_fetched) / uniq,
+                                                                                      4),
         "plan_ms": round(st["plan_seconds"] * 1e3, 3), "plan_upload_ms": round(plan_upload_ms, 3),
         "plan_update_ms": round(upd_ms, 3), "plan_update_path": upd_path,
+        "parity_sample": parity,
         "decode_with_kv_append": append,
         "multi_stream_forward": multi,
         "plan": {k: st[k] for k in ("num_items", "num_items_valu", "num_items_mfma", "num_packed_nodes",
@@ -465,8 +544,105 @@ def main():
         "timing": "HIP graph replay per call" if graphs else "eager launches",
         "roofline": roofline,
     }
+    desc = describe(c, wl)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl)
+        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
+        log("bench: cpu baseline %s" % json.dumps(rec["cpu_baseline"]))
+        if c in SINGLE_CORE_CONFIGS:
+            rec["cpu_baseline_single_core"] = cpu_baseline(wl, args.cpu_budget_s / 2, threads=1)
+            log("bench: cpu baseline, one core %s" % json.dumps(rec["cpu_baseline_single_core"]))
+    del dec, graphs, pools, outs, q, k0, v0
+    wl.release_values()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec, desc
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30, help="timed steps of the headline workload")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="all", choices=["all", "1", "2", "3", "4", "5"])
+    ap.add_argument("--pack-mode", type=int, default=0)
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=8.0, help="wall seconds of oracle work per workload")
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--copies", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0)
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--prewarm-s", type=float, default=0.2,
+                    help="seconds of untimed calls before the counted warm-up steps (GPU clocks settle)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the fused-append and multi-stream timings (profiler runs of the decode alone)")
+    ap.add_argument("--summarize-trace", default=None, metavar="DIR")
+    ap.add_argument("--summarize-counters", nargs=4, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"))
+    ap.add_argument("--command", default="", help="the profiling command, recorded in a summary")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this decode-attention library has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.summarize_trace or args.summarize_counters:
+        c = HEADLINE if args.config == "all" else int(args.config)
+        if args.summarize_trace:
+            print(trace_summary(args.summarize_trace, c, args.command))
+        else:
+            counters_summary(*args.summarize_counters, c, args.command)
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    import torch
+    import workloads as W
+    from decode_attention_prefix_amd import kvattn as K
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.init()
+    torch.empty(1, device="cuda")
+    torch.cuda.synchronize()
+    configs = [1, 2, 3, 4, 5] if args.config == "all" else [int(args.config)]
+    headline = HEADLINE if args.config == "all" else int(args.config)
+    per_config, desc = {}, {}
+    for c in configs:
+        steps = args.steps if c == headline else max(args.steps, OTHER_STEPS[c])
+        rec, d = measure(c, args, torch, K, W, steps, args.warmup, extras_on=not args.no_extras)
+        per_config[d["workload"]] = dict(rec, config=d)
+        desc[c] = d
+        log("bench: %s %.2f us/call, %.1f GB/s (%.1f %% of peak), forward frac %.4f" % (
+            d["workload"], rec["us_per_call"], rec["value"], rec["pct_of_peak_hbm"], rec["roofline"]["frac"]))
+    head = per_config[desc[headline]["workload"]]
+    result = {
+        "metric": METRIC, "value": head["value"], "unit": "GB/s", "n_gpus": 1, "steps": head["steps"],
+        "warmup": head["warmup"], "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": desc[headline],
+    }
+    for k in ("us_per_call", "us_per_call_gpu_events_median", "pct_of_peak_hbm", "redundancy_fetch_over_unique",
+              "redundancy_fetch_over_unique_with_merge", "plan_ms", "plan_upload_ms", "plan_update_ms",
+              "plan_update_path", "parity_sample", "plan", "kv_copies_rotated", "timing", "roofline"):
+        result[k] = head[k]
+    if "cpu_baseline" in head:
+        result["cpu_baseline"] = head["cpu_baseline"]
+    if len(per_config) > 1:
+        summary_keys = ("us_per_call", "value", "pct_of_peak_hbm", "redundancy_fetch_over_unique",
+                        "redundancy_fetch_over_unique_with_merge", "plan_ms", "plan_upload_ms", "plan_update_ms",
+                        "parity_sample", "decode_with_kv_append", "multi_stream_forward", "plan", "steps",
+                        "kv_copies_rotated", "cpu_baseline", "cpu_baseline_single_core")
+        result["per_config"] = {}
+        for name, rec in per_config.items():
+            r = {k: rec[k] for k in summary_keys if k in rec}
+            rf = rec["roofline"]
+            r["forward"] = {"avg_us": rf["avg_forward_us"], "merge_avg_us": rf["avg_merge_us"],
+                            "frac": rf["frac"], "achieved_GB/s": rf["achieved"], "traffic": rf["traffic"],
+                            "plain_read_GB/s": rf["plain_read"]["GB/s"],
+                            "forward_over_plain_read": rf["plain_read"]["forward_over_plain_read"]}
+            r["config"] = {k: rec["config"][k] for k in ("batch", "q_heads", "kv_heads", "head_dim",
+                                                         "unique_kv_bytes", "prefix_ratio", "structure")}
+            result["per_config"][name] = r
     print(json.dumps(result), flush=True)
 
 

@@ -1386,6 +1386,8 @@ kvattn_status kvattn_plan_update(kvattn_plan_t plan, const int32_t* block_tables
     using namespace kvattn;
     clear_error();
     if (!plan || !block_tables || !seq_lens) return set_error(KVATTN_EINVAL, "plan, block_tables or seq_lens is NULL");
+    // an upload still in flight reads the blob this call changes or frees
+    if (plan->upload_event && plan->upload_wait) plan->upload_wait(plan->upload_event);
     const auto t0 = std::chrono::steady_clock::now();
     const kvattn_shape& s = plan->shape;
     for (int b = 0; b < s.num_queries; ++b)
@@ -1415,12 +1417,16 @@ kvattn_status kvattn_plan_update(kvattn_plan_t plan, const int32_t* block_tables
             kvattn_plan_t fresh = nullptr;
             const kvattn_status st = kvattn_plan(&s, block_tables, seq_lens, nullptr, &plan->opts, &fresh);
             if (st != KVATTN_OK) return st;
-            // the plan keeps its stream events (owned by the runtime) across the rebuild
+            // the plan keeps its events (owned by the runtime) across the rebuild
             void* fork_event = plan->fork_event;
             void* join_event = plan->join_event;
+            void* upload_event = plan->upload_event;
+            void (*upload_wait)(void*) = plan->upload_wait;
             *plan = std::move(*fresh);
             plan->fork_event = fork_event;
             plan->join_event = join_event;
+            plan->upload_event = upload_event;
+            plan->upload_wait = upload_wait;
             delete fresh;
             path = 3;
         }

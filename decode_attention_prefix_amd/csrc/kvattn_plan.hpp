@@ -34,6 +34,13 @@ struct kvattn_plan_s {
     std::vector<int32_t> reads;             // new-token plans: [num_physical_blocks] most tokens a cached part reads
     void* fork_event = nullptr;             // multi-stream decode: hipEvent_t pair, created on first use
     void* join_event = nullptr;
+    // hipEvent_t recorded on the upload stream right after the last upload's
+    // copy, and the runtime's function that waits for it.  The copy reads the
+    // host blob asynchronously, so kvattn_plan_update and kvattn_plan_destroy
+    // wait for it before they change or free the blob.  Both are set by the
+    // runtime (this header has no HIP dependency); a plan never uploaded has none.
+    void* upload_event = nullptr;
+    void (*upload_wait)(void* event) = nullptr;
     void* dev_ws = nullptr;                 // bound device workspace (caller-owned)
     size_t dev_bytes = 0;
 };

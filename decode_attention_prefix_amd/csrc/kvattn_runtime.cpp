@@ -39,6 +39,9 @@ Dims dims(const kvattn_plan_s& P) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Host wait for the event recorded after a plan's last upload copy.
+void wait_upload_event(void* event) { (void)hipEventSynchronize(static_cast<hipEvent_t>(event)); }
+
 kvattn_status check_bound(kvattn_plan_t plan) {
     if (!plan) return set_error(KVATTN_EINVAL, "plan is NULL");
     if (!plan->dev_ws) return set_error(KVATTN_ESTATE, "no device workspace bound: call kvattn_plan_upload first");
@@ -89,9 +92,32 @@ kvattn_status kvattn_plan_upload(kvattn_plan_t plan, void* dev_workspace, size_t
     if (bytes < plan->header.total_bytes)
         return set_error(KVATTN_EWORKSPACE, "workspace holds " + std::to_string(bytes) + " bytes, plan needs " +
                                                 std::to_string(plan->header.total_bytes));
-    hipError_t e = hipMemcpyAsync(dev_workspace, plan->blob.data(), plan->blob.size(), hipMemcpyHostToDevice,
-                                  static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // A captured copy would read the host blob again at every replay, after
+    // updates have changed it: uploads stay outside graphs.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(s, &cap);
+    if (e != hipSuccess) return set_error(KVATTN_EHIP, std::string("stream query failed: ") + hipGetErrorString(e));
+    if (cap != hipStreamCaptureStatusNone)
+        return set_error(KVATTN_EINVAL, "kvattn_plan_upload on a capturing stream: upload before capturing decodes");
+    if (!plan->upload_event) {
+        hipEvent_t ev = nullptr;
+        e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e != hipSuccess) return set_error(KVATTN_EHIP, std::string("event creation failed: ") + hipGetErrorString(e));
+        plan->upload_event = ev;
+        plan->upload_wait = wait_upload_event;
+    }
+    // an earlier upload of this plan may still be reading the blob; it is
+    // unchanged since (updates wait for it), so the copies may overlap
+    e = hipMemcpyAsync(dev_workspace, plan->blob.data(), plan->blob.size(), hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return set_error(KVATTN_EHIP, std::string("upload copy failed: ") + hipGetErrorString(e));
+    // kvattn_plan_update and kvattn_plan_destroy wait for this event before they
+    // change or free the blob the copy reads
+    e = hipEventRecord(static_cast<hipEvent_t>(plan->upload_event), s);
+    if (e != hipSuccess) {
+        (void)hipStreamSynchronize(s);   // no event to wait on later: let the copy finish now
+        return set_error(KVATTN_EHIP, std::string("event record failed: ") + hipGetErrorString(e));
+    }
     plan->dev_ws = dev_workspace;
     plan->dev_bytes = bytes;
     return KVATTN_OK;
@@ -203,6 +229,11 @@ kvattn_status kvattn_decode_streams(const void* q, const void* k_cache, const vo
 
 void kvattn_plan_destroy(kvattn_plan_t plan) {
     if (!plan) return;
+    // an upload still in flight reads the blob freed below
+    if (plan->upload_event) {
+        (void)hipEventSynchronize(static_cast<hipEvent_t>(plan->upload_event));
+        (void)hipEventDestroy(static_cast<hipEvent_t>(plan->upload_event));
+    }
     // events exist only if kvattn_decode_streams ran, i.e. on a host with the HIP runtime
     if (plan->fork_event) (void)hipEventDestroy(static_cast<hipEvent_t>(plan->fork_event));
     if (plan->join_event) (void)hipEventDestroy(static_cast<hipEvent_t>(plan->join_event));

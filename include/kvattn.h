@@ -234,10 +234,16 @@ typedef struct {
 void kvattn_plan_options_default(kvattn_plan_options* opts);
 
 /*
- * Build a decode plan on the host (no HIP call; usable without a GPU).
+ * Build a decode plan on the host (no HIP call; usable without a GPU): the
+ * pack stage of the PAT review's pack-forward-merge paradigm (method overview;
+ * pack scheduler workflow over a tree-structured block table, Fig 7 caption;
+ * memory-centric prefix-aware packing, Fig 5(d) caption; profit-model
+ * heuristic weighing prefix length against query count, implementation
+ * details of the pack scheduler), plus the forward stage's schedule (long-KV
+ * splitting and the runtime tile selector of the multi-tile kernel).
  * Steps: derive or check the prefix tree, decide packs with the profit model,
- * split long KV ranges, pick a kernel variant per item, order items longest
- * first, build the merge map, serialise the schedule.
+ * split long KV ranges, pick a kernel variant and KV tile per item, order items
+ * longest first, build the merge map, serialise the schedule.
  *   shape, block_tables, seq_lens: required; layouts above.
  *   tree: optional (NULL derives it); opts: optional (NULL = defaults).
  *   *out receives a plan owned by the caller until kvattn_plan_destroy.
@@ -268,7 +274,8 @@ kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables
  * block cap) the plan is rebuilt from scratch with its options, the tree derived.
  * stats.update_path tells which happened.  The device copy of the schedule is
  * stale afterwards: kvattn_plan_upload again before the next kvattn_decode (its
- * size, kvattn_plan_device_bytes, changes only on a rebuild).
+ * size, kvattn_plan_device_bytes, changes only on a rebuild).  If the plan was
+ * uploaded, the call first waits (host) for that upload's copy to finish.
  * New-token plans (options.new_token) take seq_lens with each query's new
  * token, as kvattn_plan does: the cached parts are extended, each merge record
  * gets its query's new slot, and the slot-ownership rule is checked again.
@@ -303,15 +310,27 @@ kvattn_status kvattn_plan_device_bytes(kvattn_plan_t plan, size_t* bytes);
  * Copy the plan's schedule into the caller's device workspace (one async
  * host-to-device copy on `stream`) and bind the workspace to the plan.
  * dev_workspace must be 256-byte aligned and at least kvattn_plan_device_bytes.
- * The plan's host blob is read until the copy completes: keep the plan alive
- * until `stream` has passed this point.  Binding again replaces the binding.
- * Errors: EINVAL (NULL), EWORKSPACE (too small / misaligned), EHIP.
+ * The copy reads the plan's host blob asynchronously; the plan records an
+ * event (created on the first upload) right after it, and kvattn_plan_update
+ * and kvattn_plan_destroy wait on the host for that event before they change
+ * or free the blob.  So update -> upload -> decode steps may follow each other
+ * without host synchronisation: each update blocks only until the previous
+ * upload's copy, queued on its stream, has run.  The upload must not be
+ * captured into a graph (a replay would read the blob as it is then): on a
+ * capturing stream it returns EINVAL.  Binding again replaces the binding.
+ * Errors: EINVAL (NULL, capturing stream), EWORKSPACE (too small /
+ * misaligned), EHIP.
  */
 kvattn_status kvattn_plan_upload(kvattn_plan_t plan, void* dev_workspace, size_t bytes, void* stream);
 
 /*
- * One decode-attention call: forward kernels over every planned item, then
- * the merge kernel over rows that have several partial triples.  q, k_cache,
+ * One decode-attention call, out = softmax(q K^T / sqrt(d)) V per (query, q
+ * head) over the query's paged KV (PAT review, core formula): the forward
+ * stage (split-KV multi-tile kernels over every planned item, each shared
+ * block read once for all the queries packed on it; PAT review, forward
+ * stage), then the merge stage over rows that have several partial triples
+ * (online-softmax combination of (m, l, acc); PAT review, merge stage).
+ * q, k_cache,
  * v_cache, out: device pointers, layouts above, matching the plan's shape.
  * The bound workspace holds the partial triples, so at most one decode per
  * workspace may be in flight.  One plan serves any number of calls (e.g. every
@@ -385,7 +404,8 @@ kvattn_status kvattn_plan_stats(kvattn_plan_t plan, kvattn_stats* stats);
 /* Host views of the schedule, for coverage checks and inspection. */
 kvattn_status kvattn_plan_export(kvattn_plan_t plan, kvattn_export* out);
 
-/* Free a plan (NULL is a no-op).  Does not touch the bound device workspace. */
+/* Free a plan (NULL is a no-op).  Waits (host) for the plan's last upload copy, if
+ * one is pending; does not touch the bound device workspace. */
 void kvattn_plan_destroy(kvattn_plan_t plan);
 
 /* Static name of a status code. */

@@ -47,6 +47,8 @@ def _oracle():
         lib.kvattn_oracle_merge.restype = ctypes.c_int
         lib.kvattn_oracle_threads.argtypes = []
         lib.kvattn_oracle_threads.restype = ctypes.c_int
+        lib.kvattn_oracle_set_threads.argtypes = [i32]
+        lib.kvattn_oracle_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -149,3 +151,8 @@ def merge(ms, ls, accs):
 def threads() -> int:
     """OpenMP threads the oracle uses on this host."""
     return int(_oracle().kvattn_oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Run later oracle calls on n OpenMP threads."""
+    _oracle().kvattn_oracle_set_threads(int(n))

@@ -158,3 +158,9 @@ int kvattn_oracle_merge(int32_t n, int32_t D, const double* m, const double* l, 
 
 /* OpenMP threads the oracle's parallel loops use. */
 int kvattn_oracle_threads(void) { return omp_get_max_threads(); }
+
+/* Set the OpenMP threads of later calls (n >= 1); the timing of the CPU baseline
+ * uses it to run on one core as well as on all of them. */
+void kvattn_oracle_set_threads(int32_t n) {
+    if (n >= 1) omp_set_num_threads(n);
+}
