@@ -162,6 +162,14 @@ int launch_read_probe(const void* a, size_t a_bytes, const void* b, size_t b_byt
                       void* stream);
 int launch_merge_append(const DevPlan& p, const Dims& d, int q_count, const NewTokens& nt, float* out, void* stream);
 
+// kvattn_decode_noalloc: bytes of the static per-device scratch that holds a
+// plan's workspace (schedule blob + partial triples), and devices supported.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+// Device address of this device's scratch (hipGetSymbolAddress, looked up once
+// per device); returns hipSuccess or the lookup's error.
+int scratch_device_pointer(void** ptr);
+
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 }  // namespace kvattn

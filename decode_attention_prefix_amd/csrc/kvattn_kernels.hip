@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "kvattn_internal.h"
 
@@ -1092,7 +1093,33 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict
     sink[size_t(blockIdx.x) * 256 + threadIdx.x] = x;
 }
 
+// Static device scratch of kvattn_decode_noalloc: the schedule blob and the
+// partial triples of the plan being decoded, for callers that cannot allocate.
+// Every device the library runs on holds its own copy until the process ends.
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
 }  // namespace
+
+int scratch_device_pointer(void** ptr) {
+    // One address per device, looked up once with that device current.  In host
+    // code `scratch` names a host-side stand-in, not device memory: only the
+    // address returned by hipGetSymbolAddress may reach a kernel or a copy.
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return int(e);
+    if (dev < 0 || dev >= kMaxDevices) return int(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return int(e);
+        addr[dev] = a;
+    }
+    *ptr = addr[dev];
+    return int(hipSuccess);
+}
 
 int launch_read_probe(const void* a, size_t a_bytes, const void* b, size_t b_bytes, uint32_t* sink, int grid,
                       void* stream) {

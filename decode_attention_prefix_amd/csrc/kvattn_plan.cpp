@@ -11,6 +11,7 @@
 // tile selector).  Nothing here calls HIP, so plans can be built and checked
 // on a host without a GPU.
 #include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <cstdint>
 #include <cmath>
@@ -36,6 +37,11 @@ kvattn_status set_error(kvattn_status s, const std::string& msg) {
     return s;
 }
 void clear_error() { g_last_error.clear(); }
+
+uint64_t next_generation() {
+    static std::atomic<uint64_t> counter{0};
+    return ++counter;
+}
 
 namespace {
 
@@ -1369,6 +1375,7 @@ kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables
         delete P;
         return st;
     }
+    P->generation = next_generation();
     if (std::getenv("KVATTN_LOG")) {
         const kvattn_stats& x = P->stats;
         std::fprintf(stderr,
@@ -1436,6 +1443,7 @@ kvattn_status kvattn_plan_update(kvattn_plan_t plan, const int32_t* block_tables
     // the device copy of the schedule is stale until the next upload
     plan->dev_ws = nullptr;
     plan->dev_bytes = 0;
+    plan->generation = next_generation();
     plan->stats.update_path = path;
     plan->stats.plan_seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
     return KVATTN_OK;

@@ -1,6 +1,7 @@
 // Host-side plan object and error helpers (no HIP dependency).
 #pragma once
 
+#include <cstdint>
 #include <string>
 #include <vector>
 
@@ -43,9 +44,14 @@ struct kvattn_plan_s {
     void (*upload_wait)(void* event) = nullptr;
     void* dev_ws = nullptr;                 // bound device workspace (caller-owned)
     size_t dev_bytes = 0;
+    // Distinct for every plan and every state of a plan (kvattn_plan and each
+    // kvattn_plan_update draw a new one): kvattn_decode_noalloc copies the blob
+    // into its device's static scratch only when the scratch holds another one.
+    uint64_t generation = 0;
 };
 
 namespace kvattn {
 kvattn_status set_error(kvattn_status s, const std::string& msg);
 void clear_error();
+uint64_t next_generation();   // process-wide counter, starts at 1
 }  // namespace kvattn

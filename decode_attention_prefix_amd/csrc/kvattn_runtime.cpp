@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "kvattn_plan.hpp"
@@ -11,8 +12,11 @@
 namespace kvattn {
 namespace {
 
-DevPlan resolve(const kvattn_plan_s& P, int launch) {
-    auto* base = static_cast<unsigned char*>(P.dev_ws);
+// Device pointers of the plan's workspace sections at `ws` (the bound workspace,
+// or the static scratch of kvattn_decode_noalloc), for forward launch `launch`
+// (-1: the merge).
+DevPlan resolve(const kvattn_plan_s& P, int launch, void* ws) {
+    auto* base = static_cast<unsigned char*>(ws);
     const BlobHeader& h = P.header;
     DevPlan d;
     d.desc = reinterpret_cast<const int32_t*>(base + h.off_desc);
@@ -49,7 +53,8 @@ kvattn_status check_bound(kvattn_plan_t plan) {
 }
 
 kvattn_status run_forward(const void* q, const void* k, const void* v, kvattn_plan_t plan, float* out,
-                          void* stream, void* side_stream = nullptr) {
+                          void* stream, void* side_stream = nullptr, void* ws = nullptr) {
+    if (!ws) ws = plan->dev_ws;
     if (!q || !k || !v || !out) return set_error(KVATTN_EINVAL, "q, k_cache, v_cache or out is NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return set_error(KVATTN_EINVAL, "q, k_cache, v_cache and out must be 16-byte aligned");
@@ -57,7 +62,7 @@ kvattn_status run_forward(const void* q, const void* k, const void* v, kvattn_pl
     // Each launch drains its queues of MFMA and VALU tasks; launches (normally
     // one) follow each other on `stream`.
     for (const Launch& L : plan->forward_launches) {
-        const DevPlan dp = resolve(*plan, L.index);
+        const DevPlan dp = resolve(*plan, L.index, ws);
         void* s = L.side && side_stream ? side_stream : stream;
         const int rc = launch_forward(dp, d, L.valu_rows, L.mfma_tiles, L.n_tasks, static_cast<const uint16_t*>(q),
                                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), out, s);
@@ -67,16 +72,20 @@ kvattn_status run_forward(const void* q, const void* k, const void* v, kvattn_pl
     return KVATTN_OK;
 }
 
-kvattn_status run_merge(kvattn_plan_t plan, float* out, void* stream) {
+kvattn_status run_merge(kvattn_plan_t plan, float* out, void* stream, void* ws = nullptr) {
     if (!out) return set_error(KVATTN_EINVAL, "out is NULL");
     if (plan->opts.new_token)
         return set_error(KVATTN_EINVAL, "the plan takes each query's newest token from the call: use kvattn_decode_append");
-    const DevPlan dp = resolve(*plan, -1);
+    const DevPlan dp = resolve(*plan, -1, ws ? ws : plan->dev_ws);
     const Dims d = dims(*plan);
     const int rc = launch_merge(dp, d, int(plan->merge_query.size()), out, stream);
     if (rc != 0) return set_error(KVATTN_EHIP, std::string("merge launch failed: ") + hipGetErrorString(hipError_t(rc)));
     return KVATTN_OK;
 }
+
+// Generation of the plan whose blob each device's static scratch holds (0: none).
+std::mutex g_scratch_mu;
+uint64_t g_scratch_generation[kMaxDevices] = {};
 
 }  // namespace
 }  // namespace kvattn
@@ -165,7 +174,7 @@ kvattn_status kvattn_decode_append(const void* q, const void* k_new, const void*
     // the forward reads the cached parts only; the merge adds the new tokens and writes them into the cache
     s = run_forward(q, k_cache, v_cache, plan, out, stream);
     if (s != KVATTN_OK) return s;
-    const DevPlan dp = resolve(*plan, -1);
+    const DevPlan dp = resolve(*plan, -1, plan->dev_ws);
     const Dims d = dims(*plan);
     NewTokens nt;
     nt.q = static_cast<const uint16_t*>(q);
@@ -176,6 +185,55 @@ kvattn_status kvattn_decode_append(const void* q, const void* k_new, const void*
     const int rc = launch_merge_append(dp, d, int(plan->merge_query.size()), nt, out, stream);
     if (rc != 0) return set_error(KVATTN_EHIP, std::string("merge launch failed: ") + hipGetErrorString(hipError_t(rc)));
     return KVATTN_OK;
+}
+
+kvattn_status kvattn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, kvattn_plan_t plan,
+                                    float* out, void* stream) {
+    using namespace kvattn;
+    clear_error();
+    if (!plan) return set_error(KVATTN_EINVAL, "plan is NULL");
+    if (plan->opts.new_token)
+        return set_error(KVATTN_EINVAL, "the plan takes each query's newest token from the call: use kvattn_decode_append");
+    if (plan->header.total_bytes > kNoallocScratchBytes)
+        return set_error(KVATTN_EWORKSPACE, "the plan needs " + std::to_string(plan->header.total_bytes) +
+                                                " bytes of workspace; the static scratch holds " +
+                                                std::to_string(kNoallocScratchBytes) + ": use kvattn_decode");
+    void* ws = nullptr;
+    int rc = scratch_device_pointer(&ws);
+    if (rc != 0) return set_error(KVATTN_EHIP, std::string("scratch lookup failed: ") + hipGetErrorString(hipError_t(rc)));
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return set_error(KVATTN_EHIP, std::string("device query failed: ") + hipGetErrorString(e));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (g_scratch_generation[dev] != plan->generation) {
+            // stage this plan's schedule (its claim counter zeroed) in the scratch
+            hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+            e = hipStreamIsCapturing(s, &cap);
+            if (e != hipSuccess) return set_error(KVATTN_EHIP, std::string("stream query failed: ") + hipGetErrorString(e));
+            if (cap != hipStreamCaptureStatusNone)
+                return set_error(KVATTN_EINVAL, "the plan is not staged in this device's scratch: call once before capturing");
+            if (!plan->upload_event) {
+                hipEvent_t ev = nullptr;
+                e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+                if (e != hipSuccess) return set_error(KVATTN_EHIP, std::string("event creation failed: ") + hipGetErrorString(e));
+                plan->upload_event = ev;
+                plan->upload_wait = wait_upload_event;
+            }
+            e = hipMemcpyAsync(ws, plan->blob.data(), plan->blob.size(), hipMemcpyHostToDevice, s);
+            if (e != hipSuccess) return set_error(KVATTN_EHIP, std::string("staging copy failed: ") + hipGetErrorString(e));
+            e = hipEventRecord(static_cast<hipEvent_t>(plan->upload_event), s);
+            if (e != hipSuccess) {
+                (void)hipStreamSynchronize(s);
+                return set_error(KVATTN_EHIP, std::string("event record failed: ") + hipGetErrorString(e));
+            }
+            g_scratch_generation[dev] = plan->generation;
+        }
+    }
+    kvattn_status st = run_forward(q, k_cache, v_cache, plan, out, stream, nullptr, ws);
+    if (st != KVATTN_OK) return st;
+    return run_merge(plan, out, stream, ws);
 }
 
 kvattn_status kvattn_read_probe(const void* a, size_t a_bytes, const void* b, size_t b_bytes, void* sink,

@@ -88,7 +88,7 @@ def _load():
     lib.kvattn_plan_device_bytes.restype = ctypes.c_int
     lib.kvattn_plan_upload.argtypes = [vp, vp, ctypes.c_size_t, vp]
     lib.kvattn_plan_upload.restype = ctypes.c_int
-    for name in ("kvattn_decode", "kvattn_forward"):
+    for name in ("kvattn_decode", "kvattn_forward", "kvattn_decode_noalloc"):
         getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, vp]
         getattr(lib, name).restype = ctypes.c_int
     lib.kvattn_decode_streams.argtypes = [vp, vp, vp, vp, vp, vp, vp]
@@ -114,7 +114,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("kvattn_plan_options_default", "kvattn_plan", "kvattn_plan_device_bytes", "kvattn_plan_upload",
-            "kvattn_decode", "kvattn_decode_append", "kvattn_decode_streams", "kvattn_forward", "kvattn_merge", "kvattn_plan_update",
+            "kvattn_decode", "kvattn_decode_append", "kvattn_decode_streams", "kvattn_decode_noalloc", "kvattn_forward", "kvattn_merge", "kvattn_plan_update",
             "kvattn_expand_query_tokens", "kvattn_plan_stats", "kvattn_plan_export", "kvattn_plan_destroy",
             "kvattn_read_probe", "kvattn_status_string", "kvattn_last_error")
 
@@ -239,6 +239,12 @@ def kvattn_plan_upload(plan: Plan, workspace, nbytes: Optional[int] = None, stre
 def kvattn_decode(q, k_cache, v_cache, plan: Plan, out, stream=None):
     _check(_lib.kvattn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), plan.handle, _ptr(out), _stream(stream)),
            "kvattn_decode")
+
+
+def kvattn_decode_noalloc(q, k_cache, v_cache, plan: Plan, out, stream=None):
+    """kvattn_decode on the library's static per-device scratch: no workspace, no upload, no allocation."""
+    _check(_lib.kvattn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), plan.handle, _ptr(out),
+                                      _stream(stream)), "kvattn_decode_noalloc")
 
 
 def kvattn_decode_streams(q, k_cache, v_cache, plan: Plan, out, side_stream, stream=None):

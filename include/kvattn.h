@@ -377,6 +377,32 @@ kvattn_status kvattn_decode_append(const void* q, const void* k_new, const void*
 kvattn_status kvattn_decode_streams(const void* q, const void* k_cache, const void* v_cache, kvattn_plan_t plan,
                                     float* out, void* stream, void* side_stream);
 
+/*
+ * kvattn_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * plan, same kernels and same result as kvattn_decode, but the workspace
+ * (schedule blob + partial triples) is a static device array of the library,
+ * 64 MiB per device, that every GPU the library runs on holds from the first
+ * call on it until the process ends; no kvattn_plan_upload or caller workspace
+ * is needed.  The call copies the plan's schedule into the array only when the
+ * array holds another plan's (or another state's: each kvattn_plan_update makes
+ * a new one), so repeated calls with one plan (every layer of a decode step)
+ * copy nothing; that copy reads the plan's host blob like kvattn_plan_upload
+ * and is ordered against kvattn_plan_update / destroy the same way.  A copy
+ * cannot be captured: under stream capture the plan must already be staged by
+ * an earlier call on the device.  The array keeps the last call's contents
+ * (the claim counter returns to zero at the end of every launch), and all
+ * calls on one GPU share it: calls that overlap on one GPU (other streams,
+ * other threads) race and give wrong results.  Nothing is allocated: no
+ * hipMalloc, hipFree or allocating library call (the first call with a plan
+ * that was never uploaded creates its host-side upload event).
+ * Errors: EINVAL (NULL, plan made with new_token, capture with the plan not
+ * staged), EWORKSPACE (the plan's kvattn_plan_device_bytes exceed 64 MiB:
+ * use kvattn_decode), EHIP.
+ */
+kvattn_status kvattn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, kvattn_plan_t plan,
+                                    float* out, void* stream);
+
 /* The forward stage of kvattn_decode alone (PAT review, forward stage). */
 kvattn_status kvattn_forward(const void* q, const void* k_cache, const void* v_cache, kvattn_plan_t plan,
                              float* out, void* stream);
