@@ -1,8 +1,16 @@
 """Build libkvattn.so in-tree: host planner (g++), HIP runtime glue and gfx950 kernels (hipcc).
 
-Usage: python -m decode_attention_prefix_amd.build   (or build() from Python)
+Usage: python -m decode_attention_prefix_amd.build [--sanitize]   (or build() from Python)
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
 selection turned off (-Xclang -target-feature -Xclang -packed-fp32-ops).
+
+build(sanitize=True) makes a checking variant for host tests only,
+_build/san/libkvattn.so: the host planner (the part that indexes caller
+tables, trees and lengths) is compiled by g++ with AddressSanitizer and
+UndefinedBehaviorSanitizer (any report aborts), linked by g++ with the
+unchanged runtime and kernel objects.  Load it with KVATTN_LIBRARY pointing at
+it and libasan / libubsan preloaded (tests/test_sanitized_planner.py does).
+It never runs on a GPU: the sanitizers cover host code only.
 """
 from __future__ import annotations
 
@@ -28,7 +36,34 @@ def _run(cmd):
     subprocess.check_call(cmd)
 
 
-def build(verbose_isa: bool = False) -> str:
+SAN_DIR = os.path.join(BUILD, "san")
+SAN_LIB = os.path.join(SAN_DIR, "libkvattn.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized() -> str:
+    """The host planner under ASan + UBSan, linked with the regular runtime and kernel objects
+    (rebuilt first when missing or older than their sources)."""
+    objs = [os.path.join(BUILD, n) for n in ("kvattn_runtime.o", "kvattn_kernels.o")]
+    newest_src = max(os.path.getmtime(os.path.join(d, f)) for d in (CSRC, INCLUDE) for f in os.listdir(d))
+    if not all(os.path.exists(o) and os.path.getmtime(o) >= newest_src for o in objs):
+        build()
+    os.makedirs(SAN_DIR, exist_ok=True)
+    plan_o = os.path.join(SAN_DIR, "kvattn_plan_san.o")
+    _run(["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-Wall", "-Wextra", *SAN_FLAGS, "-I", INCLUDE, "-c",
+          os.path.join(CSRC, "kvattn_plan.cpp"), "-o", plan_o])
+    rocm_lib = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
+    tmp = SAN_LIB + ".tmp%d" % os.getpid()
+    _run(["g++", "-shared", *SAN_FLAGS, plan_o, os.path.join(BUILD, "kvattn_runtime.o"),
+          os.path.join(BUILD, "kvattn_kernels.o"), "-L", rocm_lib, "-Wl,-rpath," + rocm_lib, "-lamdhip64",
+          "-o", tmp])
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
+def build(verbose_isa: bool = False, sanitize: bool = False) -> str:
+    if sanitize:
+        return build_sanitized()
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     plan_o = os.path.join(BUILD, "kvattn_plan.o")
@@ -53,4 +88,4 @@ def build(verbose_isa: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose_isa="--isa" in sys.argv)
+    build(verbose_isa="--isa" in sys.argv, sanitize="--sanitize" in sys.argv)

@@ -16,7 +16,9 @@ from typing import Optional
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvattn.so")
+# KVATTN_LIBRARY selects another build of the library (the sanitized host-test
+# variant); by default the in-tree build next to this file is loaded.
+LIB_PATH = os.environ.get("KVATTN_LIBRARY") or os.path.join(_PKG, "libkvattn.so")
 
 KVATTN_OK, KVATTN_EINVAL, KVATTN_EUNSUPPORTED, KVATTN_ENOMEM, KVATTN_EWORKSPACE, KVATTN_EHIP, KVATTN_ESTATE = range(7)
 KVATTN_PACK_AUTO, KVATTN_PACK_QUERY, KVATTN_PACK_FULL = 0, 1, 2

@@ -49,6 +49,8 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
     import shutil
     import sys
     shutil.copy(os.path.join(ROOT, "decode_attention_prefix_amd", "kvattn.py"), str(tmp_path / "kvattn.py"))
-    r = subprocess.run([sys.executable, "-c", "import kvattn"], cwd=str(tmp_path), capture_output=True, text=True)
+    env = {k: v for k, v in os.environ.items() if k != "KVATTN_LIBRARY"}
+    r = subprocess.run([sys.executable, "-c", "import kvattn"], cwd=str(tmp_path), capture_output=True, text=True,
+                       env=env)
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "libkvattn.so is not built" in r.stderr
