@@ -401,7 +401,7 @@ def measure(c, args, torch, K, W, steps, warmup, extras_on):
     wl = W.WORKLOADS[c]().materialize()
     log("bench: %s generated in %.1f s; unique KV %.1f MB" % (wl.name, time.perf_counter() - t_gen,
                                                               wl.unique_kv_bytes / 1e6))
-    opts = K.make_options(pack_mode=args.pack_mode, split_tokens=args.split_tokens)
+    opts = K.make_options(pack_mode=args.pack_mode, split_tokens=args.split_tokens, fused_merge=args.fused_merge)
     # the device is initialised before this point: plan_upload_ms covers planning,
     # the workspace allocation and the upload copy only
     torch.cuda.synchronize()
@@ -566,6 +566,8 @@ def main():
     ap.add_argument("--config", default="all", choices=["all", "1", "2", "3", "4", "5"])
     ap.add_argument("--pack-mode", type=int, default=0)
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--fused-merge", type=int, default=-1, choices=[-1, 0, 1],
+                    help="plan option fused_merge: -1 auto, 0 merge launch, 1 merge inside the forward launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=8.0, help="wall seconds of oracle work per workload")
     ap.add_argument("--no-check", action="store_true")

@@ -35,7 +35,7 @@ constexpr int kMfmaMaxItemBlocks = 1408;  // KV blocks per MFMA item (22528 toke
 constexpr int kMaxGroup = 64;           // q heads per KV head supported
 constexpr int kXcds = 8;                // XCDs of an MI355X (L2 domains)
 constexpr uint32_t kBlobMagic = 0x4B564154u;  // "KVAT"
-constexpr uint32_t kBlobVersion = 8;
+constexpr uint32_t kBlobVersion = 9;
 
 // Device view of one item; identical layout to kvattn_item_info.
 struct Item {
@@ -66,8 +66,9 @@ struct Task {
 };
 
 // Task descriptor (device, int32 words, 16-byte aligned): a kDescHeader-word
-// header, n_q entries of 4 words (query, dest, limit, 0), then the item's
-// block ids, padded to a multiple of 4 words.
+// header, n_q entries of 4 words (query, dest, limit, merge record index of the
+// query, or -1 for a row written directly), then the item's block ids, padded
+// to a multiple of 4 words.
 enum : int {
     kDescKind = 0,        // KVATTN_VARIANT_VALU / _MFMA
     kDescTile = 1,        // VALU rows template; MFMA 16-row tiles per wave
@@ -100,6 +101,7 @@ struct BlobHeader {
     uint64_t off_list_ptr;    // int32 [n_launches][n_lists][3]: word offsets (MFMA begin, VALU begin, end) per list
     uint64_t off_merge_rec;   // int32 [n_merge_q][4]: (query, first slot, partials, 0); partial k at first + k Hq
     uint64_t off_claim;       // int32: list claim counter, zero between launches
+    uint64_t off_arrive;      // int32 [n_merge_q][Hkv]: fused-merge arrival counters, zero between launches
     uint64_t blob_bytes;      // bytes copied by kvattn_plan_upload
     uint64_t off_part_ml;     // float2 [n_slots]: (m in log2 units, l)
     uint64_t off_part_acc;    // float [n_slots][head_dim]
@@ -147,6 +149,11 @@ struct DevPlan {
     int32_t* claim;             // list claim counter (zero between launches)
     float* part_ml;
     float* part_acc;
+    // Fused merge (plans with fused_merge): arrival counter of each (merge record,
+    // KV head), zero between launches; NULL when a merge launch follows the forward.
+    int32_t* arrive;
+    uint32_t part_ml_bytes;     // bytes of part_ml and part_acc (< 4 GiB when fused)
+    uint32_t part_acc_bytes;
 };
 
 struct Dims {

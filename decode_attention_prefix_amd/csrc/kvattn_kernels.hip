@@ -156,6 +156,38 @@ __device__ __forceinline__ u32x4 raw_rsrc(const void* base, uint32_t bytes) {
     return r;
 }
 
+// Agent-scope coherent (sc1) stores and loads of partial triples, for plans
+// that merge inside the forward launch: a partial written on one XCD is read
+// by the task that completes its (query, KV head) on any other XCD, so it must
+// neither stay in the writer's L2 nor be served stale from the reader's.
+// `rsrc` spans a whole partial array (< 4 GiB, checked by the planner); `off`
+// is a byte offset.  Cache policy 16 is sc1 on gfx950.
+constexpr int kCpolSc1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const float* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, int(bytes), kBufferWord3);
+}
+__device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off, float a) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), r, off, 0, kCpolSc1);
+}
+__device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off, float2 a) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(a.x), __float_as_uint(a.y)}, r, off, 0, kCpolSc1);
+}
+__device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 a) {
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w)}, r, off, 0,
+        kCpolSc1);
+}
+__device__ __forceinline__ float2 load_sc1_f2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolSc1);
+    return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
+}
+__device__ __forceinline__ float4 load_sc1_f4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+
 // Buffer -> LDS copy of 16 bytes per lane: lane i reads bytes [voff, voff + 16)
 // of the resource and writes LDS bytes [lds + 16 i, lds + 16 i + 16); dwords
 // past the resource's size are written as zeros.  Inline assembly for the same
@@ -220,6 +252,91 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     v.x = (__bf16)a;
     v.y = (__bf16)b;
     return __builtin_bit_cast(uint32_t, v);
+}
+
+// ============================================================================
+// Online-softmax combination of a (query, q head) row's partial triples (PAT
+// review, merge stage), for the four consecutive head-dim values at offset e0
+// of the head: partial k sits in slot slot0 + k Hq.  Updates the running
+// (M, L, A) in place, partials read BATCH at a time with every load in flight
+// (the batch size groups the loads only; the arithmetic is the same):
+//   M' = max(M, m_k);  A = A 2^(M - M') + 2^(m_k - M') acc_k;  L likewise with l_k.
+// SC1 reads with agent-scope coherent loads (the forward's own merges).  Both
+// the merge launch and the forward's merges use this one function, so a row
+// comes out bit for bit the same either way.
+// ============================================================================
+template <int D, bool SC1, int BATCH>
+__device__ __forceinline__ void merge_partials(const DevPlan& p, int Hq, size_t slot0, int n, int e0, float& M,
+                                               float& L, float4& A) {
+    const __amdgpu_buffer_rsrc_t rml = part_rsrc(p.part_ml, p.part_ml_bytes);
+    const __amdgpu_buffer_rsrc_t racc = part_rsrc(p.part_acc, p.part_acc_bytes);
+    for (int ib = 0; ib < n; ib += BATCH) {
+        float2 ml[BATCH];
+        float4 ac[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            const size_t slot = slot0 + size_t(min(ib + j, n - 1)) * Hq;
+            if constexpr (SC1) {
+                ml[j] = load_sc1_f2(rml, uint32_t(slot * 8));
+                ac[j] = load_sc1_f4(racc, uint32_t((slot * D + e0) * 4));
+            } else {
+                ml[j] = *reinterpret_cast<const float2*>(p.part_ml + slot * 2);
+                ac[j] = *reinterpret_cast<const float4*>(p.part_acc + slot * D + e0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            // past the row's last partial: no change (weight 0, same max)
+            const float mj = ib + j < n ? ml[j].x : -INFINITY;
+            const float Mn = fmaxf(M, mj);
+            const float so = fast_exp2(M - Mn);     // 0 while M is -inf
+            const float sn = fast_exp2(mj - Mn);    // 0 past the last partial
+            L = L * so + sn * ml[j].y;
+            A.x = fmaf(sn, ac[j].x, A.x * so);
+            A.y = fmaf(sn, ac[j].y, A.y * so);
+            A.z = fmaf(sn, ac[j].z, A.z * so);
+            A.w = fmaf(sn, ac[j].w, A.w * so);
+            M = Mn;
+        }
+    }
+}
+
+// One wave merges the q heads of KV head g of merge record `rec` (wave-uniform)
+// into out: that query's G rows, 256 floats per pass.
+template <int D>
+__device__ __forceinline__ void merge_unit(const DevPlan& p, const Dims& dm, int rec, int g, float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int Hq = dm.num_q_heads;
+    const KV_CONST MergeRec* r = cptr(p.merge_rec) + rec;
+    const int b = r->query, n = r->count;
+    const size_t first = size_t(r->first);
+    const int cols = dm.group * D;
+    for (int c0 = 0; c0 < cols; c0 += 256) {
+        const int cc = c0 + 4 * lane;
+        if (cc < cols) {
+            const int col = g * cols + cc;
+            const int h = col / D;
+            float M = -INFINITY, L = 0.f;
+            float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+            merge_partials<D, true, 16>(p, Hq, first + h, n, col - h * D, M, L, A);
+            const float inv = 1.f / L;
+            *reinterpret_cast<float4*>(out + size_t(b) * Hq * D + col) =
+                make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
+        }
+    }
+}
+
+// Arrival of one task's partials of KV head g for the merge record `rec` (one
+// lane): returns true for the task that completes the (record, head), which
+// then merges it.  Its counter goes back to zero for the next launch.  The
+// caller has waited for its own sc1 partial stores (s_waitcnt vmcnt(0)).
+__device__ __forceinline__ bool arrive_last(const DevPlan& p, int Hkv, int rec, int g) {
+    int* c = p.arrive + size_t(rec) * Hkv + g;
+    const int n = p.merge_rec[rec].count;
+    const int old = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old != n - 1) return false;
+    __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
 }
 
 // ============================================================================
@@ -498,6 +615,18 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
                 } else {
                     o[0] = acc[r][0] * inv;
                 }
+            } else if (p.arrive) {
+                // merged in this launch, possibly on another XCD: agent-scope coherent stores
+                const size_t sl = size_t(e.y) + h;
+                const __amdgpu_buffer_rsrc_t racc = part_rsrc(p.part_acc, p.part_acc_bytes);
+                const uint32_t o = uint32_t((sl * D + d0) * 4);
+                if constexpr (NE / 8 == 2) {
+                    store_sc1(racc, o, make_float2(acc[r][0], acc[r][1]));
+                } else {
+                    store_sc1(racc, o, acc[r][0]);
+                }
+                if (lane == 0)
+                    store_sc1(part_rsrc(p.part_ml, p.part_ml_bytes), uint32_t(sl * 8), make_float2(mrow[r], ltot[r]));
             } else {
                 const size_t sl = size_t(e.y) + h;
                 float* o = p.part_acc + sl * D + d0;
@@ -553,6 +682,43 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
         }
     }
     flush();
+
+    // Fused merge: the stream's partial stores are complete (sc1: performed at
+    // agent scope) before its arrivals; the task completing a (query, KV head)
+    // merges it.  Arrivals come at the end of the stream, where waiting for
+    // every outstanding store costs nothing.
+    if (p.arrive) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
+        __builtin_amdgcn_sched_barrier(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        // the stream's partial entries go to lanes in order, up to 64 arrivals
+        // in flight at once; then the units this wave completed are merged
+        int my_rec = -1, my_g = 0, na = 0;
+        auto arrive_batch = [&]() {
+            const bool last = my_rec >= 0 && arrive_last(p, Hkv, my_rec, my_g);
+            uint64_t mask = __ballot(last);
+            while (mask) {
+                const int i = __builtin_ctzll(mask);
+                mask &= mask - 1;
+                merge_unit<D>(p, dm, __builtin_amdgcn_readlane(my_rec, i), __builtin_amdgcn_readlane(my_g, i), out);
+            }
+            my_rec = -1;
+        };
+        for (int off = skip(0); off < n_words; off = skip(off + hdr(off, kDescWords))) {
+            const int nq = hdr(off, kDescNq);
+            const int g = hdr(off, kDescHead) + wave;
+            for (int e = 0; e < nq; ++e) {
+                const int dest = hdr(off, kDescHeader + 4 * e + 1);
+                if (dest < 0) continue;
+                if (lane == (na & 63)) {
+                    my_rec = win[off + kDescHeader + 4 * e + 3];
+                    my_g = g;
+                }
+                if ((++na & 63) == 0) arrive_batch();
+            }
+        }
+        if (na & 63) arrive_batch();
+    }
 }
 
 // ============================================================================
@@ -842,6 +1008,18 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
         if (r >= it.n_rows) continue;
         const Entry e = entry_of(it, r / G);
         const int h = g * G + r % G;
+        if (e.dest >= 0 && p.arrive) {
+            // merged in this launch, possibly on another XCD: agent-scope coherent stores
+            const size_t slot = size_t(e.dest) + h;
+            if (lg == 0)
+                store_sc1(part_rsrc(p.part_ml, p.part_ml_bytes), uint32_t(slot * 8), make_float2(mref[rt], lt));
+            const __amdgpu_buffer_rsrc_t racc = part_rsrc(p.part_acc, p.part_acc_bytes);
+#pragma unroll
+            for (int j = 0; j < NDT; ++j)
+                store_sc1(racc, uint32_t((slot * D + 16 * j + 4 * lg) * 4),
+                          make_float4(acc[rt][j][0], acc[rt][j][1], acc[rt][j][2], acc[rt][j][3]));
+            continue;
+        }
         float* dst;
         float scale;
         if (e.dest < 0) {
@@ -888,6 +1066,26 @@ __device__ __forceinline__ void wait_all_and_sync() {
     __syncthreads();
 }
 
+// Fused merge after an MFMA task (every wave's partial stores complete): one
+// arrival per query entry on the task's KV head; the waves merge the
+// (query, KV head) units this task completed.
+template <int D>
+__device__ __forceinline__ void mfma_arrivals(const DevPlan& p, const Dims& dm, const TaskView& it,
+                                              float* __restrict__ out, int* s_last, int* s_nlast) {
+    const int g = it.head;
+    if (threadIdx.x == 0) *s_nlast = 0;
+    __syncthreads();
+    for (int e = threadIdx.x; e < it.n_q; e += 64 * kWaves) {
+        const int4 en = *reinterpret_cast<const int4*>(it.ent + 4 * e);
+        if (en.y >= 0 && arrive_last(p, dm.num_kv_heads, en.w, g)) s_last[atomicAdd(s_nlast, 1)] = en.w;
+    }
+    __syncthreads();
+    const int nl = __builtin_amdgcn_readfirstlane(*s_nlast);
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+    for (int i = wave; i < nl; i += kWaves) merge_unit<D>(p, dm, __builtin_amdgcn_readfirstlane(s_last[i]), g, out);
+    __syncthreads();   // s_last is free for the next task
+}
+
 template <int D, int R, int TPW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fwd_kernel(
     DevPlan p, Dims dm, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
@@ -898,7 +1096,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     static_assert(KV_ELEMS * 2 == WIN * 4 + kWaves * 4 * R * D * 2, "VALU window layout");
     __shared__ __attribute__((aligned(16))) uint16_t s_kv[KV_ELEMS];
     __shared__ __attribute__((aligned(16))) int32_t s_desc[2][kDescMaxWords];
-    static_assert(D != 128 || KV_ELEMS * 2 + sizeof(s_desc) + 64 <= 80 * 1024, "two workgroups per CU");
+    __shared__ int s_last[kMaxItemQueries + 1];   // fused merge: units an MFMA task completed, and their count
+    static_assert(D != 128 || KV_ELEMS * 2 + sizeof(s_desc) + sizeof(s_last) + 64 <= 80 * 1024,
+                  "two workgroups per CU");
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     // All control flow below is wave-uniform: the loops hold barriers, so
     // lane-divergent branches must stay out of their exits and back edges.
@@ -934,6 +1134,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
                 const TaskView it = view_of(d);
                 mfma_task<D, TPW>(p, dm, it, it.head, q, kc, vc, out, s_kv);
                 wait_all_and_sync();   // the prefetched descriptor landed; this task's LDS is free
+                if (p.arrive) mfma_arrivals<D>(p, dm, it, out, s_last, s_last + kMaxItemQueries);
                 if (noff >= v0) break;
                 off = noff;
                 buf ^= 1;
@@ -976,7 +1177,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 // ============================================================================
 template <int D, bool NEW>
 __global__ __launch_bounds__(64) void merge_kernel(DevPlan p, Dims dm, NewTokens nt, float* __restrict__ out) {
-    constexpr int BATCH = 8;
     const int Hq = dm.num_q_heads;
     const int mq = blockIdx.x;
     const int col = int(blockIdx.y) * 256 + 4 * int(threadIdx.x);   // float index in [Hq][D]
@@ -1007,30 +1207,7 @@ __global__ __launch_bounds__(64) void merge_kernel(DevPlan p, Dims dm, NewTokens
             *reinterpret_cast<uint2*>(nt.v_cache + at) = vw;
         }
     }
-    for (int ib = 0; ib < n; ib += BATCH) {
-        float2 ml[BATCH];
-        float4 ac[BATCH];
-#pragma unroll
-        for (int j = 0; j < BATCH; ++j) {
-            const size_t slot = slot0 + size_t(min(ib + j, n - 1)) * Hq;
-            ml[j] = *reinterpret_cast<const float2*>(p.part_ml + slot * 2);
-            ac[j] = *reinterpret_cast<const float4*>(p.part_acc + slot * D + (col - h * D));
-        }
-#pragma unroll
-        for (int j = 0; j < BATCH; ++j) {
-            // past the query's last partial: no change (weight 0, same max)
-            const float mj = ib + j < n ? ml[j].x : -INFINITY;
-            const float Mn = fmaxf(M, mj);
-            const float so = fast_exp2(M - Mn);     // 0 while M is -inf
-            const float sn = fast_exp2(mj - Mn);    // 0 past the last partial
-            L = L * so + sn * ml[j].y;
-            A.x = fmaf(sn, ac[j].x, A.x * so);
-            A.y = fmaf(sn, ac[j].y, A.y * so);
-            A.z = fmaf(sn, ac[j].z, A.z * so);
-            A.w = fmaf(sn, ac[j].w, A.w * so);
-            M = Mn;
-        }
-    }
+    merge_partials<D, false, 8>(p, Hq, slot0, n, col - h * D, M, L, A);
     const float inv = 1.f / L;
     *reinterpret_cast<float4*>(out + size_t(b) * Hq * D + col) = make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
 }

@@ -331,6 +331,7 @@ int32_t put_desc(kvattn_plan_s& P, const Task& t) {
         d[kDescHeader + 4 * e + 0] = en.query;
         d[kDescHeader + 4 * e + 1] = en.dest;
         d[kDescHeader + 4 * e + 2] = en.limit;
+        d[kDescHeader + 4 * e + 3] = en.dest >= 0 ? P.rec_of_query[size_t(en.query)] : -1;
     }
     int32_t* blk = d + kDescHeader + 4 * it.n_q;
     for (int j = 0; j < nblk; ++j) blk[j] = P.block_ids[size_t(it.blk_begin + j)];
@@ -397,6 +398,8 @@ void serialize_blob(kvattn_plan_s& P) {
     h.off_list_ptr = off;     off = align256(off + P.desc_list_ptr.size() * 4);
     h.off_merge_rec = off;    off = align256(off + P.merge_rec.size() * 4);
     h.off_claim = off;        off = align256(off + 2 * 4);   // one counter per stream
+    h.off_arrive = off;
+    if (P.fused_merge) off = align256(off + uint64_t(P.merge_query.size()) * uint64_t(P.shape.num_kv_heads) * 4);
     h.blob_bytes = off;
     h.off_part_ml = off;      off = align256(off + uint64_t(P.n_slots) * 8);
     h.off_part_acc = off;     off = align256(off + uint64_t(P.n_slots) * uint64_t(P.shape.head_dim) * 4);
@@ -644,7 +647,9 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     auto stripe_list = [&](int s, int q) {
         return xcd_stripes ? (s / kXcds) * kXcds * quads + s % kXcds + kXcds * q : s * quads + q;
     };
-    auto stripe_rate = [&](int s) { return (stripe_list(s, 0) % kXcds) % 2 ? kOddXcdRate : 1.0; };
+    // relative streaming rate of list w (odd XCDs are slower)
+    auto list_rate = [&](int w) { return (w % kXcds) % 2 ? kOddXcdRate : 1.0; };
+    auto stripe_rate = [&](int s) { return list_rate(stripe_list(s, 0)); };
     const double pu_mfma = (kPartialWriteCostMfma + 1.0) * double(partial_row_bytes) / double(2 * D * 2);
     auto mfma_cost = [&](const Group& g, int64_t tok) { return double(tok) * g.w + kMfmaTaskCost; };
     auto unit_tokens = [&](const Group& g) { return units[g.unit].tokens; };
@@ -721,6 +726,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             // the least of the XCD minima
             using LE = std::pair<double, int>;
             using Heap = std::priority_queue<LE, std::vector<LE>, std::greater<LE>>;
+            // keys are times: a list's load divided by its rate
             std::vector<Heap> heap_x(kXcds);
             for (int w = 0; w < n_lists; ++w) heap_x[size_t(w % kXcds)].push({0.0, w});
             for (const T& t : tasks) {
@@ -735,7 +741,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
                 heap_x[size_t(x)].pop();
                 mp.pieces[size_t(t.piece)].head_list[size_t(t.head)] = w;
                 mp.load[size_t(w)] += t.cost;
-                heap_x[size_t(x)].push({mp.load[size_t(w)], w});
+                heap_x[size_t(x)].push({mp.load[size_t(w)] / list_rate(w), w});
             }
             return mp;
         };
@@ -790,7 +796,8 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             if (!tried.insert(key).second) continue;
             MfmaPlan mp = place_mfma(target);
             const std::vector<double> base = stripe_base(mp.load);
-            double makespan = *std::max_element(mp.load.begin(), mp.load.end());
+            double makespan = 0.0;
+            for (int w = 0; w < n_lists; ++w) makespan = std::max(makespan, mp.load[size_t(w)] / list_rate(w));
             if (!vg.empty()) makespan = std::max(makespan, fill_level(base, valu_work));
             const double score = makespan + mp.extra / (double(n_lists) * kWaves);
             if (!have || score < best_score * 0.995) {
@@ -966,6 +973,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     P.merge_dest.clear();
     P.merge_ptr.assign(1, 0);
     P.merge_rec.clear();
+    P.rec_of_query.assign(size_t(B), -1);
     int direct_rows = 0;
     for (int b = 0; b < B; ++b) {
         if (count[b] < min_merged && !o.new_token) {
@@ -973,9 +981,23 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             continue;
         }
         P.merge_rec.insert(P.merge_rec.end(), {b, std::max(slot_base[b], 0), count[b], o.new_token ? new_slot[size_t(b)] : 0});
+        P.rec_of_query[size_t(b)] = int32_t(P.merge_query.size());
         P.merge_query.push_back(b);
         P.merge_dest.insert(P.merge_dest.end(), dests[b].begin(), dests[b].end());
         P.merge_ptr.push_back(int32_t(P.merge_dest.size()));
+    }
+
+    // ---- fused merge: the forward's last task of each (query, KV head) merges ----------------
+    // Not with a new token (its merge also scores the token and writes the cache)
+    // or with concurrent multi-stream launches; the kernels address the partials
+    // with 32-bit byte offsets.
+    {
+        const bool eligible = !o.new_token && !o.multi_stream && !P.merge_query.empty() &&
+                              uint64_t(slots_used) * uint64_t(D) * 4 < (uint64_t(1) << 32);
+        // measured on MI355X: merging in the forward is slower on every workload here
+        // (the last arrivers' merges lengthen the tail by more than a merge launch
+        // costs), so AUTO keeps the merge launch
+        P.fused_merge = eligible && o.fused_merge == 1;
     }
 
     // ---- tasks: one static list per persistent workgroup -------------------------------------------
@@ -1083,7 +1105,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     st.num_partial_slots = slots_used;
     st.num_merge_rows = int32_t(P.merge_query.size()) * Hq;
     st.num_direct_rows = direct_rows;
-    st.num_launches = int32_t(P.forward_launches.size() + (P.merge_query.empty() ? 0 : 1));
+    st.num_launches = int32_t(P.forward_launches.size() + (P.merge_query.empty() || P.fused_merge ? 0 : 1));
     st.split_tokens = int32_t(C);
     st.blob_bytes = h.blob_bytes;
     st.workspace_bytes = h.total_bytes;
@@ -1332,6 +1354,7 @@ void kvattn_plan_options_default(kvattn_plan_options* o) {
     o->num_cus = 0;
     o->new_token = 0;
     o->multi_stream = 0;
+    o->fused_merge = -1;
 }
 
 kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables, const int32_t* seq_lens,
@@ -1358,7 +1381,8 @@ kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables
     if (opts) o = *opts;
     if (o.pack_mode < 0 || o.pack_mode > 2 || o.scheme < 0 || o.scheme > 2 || o.force_variant < -1 ||
         o.force_variant > 1 || o.split_tokens < 0 || o.num_cus < 0 || !(o.scale >= 0.f) || std::isinf(o.scale) ||
-        o.new_token < 0 || o.new_token > 1 || o.multi_stream < 0 || o.multi_stream > 1)
+        o.new_token < 0 || o.new_token > 1 || o.multi_stream < 0 || o.multi_stream > 1 || o.fused_merge < -1 ||
+        o.fused_merge > 1)
         return set_error(KVATTN_EINVAL, "bad option value");
     kvattn_plan_s* P = new (std::nothrow) kvattn_plan_s();
     if (!P) return set_error(KVATTN_ENOMEM, "plan allocation failed");

@@ -3,6 +3,7 @@
 // provides every device buffer (the workspace included).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <mutex>
 #include <string>
@@ -28,6 +29,10 @@ DevPlan resolve(const kvattn_plan_s& P, int launch, void* ws) {
     if (launch >= 0) d.claim += P.forward_launches[size_t(launch)].side;   // concurrent launches count apart
     d.part_ml = reinterpret_cast<float*>(base + h.off_part_ml);
     d.part_acc = reinterpret_cast<float*>(base + h.off_part_acc);
+    d.arrive = P.fused_merge ? reinterpret_cast<int32_t*>(base + h.off_arrive) : nullptr;
+    // < 4 GiB whenever the plan fuses its merge (the planner checks); unused otherwise
+    d.part_ml_bytes = uint32_t(std::min<uint64_t>(uint64_t(P.n_slots) * 8, 0xFFFFFFF0u));
+    d.part_acc_bytes = uint32_t(std::min<uint64_t>(uint64_t(P.n_slots) * uint64_t(h.head_dim) * 4, 0xFFFFFFF0u));
     return d;
 }
 
@@ -159,6 +164,7 @@ kvattn_status kvattn_decode(const void* q, const void* k_cache, const void* v_ca
         return set_error(KVATTN_EINVAL, "the plan takes each query's newest token from the call: use kvattn_decode_append");
     s = run_forward(q, k_cache, v_cache, plan, out, stream);
     if (s != KVATTN_OK) return s;
+    if (plan->fused_merge) return KVATTN_OK;   // the forward launch merged
     return run_merge(plan, out, stream);
 }
 
@@ -233,6 +239,7 @@ kvattn_status kvattn_decode_noalloc(const void* q, const void* k_cache, const vo
     }
     kvattn_status st = run_forward(q, k_cache, v_cache, plan, out, stream, nullptr, ws);
     if (st != KVATTN_OK) return st;
+    if (plan->fused_merge) return KVATTN_OK;   // the forward launch merged
     return run_merge(plan, out, stream, ws);
 }
 

@@ -40,7 +40,7 @@ class kvattn_prefix_tree(ctypes.Structure):
 
 class kvattn_plan_options(ctypes.Structure):
     _fields_ = [("scale", f32), ("pack_mode", i32), ("scheme", i32), ("force_variant", i32), ("split_tokens", i32),
-                ("num_cus", i32), ("new_token", i32), ("multi_stream", i32)]
+                ("num_cus", i32), ("new_token", i32), ("multi_stream", i32), ("fused_merge", i32)]
 
 
 class kvattn_stats(ctypes.Structure):

@@ -138,6 +138,19 @@ enum { KVATTN_VARIANT_AUTO = -1, KVATTN_VARIANT_VALU = 0, KVATTN_VARIANT_MFMA = 
  *                  details); kvattn_decode_streams runs the MFMA launches on a
  *                  side stream beside the VALU ones.  kvattn_decode runs all
  *                  launches in turn on one stream.
+ *   fused_merge    -1 auto (0: measured faster on every workload), 0 or 1: with
+ *                  1, the forward launch also merges: the
+ *                  task that completes the last partial triple of a (query, KV
+ *                  head) combines that query's partials for the head's q heads
+ *                  with the same online-softmax rule and writes out, and no merge
+ *                  launch follows (PAT review, merge stage).  Partials are
+ *                  written and read with agent-scope coherent accesses, and a
+ *                  per-(query, KV head) arrival counter in the workspace tells
+ *                  which task is last; it returns to zero within the launch.  0
+ *                  keeps the separate merge launch.  Plans with new_token or
+ *                  multi_stream always use the merge launch.  kvattn_forward of
+ *                  a fused plan therefore writes every output row, and
+ *                  kvattn_merge recomputes the merged rows identically.
  */
 typedef struct {
     float scale;
@@ -148,6 +161,7 @@ typedef struct {
     int32_t num_cus;
     int32_t new_token;
     int32_t multi_stream;
+    int32_t fused_merge;
 } kvattn_plan_options;
 
 /* Statistics of a plan (bytes are per decode call, all KV heads). */
@@ -216,7 +230,8 @@ typedef struct {
      * int32 words: a 16-word header (kind, tile, first KV head, tokens, entries
      * n_q, rows, blocks nb, min limit, words of this descriptor, words of the
      * next MFMA descriptor of the same list or 0, then 6 zero words), n_q
-     * entries of 4 words (query, dest, limit, 0), nb block ids, zero padding to
+     * entries of 4 words (query, dest, limit, index of the query's merge record
+     * or -1 when dest is -1), nb block ids, zero padding to
      * a multiple of 4 words.  List l of launch L (one per persistent
      * workgroup) holds its MFMA descriptors in words [lp[0], lp[1]) and its
      * VALU descriptors in [lp[1], lp[2]), lp = list_ptr + 3 (L num_lists + l). */

@@ -577,3 +577,38 @@ def test_upload_refused_under_capture():
             k.kvattn_plan_upload(dec.plan, dec.workspace, dec.workspace.numel(), s)
     assert ei.value.status == k.KVATTN_EINVAL
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("case", ["c2", "c3", "c5", "forest"])
+def test_fused_merge_matches_merge_launch_across_calls(case):
+    """Plans that merge inside the forward launch (fused_merge=1) against the same plans with a
+    merge launch (fused_merge=0): bit-identical outputs, within the oracle's tolerance, over calls
+    that alternate two different query batches and two KV pools on one plan -- a partial read
+    stale from another XCD's cache or from the previous call would show."""
+    from test_plan import random_tree_workload
+    k = K()
+    wl = random_tree_workload(1201).materialize() if case == "forest" else small(int(case[1]))
+    fused = k.Decoder(wl.shape_tuple(), wl.block_tables, wl.seq_lens, options=k.make_options(fused_merge=1))
+    sep = k.Decoder(wl.shape_tuple(), wl.block_tables, wl.seq_lens, options=k.make_options(fused_merge=0))
+    assert fused.stats()["num_launches"] == sep.stats()["num_launches"] - 1
+    q, kc, vc = device_inputs(wl)
+    q2 = torch.from_numpy(W.normal_bf16(wl.seed_values + 7, W.TAG_Q, 0, q.numel()).view(np.int16)).cuda().view(
+        q.shape)
+    vc2 = vc.clone()
+    vc2.view(torch.bfloat16).mul_(-0.5)   # another V pool (NaN slots stay NaN)
+    import dataclasses
+    wl2 = dataclasses.replace(wl, q=q2.cpu().numpy().view(np.uint16),
+                              v_pool=vc2.cpu().numpy().view(np.uint16))
+    refs = {0: oracle.decode_workload(wl), 1: oracle.decode_workload(wl2)}
+    inputs = {0: (q, kc, vc), 1: (q2, kc, vc2)}
+    shape = (wl.num_queries, wl.num_q_heads, wl.head_dim)
+    print("case fused merge %s" % wl.name, flush=True)
+    for call, which in enumerate([0, 1, 0, 0, 1, 1, 0, 1]):
+        a = torch.full(shape, float("nan"), device="cuda")
+        b = torch.full(shape, float("nan"), device="cuda")
+        fused.decode(*inputs[which], a)
+        sep.decode(*inputs[which], b)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), "call %d: fused and separate merges differ (max %.3e)" % (
+            call, float((a - b).abs().nan_to_num(1e9).max()))
+        assert_close(a.cpu().numpy().astype(np.float64), refs[which], "fused %s call %d" % (wl.name, call))

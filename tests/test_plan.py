@@ -98,11 +98,13 @@ def check_descriptors(ex):
     """The device descriptor stream encodes exactly the exported tasks, each once.
 
     Layout (public header): 16 header words (kind, tile, head, tokens, n_q,
-    rows, blocks, min limit, words, next words, 0 x 6), n_q entries of 4 words,
-    the block ids, zero padding to a multiple of 4 words.  Each list holds its
+    rows, blocks, min limit, words, next words, 0 x 6), n_q entries of 4 words
+    (query, dest, limit, merge record or -1), the block ids, zero padding to a
+    multiple of 4 words.  Each list holds its
     MFMA descriptors, then its VALU descriptors.
     """
     it, en, ids, desc = ex["items"], ex["entries"], ex["block_ids"], ex["desc"]
+    rec_of = {int(b): i for i, b in enumerate(ex["merge_query"])}
 
     def expected(item, head):
         nt, nq = int(it["n_tokens"][item]), int(it["n_q"][item])
@@ -119,7 +121,8 @@ def check_descriptors(ex):
         assert words == 16 + 4 * nq + (nb + 3) // 4 * 4 and words <= DESC_MAX_WORDS
         assert not h[10:16].any()
         ent = tuple(tuple(int(x) for x in desc[off + 16 + 4 * k: off + 19 + 4 * k]) for k in range(nq))
-        assert all(desc[off + 19 + 4 * k] == 0 for k in range(nq))
+        # word 3: the query's merge record for a partial entry, -1 for a direct row
+        assert all(int(desc[off + 19 + 4 * k]) == (rec_of[e[0]] if e[1] >= 0 else -1) for k, e in enumerate(ent))
         blk = tuple(int(x) for x in desc[off + 16 + 4 * nq: off + 16 + 4 * nq + nb])
         assert not desc[off + 16 + 4 * nq + nb: off + words].any()
         return (int(h[0]), int(h[1]), int(h[2]), int(h[3]), nq, int(h[5]), nb, int(h[7]), ent, blk), words
