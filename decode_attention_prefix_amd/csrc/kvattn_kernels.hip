@@ -351,9 +351,18 @@ __device__ __forceinline__ bool arrive_last(const DevPlan& p, int Hkv, int rec, 
 // head-dim chunk set of c (elements [8c, 8c+8) and, for D = 128, [64+8c, 64+8c+8)),
 // so every load instruction reads whole 128-byte rows of a block.
 // ============================================================================
-template <int D, int R>
+//
+// SPLIT (the VALU_SPLIT tile): the wave runs the list's VALU_SPLIT tasks
+// instead, all four waves on the task's one KV head, wave w on blocks
+// [w nb / 4, (w + 1) nb / 4) of it.  At the end of each task the waves put
+// their (m, l, acc) rows into `cbuf` (LDS) and, between two workgroup
+// barriers, combine them with the online-softmax rule and store.  Every wave
+// has at least one block of every such task (the planner emits the tile for 4
+// or more blocks; shorter ones are skipped here by every wave alike), so all
+// waves reach the same barriers.
+template <int D, int R, bool SPLIT>
 __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, const int32_t* win, int n_words,
-                                            uint16_t* qs, const uint16_t* __restrict__ q,
+                                            uint16_t* qs, float* cbuf, const uint16_t* __restrict__ q,
                                             const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
                                             float* __restrict__ out) {
     constexpr int NPC = D / 64;      // 16-byte pieces per token per lane
@@ -375,15 +384,24 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
     const uint32_t qs_lds = uint32_t(uintptr_t(qs));
 
     auto hdr = [&](int off, int f) { return __builtin_amdgcn_readfirstlane(win[off + f]); };
-    // first task at or after `off` that has a KV head for this wave
+    // this wave's KV head of the task at `off`, and its blocks [lo, hi) of the task's nb
+    auto head_of = [&](int off) { return hdr(off, kDescHead) + (SPLIT ? 0 : wave); };
+    auto range_lo = [&](int nb) { return SPLIT ? (wave * nb) / kWaves : 0; };
+    auto range_hi = [&](int nb) { return SPLIT ? ((wave + 1) * nb) / kWaves : nb; };
+    // first task at or after `off` that this wave runs: VALU_SPLIT tasks of 4 or
+    // more blocks (SPLIT), else VALU tasks that have a KV head for this wave
     auto skip = [&](int off) {
-        while (off < n_words && hdr(off, kDescHead) + wave >= Hkv) off += hdr(off, kDescWords);
+        while (off < n_words) {
+            const bool split = hdr(off, kDescKind) == KVATTN_VARIANT_VALU_SPLIT;
+            if (SPLIT ? split && hdr(off, kDescBlocks) >= kWaves : !split && hdr(off, kDescHead) + wave < Hkv) break;
+            off += hdr(off, kDescWords);
+        }
         return off;
     };
     // copy the q rows of the task at `off` into slot `s` of this wave
     auto fetch_q = [&](int off, int s) {
         const int nrows = hdr(off, kDescRows);
-        const int g = hdr(off, kDescHead) + wave;
+        const int g = head_of(off);
         // The lane index is re-read here so that the per-lane terms below are
         // not hoisted out of the stream loop as live registers: spilled, their
         // reload would wait for every load in flight.
@@ -403,18 +421,24 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
     // ---- load side
     int l_off = skip(0);
     int l_blk = 0, l_slot = 0;
-    int l_nblk = 0, l_ntok = 0, l_bids = 0, l_g = 0;
+    int l_lo = 0, l_hi = 0, l_ntok = 0, l_bids = 0, l_g = 0;
     auto l_enter = [&]() {
         if (l_off < n_words) {
-            l_nblk = hdr(l_off, kDescBlocks);
+            const int nb = hdr(l_off, kDescBlocks);
+            l_lo = range_lo(nb);
+            l_hi = range_hi(nb);
+            l_blk = l_lo;
             l_ntok = hdr(l_off, kDescTokens);
             l_bids = l_off + kDescHeader + 4 * hdr(l_off, kDescNq);
-            l_g = hdr(l_off, kDescHead) + wave;
+            l_g = head_of(l_off);
         }
     };
     l_enter();
     int total = 0;   // blocks of this wave's stream
-    for (int off = l_off; off < n_words; off = skip(off + hdr(off, kDescWords))) total += hdr(off, kDescBlocks);
+    for (int off = l_off; off < n_words; off = skip(off + hdr(off, kDescWords))) {
+        const int nb = hdr(off, kDescBlocks);
+        total += range_hi(nb) - range_lo(nb);
+    }
 
     // A block's K and V slices of KV head l_g are read through buffer resources
     // whose size covers the block's valid tokens only: the hardware returns
@@ -431,7 +455,7 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
         // A task's q rows are copied right before its first block's loads: the
         // copy is then older than those loads, and at most NR - 1 tasks (the
         // blocks still in the ring) are pending, so NR slots never collide.
-        if (live && l_blk == 0) fetch_q(l_off, l_slot);
+        if (live && l_blk == l_lo) fetch_q(l_off, l_slot);
         const int blk = live ? __builtin_amdgcn_readfirstlane(win[l_bids + l_blk]) : 0;
         const int valid = live ? min(16, l_ntok - l_blk * 16) : 0;
         const size_t o = size_t(blk) * blk_elems + size_t(l_g) * head_elems;
@@ -449,9 +473,8 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
                 vb[tt][pc] = make_uint4(b.x, b.y, b.z, b.w);
             }
         }
-        if (live && ++l_blk == l_nblk) {
+        if (live && ++l_blk == l_hi) {
             l_off = skip(l_off + hdr(l_off, kDescWords));
-            l_blk = 0;
             l_slot = (l_slot + 1) & 3;
             l_enter();
         }
@@ -459,7 +482,7 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
 
     // ---- process side
     int p_off = skip(0);
-    int p_blk = 0, p_slot = 0, p_nblk = 0;
+    int p_blk = -1, p_slot = 0, p_hi = 0;   // p_blk < 0: the next block starts a task
     int limit[R];
     float m[R], l[R], acc[R][NE];
 
@@ -468,7 +491,9 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
         // are complete once at most two blocks' loads remain outstanding
         __builtin_amdgcn_s_waitcnt(waitcnt_vm<(NR - 1) * LPB>());
         __builtin_amdgcn_sched_barrier(0);   // no LDS read of the slot moves above the wait
-        p_nblk = hdr(p_off, kDescBlocks);
+        const int nb = hdr(p_off, kDescBlocks);
+        p_blk = range_lo(nb);
+        p_hi = range_hi(nb);
         const int nrows = hdr(p_off, kDescRows);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -597,7 +622,7 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
     // write the results of the task at `off` (output rows or partial triples)
     auto store_task = [&](int off) {
         const int nrows = hdr(off, kDescRows);
-        const int g = hdr(off, kDescHead) + wave;
+        const int g = head_of(off);
         const bool u32 = (lane & 32) != 0, u16 = (lane & 16) != 0, u8 = (lane & 8) != 0;
         const int ebase = (u32 ? NE / 2 : 0) + (u16 ? NE / 4 : 0) + (u8 ? NE / 8 : 0);
         // element e of chunk set c is head-dim index 8c + e (e < 8) or 64 + 8c + (e - 8)
@@ -646,14 +671,64 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
     // after it, the stores have NR block-times to complete before any wait
     // depends on them.
     int f_off = -1;   // task whose results await their stores
+    // SPLIT: the four waves' rows of the task at `off` combined through LDS and stored
+    auto split_combine = [&](int off) {
+        const int nrows = hdr(off, kDescRows);
+        const int g = hdr(off, kDescHead);
+        constexpr int RS = D + 2;   // floats per row in cbuf: acc[D], m, l
+        const bool u32 = (lane & 32) != 0, u16 = (lane & 16) != 0, u8 = (lane & 8) != 0;
+        const int ebase = (u32 ? NE / 2 : 0) + (u16 ? NE / 4 : 0) + (u8 ? NE / 8 : 0);
+        const int d0 = (ebase < 8) ? 8 * c + ebase : 64 + 8 * c + (ebase - 8);
+        float* mine = cbuf + wave * R * RS;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (r >= nrows) continue;
+#pragma unroll
+            for (int i = 0; i < NE / 8; ++i) mine[r * RS + d0 + i] = acc[r][i];
+            if (lane == 0) {
+                mine[r * RS + D] = mrow[r];
+                mine[r * RS + D + 1] = ltot[r];
+            }
+        }
+        __syncthreads();
+        for (int e = int(threadIdx.x); e < nrows * D; e += 64 * kWaves) {
+            const int r = e / D, d = e - r * D;
+            float M = cbuf[r * RS + D];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) M = fmaxf(M, cbuf[(w * R + r) * RS + D]);
+            float L = 0.f, A = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float* x = cbuf + (w * R + r) * RS;
+                const float f = fast_exp2(x[D] - M);
+                L = fmaf(f, x[D + 1], L);
+                A = fmaf(f, x[d], A);
+            }
+            const int query = win[off + kDescHeader + 4 * (r / G)];
+            const int dest = win[off + kDescHeader + 4 * (r / G) + 1];
+            const int h = g * G + r % G;
+            if (dest < 0) {
+                out[(size_t(query) * Hq + h) * D + d] = A / L;
+            } else {
+                const size_t sl = size_t(dest) + h;
+                p.part_acc[sl * D + d] = A;
+                if (d == 0) *reinterpret_cast<float2*>(p.part_ml + sl * 2) = make_float2(M, L);
+            }
+        }
+        __syncthreads();   // cbuf is free for the next task
+    };
     auto proc_block = [&](const uint4 (&kb)[2][NPC], const uint4 (&vb)[2][NPC]) {
-        if (p_blk == 0) begin_task();
+        if (p_blk < 0) begin_task();
         process(p_blk, kb, vb);
-        if (++p_blk == p_nblk) {
+        if (++p_blk == p_hi) {
             end_task();
-            f_off = p_off;
+            if constexpr (SPLIT) {
+                split_combine(p_off);
+            } else {
+                f_off = p_off;
+            }
             p_off = skip(p_off + hdr(p_off, kDescWords));
-            p_blk = 0;
+            p_blk = -1;
             p_slot = (p_slot + 1) & 3;
         }
     };
@@ -687,7 +762,7 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
     // agent scope) before its arrivals; the task completing a (query, KV head)
     // merges it.  Arrivals come at the end of the stream, where waiting for
     // every outstanding store costs nothing.
-    if (p.arrive) {
+    if (!SPLIT && p.arrive) {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
         __builtin_amdgcn_sched_barrier(0);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -706,7 +781,7 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
         };
         for (int off = skip(0); off < n_words; off = skip(off + hdr(off, kDescWords))) {
             const int nq = hdr(off, kDescNq);
-            const int g = hdr(off, kDescHead) + wave;
+            const int g = head_of(off);
             for (int e = 0; e < nq; ++e) {
                 const int dest = hdr(off, kDescHeader + 4 * e + 1);
                 if (dest < 0) continue;
@@ -1097,6 +1172,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     __shared__ __attribute__((aligned(16))) uint16_t s_kv[KV_ELEMS];
     __shared__ __attribute__((aligned(16))) int32_t s_desc[2][kDescMaxWords];
     __shared__ int s_last[kMaxItemQueries + 1];   // fused merge: units an MFMA task completed, and their count
+    static_assert(kWaves * R * (D + 2) * 4 <= int(sizeof(s_desc)), "VALU_SPLIT combine rows fit the descriptor buffers");
     static_assert(D != 128 || KV_ELEMS * 2 + sizeof(s_desc) + sizeof(s_last) + 64 <= 80 * 1024,
                   "two workgroups per CU");
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
@@ -1147,7 +1223,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             fetch_desc(p.desc + v0, e0 - v0, win);
             wait_all_and_sync();
             uint16_t* qs = s_kv + 2 * WIN + wave * 4 * R * D;
-            valu_stream<D, R>(p, dm, win, e0 - v0, qs, q, kc, vc, out);
+            float* cbuf = reinterpret_cast<float*>(&s_desc[0][0]);   // the descriptor buffers are idle here
+            valu_stream<D, R, false>(p, dm, win, e0 - v0, qs, cbuf, q, kc, vc, out);
+            wait_all_and_sync();
+            valu_stream<D, R, true>(p, dm, win, e0 - v0, qs, cbuf, q, kc, vc, out);
             wait_all_and_sync();   // the window is free for the next list
         }
         if (!claims) break;

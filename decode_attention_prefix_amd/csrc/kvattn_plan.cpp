@@ -306,6 +306,13 @@ constexpr double kOddXcdRate = 0.9;
 // only above that load plus this start cost, so no such list gets a remainder
 // too small to pay for its start.
 constexpr double kValuRestartCost = 40.0;
+// The VALU_SPLIT tile gives each of a workgroup's four waves at least one block
+// of the range.
+constexpr int kSplitMinBlocks = kWaves;
+// Fixed cost of the merge launch and the launch gap before it, in block-times of
+// one wave on an otherwise idle GPU (a wave streams a block in ~0.6 us there,
+// two in flight; the merge launch of a small batch measured ~6 us).
+constexpr double kMergeLaunchBlocks = 10.0;
 
 // Append the descriptor of task t (see kDesc*) to P.desc; returns its words.
 int32_t put_desc(kvattn_plan_s& P, const Task& t) {
@@ -448,14 +455,42 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         derive_tree(bt, nodes, leaf);
     }
 
-    // ---- pack decision (profit model) -----------------------------------------
     const int64_t bpt = int64_t(2) * Hkv * D * 2;          // K+V bytes per token, all KV heads
     const int64_t partial_row_bytes = int64_t(D + 2) * 4;   // one (m, l, acc) triple
     const int num_cus = o.num_cus > 0 ? o.num_cus : 256;
+
+    // ---- one launch for batches too small to fill the GPU (runtime tile selector) ----
+    // Cutting ranges across workgroups spreads a decode over the GPU but adds
+    // partials and a merge launch.  A batch whose (query, KV head) blocks, read
+    // as they are, do not even give every wave one block leaves most of the GPU
+    // idle either way; when each query's range, read four-wide by the
+    // VALU_SPLIT tile, then finishes sooner than the usual plan's share plus the
+    // merge launch's fixed cost, the plan reads each query's own range once per
+    // KV head, in one launch, with no packs, cuts or partials.  Times are in
+    // block-times of one wave.
+    bool one_launch = false;
+    if (o.pack_mode == KVATTN_PACK_AUTO && o.force_variant == KVATTN_VARIANT_AUTO && o.split_tokens == 0 &&
+        !o.new_token && !o.multi_stream && G <= valu_max_rows(D)) {
+        const double waves = double(num_cus) * 2.0 * kWaves;
+        double t_one = 0.0, all = 0.0;
+        int max_nb = 0;
+        for (int b = 0; b < B; ++b) {
+            const int nb = bt.nb[b];
+            max_nb = std::max(max_nb, nb);
+            t_one = std::max(t_one, nb >= kSplitMinBlocks ? std::ceil(nb / double(kWaves)) : double(nb));
+            all += double(nb) * Hkv;
+        }
+        double uniq_tok = 0.0;
+        for (int32_t v : block_reads(s, block_tables, seq_lens)) uniq_tok += v;
+        const double t_two = std::ceil(uniq_tok / kBlock * Hkv / waves) + kMergeLaunchBlocks;
+        one_launch = all <= waves && max_nb <= kMaxItemBlocks && t_one <= t_two;
+    }
+
+    // ---- pack decision (profit model) -----------------------------------------
     int packed_nodes = 0;
     for (Node& n : nodes) {
         const int64_t k = int64_t(n.queries.size());
-        if (k < 2 || o.pack_mode == KVATTN_PACK_QUERY) continue;
+        if (k < 2 || o.pack_mode == KVATTN_PACK_QUERY || one_launch) continue;
         if (o.pack_mode == KVATTN_PACK_FULL) {
             n.packed = true;
         } else {
@@ -557,12 +592,15 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         int kind, tile, rows;
         double w;                // cost per token and KV head relative to streaming it from HBM
     };
+    // VALU groups read ranges of kSplitMinBlocks or more blocks with the VALU_SPLIT
+    // tile when it is forced or in a one-launch plan; shorter ones keep the VALU tile.
+    const bool split_tiles = one_launch || o.force_variant == KVATTN_VARIANT_VALU_SPLIT;
     std::vector<Group> groups;
     for (size_t ui = 0; ui < units.size(); ++ui) {
         const Unit& u = units[ui];
         const int R = int(u.queries.size()) * G;
         int kind;
-        if (o.force_variant == KVATTN_VARIANT_VALU) {
+        if (o.force_variant == KVATTN_VARIANT_VALU || o.force_variant == KVATTN_VARIANT_VALU_SPLIT) {
             if (G > valu_max_rows(D))
                 return set_error(KVATTN_EUNSUPPORTED, "VALU forward holds at most " + std::to_string(valu_max_rows(D)) +
                                                           " rows per KV head at this head_dim");
@@ -659,7 +697,9 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         int64_t tok0, ntok;             // range within the group's unit (ntok excludes a folded leaf)
         bool last;
         int stripe = -1;                // VALU: stripe; MFMA: -1
-        std::vector<int> head_list;     // MFMA: list of each KV head's task
+        std::vector<int> head_list;     // MFMA: list of each KV head's task; one-launch VALU plans: list of
+                                        // each task (per KV head, or per four heads on the VALU tile)
+        bool split = false;             // VALU piece on the VALU_SPLIT tile
     };
     std::vector<Piece> pieces;
     int64_t C = 0;                      // longest chunk of a split range (statistics)
@@ -810,7 +850,54 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         const std::vector<double> base = stripe_base(best.load);
 
         // VALU pieces
-        if (o.split_tokens > 0) {
+        auto split_piece = [&](int64_t ntok) { return split_tiles && (ntok + kBlock - 1) / kBlock >= kSplitMinBlocks; };
+        if (one_launch) {
+            // Each range whole (up to the item cap); its tasks -- one per KV head on the
+            // VALU_SPLIT tile, one per four heads on the VALU tile -- placed longest
+            // first on the least-loaded list, in block-times of one wave.
+            struct T {
+                size_t piece;
+                int slot;
+                double cost;
+            };
+            std::vector<T> tl;
+            const size_t first_piece = best.pieces.size();
+            for (int gi : vg) {
+                const int64_t tokens = unit_tokens(groups[size_t(gi)]);
+                const int64_t nch = (tokens + kChunkCapTokens - 1) / kChunkCapTokens;
+                const int64_t len = ceil16((tokens + nch - 1) / nch);
+                for (int64_t c = 0; c < nch; ++c) {
+                    const int64_t tok0 = c * len;
+                    if (tok0 >= tokens) break;
+                    Piece pc;
+                    pc.group = gi;
+                    pc.tok0 = tok0;
+                    pc.ntok = std::min(len, tokens - tok0);
+                    pc.last = tok0 + pc.ntok == tokens;
+                    pc.split = split_piece(pc.ntok);
+                    if (pc.ntok < tokens) C = std::max(C, pc.ntok);
+                    const double nb = double((pc.ntok + kBlock - 1) / kBlock);
+                    const int n_t = pc.split ? Hkv : quads;
+                    pc.head_list.assign(size_t(n_t), 0);
+                    for (int k = 0; k < n_t; ++k)
+                        tl.push_back({best.pieces.size(), k, pc.split ? std::ceil(nb / kWaves) : nb});
+                    best.pieces.push_back(std::move(pc));
+                }
+            }
+            std::stable_sort(tl.begin(), tl.end(), [](const T& a, const T& b) { return a.cost > b.cost; });
+            using LE = std::pair<double, int>;
+            std::priority_queue<LE, std::vector<LE>, std::greater<LE>> heap;
+            std::vector<double> lload(static_cast<size_t>(n_lists), 0.0);
+            for (int w = 0; w < n_lists; ++w) heap.push({0.0, w});
+            for (const T& t : tl) {
+                const int w = heap.top().second;
+                heap.pop();
+                best.pieces[t.piece].head_list[size_t(t.slot)] = w;
+                lload[size_t(w)] += t.cost + kValuTaskCost / kBlock;
+                heap.push({lload[size_t(w)] / list_rate(w), w});
+            }
+            (void)first_piece;
+        } else if (o.split_tokens > 0) {
             const int64_t chunk = std::min<int64_t>(ceil16(o.split_tokens), kChunkCapTokens);
             std::vector<double> sload = base;
             for (int gi : vg) {
@@ -825,6 +912,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
                     pc.tok0 = tok0;
                     pc.ntok = std::min(len, tokens - tok0);
                     pc.last = tok0 + pc.ntok == tokens;
+                    pc.split = split_piece(pc.ntok);
                     pc.stripe = int(std::min_element(sload.begin(), sload.end()) - sload.begin());
                     sload[size_t(pc.stripe)] += double(pc.ntok) + kValuTaskCost;
                     if (pc.ntok < tokens) C = std::max(C, pc.ntok);
@@ -859,6 +947,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
                             pc.tok0 = t0;
                             pc.ntok = take;
                             pc.last = t0 + take == tokens;
+                            pc.split = split_piece(take);
                             pc.stripe = s;
                             if (take < tokens) C = std::max(C, take);
                             out->push_back(std::move(pc));
@@ -891,7 +980,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         const bool has_fold = u.fold_query >= 0 &&
                               std::find(g.queries.begin(), g.queries.end(), u.fold_query) != g.queries.end();
         Proto p;
-        p.it.kind = g.kind;
+        p.it.kind = g.kind == KVATTN_VARIANT_VALU && pc.split ? KVATTN_VARIANT_VALU_SPLIT : g.kind;
         p.it.tile = g.tile;
         p.it.pos_begin = u.pos_begin + int(pc.tok0 / kBlock);
         const int nblk = int((pc.ntok + kBlock - 1) / kBlock);
@@ -992,7 +1081,9 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     // or with concurrent multi-stream launches; the kernels address the partials
     // with 32-bit byte offsets.
     {
-        const bool eligible = !o.new_token && !o.multi_stream && !P.merge_query.empty() &&
+        bool split_items = false;   // VALU_SPLIT tasks write their partials with plain stores
+        for (const Item& it : P.items) split_items |= it.kind == KVATTN_VARIANT_VALU_SPLIT;
+        const bool eligible = !o.new_token && !o.multi_stream && !P.merge_query.empty() && !split_items &&
                               uint64_t(slots_used) * uint64_t(D) * 4 < (uint64_t(1) << 32);
         // measured on MI355X: merging in the forward is slower on every workload here
         // (the last arrivers' merges lengthen the tail by more than a merge launch
@@ -1024,9 +1115,11 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             if (it.kind == KVATTN_VARIANT_MFMA) {
                 for (int h = 0; h < Hkv; ++h) mlist[size_t(pc.head_list[size_t(h)])].push_back({int32_t(i), h});
             } else {
+                // VALU tile: one task per four KV heads; VALU_SPLIT: one task per KV head
+                const bool split = it.kind == KVATTN_VARIANT_VALU_SPLIT;
                 const int32_t words = desc_words(it.n_q, (it.n_tokens + kBlock - 1) / kBlock);
-                for (int q = 0; q < quads; ++q) {
-                    int w = stripe_list(pc.stripe, q);
+                for (int q = 0; q < (split ? Hkv : quads); ++q) {
+                    int w = pc.head_list.empty() ? stripe_list(pc.stripe, split ? q / kWaves : q) : pc.head_list[size_t(q)];
                     if (vwords[size_t(w)] + words > window) {
                         // the stripe's window is full: the least-filled list with room takes it
                         int best_w = -1;
@@ -1036,7 +1129,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
                         if (best_w < 0) return set_error(KVATTN_EINVAL, "internal: VALU task descriptors exceed the LDS windows");
                         w = best_w;
                     }
-                    vlist[size_t(w)].push_back({int32_t(i), q * kWaves});
+                    vlist[size_t(w)].push_back({int32_t(i), split ? q : q * kWaves});
                     vwords[size_t(w)] += words;
                 }
             }
@@ -1091,10 +1184,11 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     int64_t planned = 0;
     for (const Item& it : P.items) {
         planned += it.n_tokens;
-        if (it.kind == KVATTN_VARIANT_VALU)
-            st.num_items_valu++;
-        else
+        if (it.kind == KVATTN_VARIANT_MFMA)
             st.num_items_mfma++;
+        else
+            st.num_items_valu++;
+        if (it.kind == KVATTN_VARIANT_VALU_SPLIT) st.num_items_valu_split++;
     }
     st.planned_kv_bytes = planned * bpt;
     st.partial_bytes = int64_t(slots_used) * partial_row_bytes * 2;
@@ -1107,6 +1201,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     st.num_direct_rows = direct_rows;
     st.num_launches = int32_t(P.forward_launches.size() + (P.merge_query.empty() || P.fused_merge ? 0 : 1));
     st.split_tokens = int32_t(C);
+    st.one_launch = one_launch ? 1 : 0;
     st.blob_bytes = h.blob_bytes;
     st.workspace_bytes = h.total_bytes;
     st.plan_seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
@@ -1380,7 +1475,7 @@ kvattn_status kvattn_plan(const kvattn_shape* shape, const int32_t* block_tables
     kvattn_plan_options_default(&o);
     if (opts) o = *opts;
     if (o.pack_mode < 0 || o.pack_mode > 2 || o.scheme < 0 || o.scheme > 2 || o.force_variant < -1 ||
-        o.force_variant > 1 || o.split_tokens < 0 || o.num_cus < 0 || !(o.scale >= 0.f) || std::isinf(o.scale) ||
+        o.force_variant > 2 || o.split_tokens < 0 || o.num_cus < 0 || !(o.scale >= 0.f) || std::isinf(o.scale) ||
         o.new_token < 0 || o.new_token > 1 || o.multi_stream < 0 || o.multi_stream > 1 || o.fused_merge < -1 ||
         o.fused_merge > 1)
         return set_error(KVATTN_EINVAL, "bad option value");

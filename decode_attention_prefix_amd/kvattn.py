@@ -22,7 +22,7 @@ LIB_PATH = os.environ.get("KVATTN_LIBRARY") or os.path.join(_PKG, "libkvattn.so"
 
 KVATTN_OK, KVATTN_EINVAL, KVATTN_EUNSUPPORTED, KVATTN_ENOMEM, KVATTN_EWORKSPACE, KVATTN_EHIP, KVATTN_ESTATE = range(7)
 KVATTN_PACK_AUTO, KVATTN_PACK_QUERY, KVATTN_PACK_FULL = 0, 1, 2
-KVATTN_VARIANT_AUTO, KVATTN_VARIANT_VALU, KVATTN_VARIANT_MFMA = -1, 0, 1
+KVATTN_VARIANT_AUTO, KVATTN_VARIANT_VALU, KVATTN_VARIANT_MFMA, KVATTN_VARIANT_VALU_SPLIT = -1, 0, 1, 2
 
 i32, i64, u64, f32, f64, vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float, ctypes.c_double,
                                ctypes.c_void_p)
@@ -49,7 +49,7 @@ class kvattn_stats(ctypes.Structure):
                 ("num_items_valu", i32), ("num_items_mfma", i32), ("num_folded_leaves", i32),
                 ("num_partial_slots", i32), ("num_merge_rows", i32), ("num_direct_rows", i32),
                 ("num_launches", i32), ("split_tokens", i32), ("update_path", i32), ("plan_seconds", f64),
-                ("blob_bytes", u64), ("workspace_bytes", u64)]
+                ("blob_bytes", u64), ("workspace_bytes", u64), ("num_items_valu_split", i32), ("one_launch", i32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_ if k != "reserved"}

@@ -94,7 +94,7 @@ typedef struct {
 } kvattn_prefix_tree;
 
 enum { KVATTN_PACK_AUTO = 0, KVATTN_PACK_QUERY = 1, KVATTN_PACK_FULL = 2 };
-enum { KVATTN_VARIANT_AUTO = -1, KVATTN_VARIANT_VALU = 0, KVATTN_VARIANT_MFMA = 1 };
+enum { KVATTN_VARIANT_AUTO = -1, KVATTN_VARIANT_VALU = 0, KVATTN_VARIANT_MFMA = 1, KVATTN_VARIANT_VALU_SPLIT = 2 };
 
 /*
  * Plan options.  kvattn_plan_options_default() fills the defaults.
@@ -109,10 +109,22 @@ enum { KVATTN_VARIANT_AUTO = -1, KVATTN_VARIANT_VALU = 0, KVATTN_VARIANT_MFMA = 
  *   scheme         0 auto, 1 = packing scheme 1 only (leaves always split off their
  *                  parent, Fig 7(c)), 2 = also allow scheme 2 (one short leaf folded
  *                  into its parent's item, Fig 7(d)).
- *   force_variant  -1 auto; KVATTN_VARIANT_VALU / _MFMA force one forward kernel
- *                  family for every item (for tests).  VALU handles at most 8 rows
- *                  per KV head at head_dim 64 and 4 at head_dim 128 (wider packs are
- *                  split into several items; a wider GQA group is EUNSUPPORTED).
+ *   force_variant  -1 auto; KVATTN_VARIANT_VALU / _MFMA / _VALU_SPLIT force one
+ *                  forward tile for every item (for tests).  VALU handles at most 8
+ *                  rows per KV head at head_dim 64 and 4 at head_dim 128 (wider packs
+ *                  are split into several items; a wider GQA group is EUNSUPPORTED).
+ *                  The two VALU tiles differ in how a workgroup's four waves share an
+ *                  item: VALU gives each wave one KV head of the item's range (four
+ *                  heads per task); VALU_SPLIT gives the four waves a quarter each of
+ *                  one KV head's range and combines their partial results in LDS
+ *                  (one task per head), so a range is read four-wide without being
+ *                  cut into partials across workgroups.  VALU_SPLIT needs at least 4
+ *                  blocks (64 tokens) per range; shorter ranges keep the VALU tile.
+ *                  AUTO picks the tile per item by its KV length (runtime tile
+ *                  selector): MFMA for packed groups, VALU for single queries and
+ *                  small packs, and -- for batches too small to fill the GPU, where
+ *                  one launch without partials beats cutting ranges and merging --
+ *                  VALU_SPLIT for every range of 4 or more blocks.
  *   split_tokens   0 auto; otherwise the KV chunk length of split items, rounded
  *                  up to a multiple of 16 (long-KV splitting).
  *   num_cus        compute units the split model balances over; 0 means 256
@@ -187,12 +199,14 @@ typedef struct {
     double plan_seconds;             /* host wall time of kvattn_plan                            */
     uint64_t blob_bytes;             /* schedule bytes uploaded by kvattn_plan_upload            */
     uint64_t workspace_bytes;        /* = kvattn_plan_device_bytes                               */
+    int32_t num_items_valu_split;    /* items on the VALU_SPLIT tile (counted in num_items_valu) */
+    int32_t one_launch;              /* 1: a small batch planned as one launch without partials */
 } kvattn_stats;
 
 /* One forward work item, as exported for inspection and coverage checks. */
 typedef struct {
-    int32_t kind;        /* KVATTN_VARIANT_VALU or _MFMA                                      */
-    int32_t tile;        /* VALU: rows per KV head (1,2,4,8); MFMA: 16-row tiles per wave (1,2) */
+    int32_t kind;        /* KVATTN_VARIANT_VALU, _MFMA or _VALU_SPLIT                          */
+    int32_t tile;        /* VALU tiles: rows per KV head (1,2,4,8); MFMA: 16-row tiles per wave (1,2) */
     int32_t pos_begin;   /* first logical block position of the item's KV range               */
     int32_t n_tokens;    /* tokens in the item's KV range                                     */
     int32_t q_begin;     /* first entry in entries[]                                          */
@@ -224,8 +238,9 @@ typedef struct {
     int32_t num_partial_slots;
     int32_t head_dim;
     int32_t num_tasks;
-    const int32_t* tasks;         /* [num_tasks][2]: (item, first KV head); an MFMA item runs one
-                                     task per KV head, a VALU item one per 4 consecutive KV heads */
+    const int32_t* tasks;         /* [num_tasks][2]: (item, first KV head); MFMA and VALU_SPLIT
+                                     items run one task per KV head, a VALU item one per 4
+                                     consecutive KV heads */
     /* The task descriptors as uploaded to the device.  A descriptor is a run of
      * int32 words: a 16-word header (kind, tile, first KV head, tokens, entries
      * n_q, rows, blocks nb, min limit, words of this descriptor, words of the

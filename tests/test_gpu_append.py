@@ -76,10 +76,11 @@ def run_append(wl, seed, rows=None, **opts):
 
 @pytest.mark.parametrize("c", [1, 2, 3, 5])
 @pytest.mark.parametrize("opts", [{}, {"pack_mode": 1}, {"pack_mode": 2, "force_variant": 0},
-                                  {"pack_mode": 2, "force_variant": 1, "split_tokens": 48}])
+                                  {"pack_mode": 2, "force_variant": 1, "split_tokens": 48},
+                                  {"pack_mode": 2, "force_variant": 2}])
 def test_append_parity_small_configs(c, opts):
     wl = small(c)
-    if opts.get("force_variant") == 0 and wl.group > valu_max_rows(wl.head_dim):
+    if opts.get("force_variant") in (0, 2) and wl.group > valu_max_rows(wl.head_dim):
         expect_unsupported(wl, new_token=1, **opts)
         return
     got, ref, _ = run_append(wl, 40 + c, **opts)

@@ -104,11 +104,11 @@ def test_parity_small_configs_auto_variant(c, mode):
 
 
 @pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
-@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("variant", [0, 1, 2])
 @pytest.mark.parametrize("scheme,split", [(1, 0), (2, 0), (1, 16), (2, 48), (0, 208)])
 def test_parity_small_configs_forced_variant(c, variant, scheme, split):
     wl = small(c)
-    if variant == 0 and wl.group > valu_max_rows(wl.head_dim):
+    if variant in (0, 2) and wl.group > valu_max_rows(wl.head_dim):
         expect_unsupported(wl, pack_mode=2, force_variant=variant, scheme=scheme, split_tokens=split)
         return
     got, _ = gpu_decode(wl, pack_mode=2, force_variant=variant, scheme=scheme, split_tokens=split)
@@ -116,13 +116,13 @@ def test_parity_small_configs_forced_variant(c, variant, scheme, split):
 
 
 @pytest.mark.parametrize("c", [2, 3, 5])
-@pytest.mark.parametrize("variant", [-1, 0, 1])
+@pytest.mark.parametrize("variant", [-1, 0, 1, 2])
 def test_parity_lists_claimed_past_the_grid(c, variant):
     """A plan for more workgroup slots than the GPU has (num_cus 1024: 2048
     lists) leaves the lists past the grid to run-time claims.  Two decodes in
     a row: the claim counter must be back at zero after the first."""
     wl = small(c)
-    if variant == 0 and wl.group > valu_max_rows(wl.head_dim):
+    if variant in (0, 2) and wl.group > valu_max_rows(wl.head_dim):
         expect_unsupported(wl, num_cus=1024, force_variant=variant)
         return
     k = K()
@@ -216,7 +216,9 @@ def test_parity_multi_token_queries(m):
     ref_rows = dataclasses.replace(base, name="multi_tok_ref_%d" % m, seq_lens=ref_sl, block_tables=ref_bt, q=q)
     print("case multi-token m=%d rows %d" % (m, rows), flush=True)
     got, dec = gpu_decode(lib_rows)
-    assert dec.stats()["num_items_mfma"] > 0 or base.group * m <= 4
+    st = dec.stats()
+    # the rows of a query are packed onto MFMA, unless the batch is small enough for a one-launch plan
+    assert st["num_items_mfma"] > 0 or st["one_launch"] or base.group * m <= 4
     assert_close(got, oracle.decode_workload(ref_rows), "multi-token m=%d" % m)
 
 
@@ -242,11 +244,11 @@ def edge_workload(lengths, shared, Hq, Hkv, D, seed):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("G,Hkv", [(1, 4), (4, 2), (8, 1)])
-@pytest.mark.parametrize("variant", [-1, 0, 1])
+@pytest.mark.parametrize("variant", [-1, 0, 1, 2])
 def test_parity_boundary_lengths(D, G, Hkv, variant):
-    lengths = [1, 15, 16, 17, 32, 33, 31, 2, 47, 48, 49]
+    lengths = [1, 15, 16, 17, 32, 33, 31, 2, 47, 48, 49, 63, 64, 65, 129]
     wl = edge_workload(lengths, 0, G * Hkv, Hkv, D, 7 + D + G)
-    if variant == 0 and G > valu_max_rows(D):
+    if variant in (0, 2) and G > valu_max_rows(D):
         expect_unsupported(wl, force_variant=variant)
         return
     got, _ = gpu_decode(wl, force_variant=variant)
@@ -261,7 +263,7 @@ def test_parity_boundary_lengths(D, G, Hkv, variant):
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(1, 1, 64), (3, 1, 64), (6, 2, 128), (16, 1, 128), (32, 32, 128),
                                        (64, 2, 128), (64, 1, 64), (128, 8, 128)])
-@pytest.mark.parametrize("variant", [-1, 0, 1])
+@pytest.mark.parametrize("variant", [-1, 0, 1, 2])
 def test_parity_head_shapes(Hq, Hkv, D, variant):
     """Head counts off the configs' 32/8 and 4/4: one head, odd groups, MHA with 32 KV heads,
     the widest GQA group (64 q heads per KV head) and 128 q heads, over a shared prefix
@@ -269,14 +271,14 @@ def test_parity_head_shapes(Hq, Hkv, D, variant):
     G = Hq // Hkv
     lengths = [1, 17, 33, 40, 64, 90, 129]
     wl = edge_workload(lengths, 32, Hq, Hkv, D, 60 + Hq + Hkv + D)
-    if variant == 0 and G > valu_max_rows(D):
+    if variant in (0, 2) and G > valu_max_rows(D):
         expect_unsupported(wl, force_variant=variant)
         return
     got, dec = gpu_decode(wl, force_variant=variant)
     assert_close(got, oracle_out(wl), "heads %d/%d D%d v%d" % (Hq, Hkv, D, variant))
 
 
-@pytest.mark.parametrize("variant", [-1, 0, 1])
+@pytest.mark.parametrize("variant", [-1, 0, 1, 2])
 @pytest.mark.parametrize("shared", [16, 32, 48])
 def test_parity_shared_prefix_ragged(variant, shared):
     lengths = [shared + x for x in (1, 15, 16, 17, 33, 100)] + [shared]
@@ -292,7 +294,7 @@ def test_parity_peaked_scores():
     q = W.bf16_bits_to_f32(wl.q) * 8.0
     wl.q = W.f32_to_bf16_bits(q)
     wl.name = "c2_small_peaked"
-    for variant in (0, 1):
+    for variant in (0, 1, 2):
         got, _ = gpu_decode(wl, pack_mode=2, force_variant=variant)
         assert_close(got, oracle_out(wl), "peaked v%d" % variant)
 
@@ -466,6 +468,8 @@ def test_parity_random_trees(seed):
     cases = [{}, {"pack_mode": 2}, {"force_variant": 1, "split_tokens": 32}, {"multi_stream": 1}]
     if wl.group <= valu_max_rows(wl.head_dim):
         cases.append({"force_variant": 0, "pack_mode": 2, "scheme": 2})
+        cases.append({"force_variant": 2, "pack_mode": 2, "scheme": 2})
+        cases.append({"force_variant": 2, "pack_mode": 1, "split_tokens": 80})
     for opts in cases:
         if opts.get("multi_stream"):
             print("case %s opts %s" % (wl.name, opts), flush=True)
@@ -588,8 +592,9 @@ def test_fused_merge_matches_merge_launch_across_calls(case):
     from test_plan import random_tree_workload
     k = K()
     wl = random_tree_workload(1201).materialize() if case == "forest" else small(int(case[1]))
-    fused = k.Decoder(wl.shape_tuple(), wl.block_tables, wl.seq_lens, options=k.make_options(fused_merge=1))
-    sep = k.Decoder(wl.shape_tuple(), wl.block_tables, wl.seq_lens, options=k.make_options(fused_merge=0))
+    # full packing: partials to merge even where AUTO would plan a small batch as one launch
+    fused = k.Decoder(wl.shape_tuple(), wl.block_tables, wl.seq_lens, options=k.make_options(fused_merge=1, pack_mode=2))
+    sep = k.Decoder(wl.shape_tuple(), wl.block_tables, wl.seq_lens, options=k.make_options(fused_merge=0, pack_mode=2))
     assert fused.stats()["num_launches"] == sep.stats()["num_launches"] - 1
     q, kc, vc = device_inputs(wl)
     q2 = torch.from_numpy(W.normal_bf16(wl.seed_values + 7, W.TAG_Q, 0, q.numel()).view(np.int16)).cuda().view(
@@ -612,3 +617,19 @@ def test_fused_merge_matches_merge_launch_across_calls(case):
         assert torch.equal(a, b), "call %d: fused and separate merges differ (max %.3e)" % (
             call, float((a - b).abs().nan_to_num(1e9).max()))
         assert_close(a.cpu().numpy().astype(np.float64), refs[which], "fused %s call %d" % (wl.name, call))
+
+
+
+def test_parity_one_launch_small_batches():
+    """Small batches planned as one launch without partials (VALU_SPLIT tile for ranges of 4+ blocks,
+    VALU below): one launch, no merge rows, outputs within tolerance, at both head sizes."""
+    k = K()
+    for D, Hq, Hkv in ((64, 4, 4), (128, 16, 4), (128, 8, 8)):
+        rng = np.random.default_rng(D + Hq)
+        lengths = [int(x) for x in rng.integers(1, 700, size=5)] + [1, 63, 64]
+        wl = edge_workload(lengths, 0, Hq, Hkv, D, 300 + D + Hq)
+        got, dec = gpu_decode(wl)
+        st = dec.stats()
+        assert st["one_launch"] == 1 and st["num_launches"] == 1 and st["num_merge_rows"] == 0, st
+        assert st["num_items_valu_split"] >= 1
+        assert_close(got, oracle_out(wl), "one-launch D%d %d/%d" % (D, Hq, Hkv))

@@ -31,13 +31,16 @@ def check_coverage(wl_bt, seq_lens, Hq, Hkv, ex, all_merged=False):
         n_tok, pb = int(it["n_tokens"][i]), int(it["pos_begin"][i])
         q0, nq = int(it["q_begin"][i]), int(it["n_q"][i])
         assert it["n_rows"][i] == nq * G
-        assert it["kind"][i] in (K.KVATTN_VARIANT_VALU, K.KVATTN_VARIANT_MFMA)
-        if it["kind"][i] == K.KVATTN_VARIANT_VALU:
+        assert it["kind"][i] in (K.KVATTN_VARIANT_VALU, K.KVATTN_VARIANT_MFMA, K.KVATTN_VARIANT_VALU_SPLIT)
+        valu = it["kind"][i] != K.KVATTN_VARIANT_MFMA
+        if valu:
             assert it["n_rows"][i] <= it["tile"][i] <= (4 if ex["head_dim"] == 128 else 8)
         else:
             assert it["tile"][i] in (1, 2) and it["n_rows"][i] <= 64 * it["tile"][i]
         nblk = (n_tok + 15) // 16
-        assert nblk <= (512 if it["kind"][i] == K.KVATTN_VARIANT_VALU else 1408)
+        assert nblk <= (512 if valu else 1408)
+        if it["kind"][i] == K.KVATTN_VARIANT_VALU_SPLIT:
+            assert nblk >= 4, "the split tile gives each of four waves a block"
         blk = ids[int(it["blk_begin"][i]): int(it["blk_begin"][i]) + nblk]
         assert blk.size == nblk
         assert any(int(en["limit"][q0 + k]) == n_tok for k in range(nq))
@@ -80,13 +83,13 @@ def check_coverage(wl_bt, seq_lens, Hq, Hkv, ex, all_merged=False):
                     assert (x + h) not in slots_used
                     slots_used[x + h] = b
     assert len(slots_used) == ex["num_partial_slots"]
-    # every item runs on every KV head exactly once: one task per head (MFMA) or per 4 heads (VALU)
+    # every item runs on every KV head exactly once: one task per head (MFMA, VALU_SPLIT) or per 4 heads (VALU)
     seen = {}
     for item, head in ex["tasks"]:
         seen.setdefault(int(item), []).append(int(head))
     for i in range(len(it["kind"])):
         heads = sorted(seen.get(i, []))
-        step = 1 if it["kind"][i] == K.KVATTN_VARIANT_MFMA else 4
+        step = 4 if it["kind"][i] == K.KVATTN_VARIANT_VALU else 1
         assert heads == list(range(0, Hkv, step)), (i, heads)
     check_descriptors(ex)
 
@@ -146,9 +149,9 @@ def check_descriptors(ex):
                 off = nxt
             assert off == v0
             rows_max = 1
-            while off < e0:     # VALU descriptors, copied to LDS in one piece
+            while off < e0:     # VALU descriptors (both VALU tiles), copied to LDS in one piece
                 d, words = decode(off)
-                assert d[0] == K.KVATTN_VARIANT_VALU and int(desc[off + 9]) == 0
+                assert d[0] in (K.KVATTN_VARIANT_VALU, K.KVATTN_VARIANT_VALU_SPLIT) and int(desc[off + 9]) == 0
                 rows_max = max(rows_max, d[1])
                 got.append(d)
                 covered += words
@@ -174,7 +177,9 @@ def test_coverage_full_size_configs(c, mode):
     s = K.kvattn_plan_stats(p)
     assert s["unique_kv_bytes"] == wl.unique_kv_bytes
     assert s["query_centric_kv_bytes"] == wl.query_centric_kv_bytes
-    if mode == K.KVATTN_PACK_QUERY:
+    # only the tiny batch is planned as one launch without partials (its queries read their own ranges)
+    assert s["one_launch"] == (1 if (c == 1 and mode == K.KVATTN_PACK_AUTO) else 0)
+    if mode == K.KVATTN_PACK_QUERY or s["one_launch"]:
         assert s["planned_kv_bytes"] == wl.query_centric_kv_bytes
     else:
         # every shared segment is read once per group of at most 128 rows (q heads of the
@@ -192,11 +197,11 @@ def test_coverage_full_size_configs(c, mode):
 
 
 @pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
-@pytest.mark.parametrize("variant", [K.KVATTN_VARIANT_VALU, K.KVATTN_VARIANT_MFMA])
+@pytest.mark.parametrize("variant", [K.KVATTN_VARIANT_VALU, K.KVATTN_VARIANT_MFMA, K.KVATTN_VARIANT_VALU_SPLIT])
 @pytest.mark.parametrize("scheme", [1, 2])
 def test_coverage_forced_variants_and_schemes(c, variant, scheme):
     wl = W.small(c)
-    if variant == K.KVATTN_VARIANT_VALU and wl.group > (4 if wl.head_dim == 128 else 8):
+    if variant != K.KVATTN_VARIANT_MFMA and wl.group > (4 if wl.head_dim == 128 else 8):
         with pytest.raises(K.KvattnError):
             plan_of(wl, force_variant=variant)
         return
@@ -463,3 +468,25 @@ def test_multi_stream_plans_split_launches_by_kind(c):
     assert s2["num_launches"] == lp.shape[0] + (1 if len(ex["merge_query"]) else 0)
     if len(kinds) == 2:
         assert s2["num_launches"] > s1["num_launches"]
+
+
+def test_tile_selector_by_kv_length():
+    """The VALU_SPLIT tile goes to ranges of 4 or more blocks only; shorter ranges keep the VALU
+    tile.  The tiny batch is planned as one launch: every query's range whole, no partials, no
+    merge launch; larger batches keep the usual plan."""
+    wl = W.config1()
+    st = K.kvattn_plan_stats(plan_of(wl))
+    assert st["one_launch"] == 1 and st["num_launches"] == 1 and st["num_merge_rows"] == 0
+    assert st["num_items"] == wl.num_queries and st["num_items_valu_split"] == wl.num_queries
+    for c in (2, 3, 4, 5):
+        s = K.kvattn_plan_stats(plan_of(W.WORKLOADS[c]()))
+        assert s["one_launch"] == 0 and s["num_items_valu_split"] == 0
+    # forced: split where the range has 4+ blocks, the VALU tile below
+    segs = [[(("own", b), n)] for b, n in enumerate([1, 16, 47, 48, 63, 64, 65, 200, 1000])]
+    w2 = W.from_segments("split_lengths", segs, 8, 2, 128, 3, 903)
+    ex = K.kvattn_plan_export(plan_of(w2, force_variant=K.KVATTN_VARIANT_VALU_SPLIT, pack_mode=K.KVATTN_PACK_QUERY,
+                                      split_tokens=4096))
+    check_coverage(w2.block_tables, w2.seq_lens, 8, 2, ex)
+    for kind, n in zip(ex["items"]["kind"], ex["items"]["n_tokens"]):
+        want = K.KVATTN_VARIANT_VALU_SPLIT if (n + 15) // 16 >= 4 else K.KVATTN_VARIANT_VALU
+        assert kind == want, (kind, n)

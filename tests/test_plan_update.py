@@ -149,7 +149,8 @@ def test_shared_item_growing_apart_rebuilds():
     # cut every query back into the shared root: the queries end together there
     cut = np.full(wl.num_queries, 40, dtype=np.int32)
     bt, lens = state(wl, cut)
-    plan = K.kvattn_plan(wl.shape_tuple(), bt, lens)
+    # packed explicitly: AUTO plans a batch this small as one launch without packs
+    plan = K.kvattn_plan(wl.shape_tuple(), bt, lens, None, K.make_options(pack_mode=K.KVATTN_PACK_FULL))
     cut -= 1
     bt, lens = state(wl, cut)
     K.kvattn_plan_update(plan, bt, lens)
