@@ -285,26 +285,39 @@ def multi_stream_timing(K, torch, wl, dec, pools, q, outs, steps, warmup):
             "multi_stream_launches": st["num_launches"], "max_abs_diff": diff}
 
 
+# (workgroups per CU, loads in flight per lane, threads): the best of these is the plain-read
+# ceiling; a sweep over 2-8 loads, 256-1024 threads and 1-16 workgroups per CU found one of them
+# best at every pool size from 169 MB to 8.6 GB
+PROBE_CONFIGS = ((2, 4, 256), (1, 2, 1024), (2, 8, 512), (2, 8, 1024))
+
+
 def plain_read(K, torch, pools, stream, n_ev):
-    """A plain streaming read of the same K/V pools (kvattn_read_probe, one contiguous
-    share per workgroup), median of HIP-event timed launches: what the memory system
-    delivers for those bytes at that size, as context beside the peak."""
+    """A plain streaming read of the same K/V pools (kvattn_read_probe, one contiguous share
+    per workgroup), median of HIP-event timed launches, for a few launch shapes: what the
+    memory system delivers for those bytes at that size, as context beside the peak."""
     copies = len(pools)
-    grid = 2 * torch.cuda.get_device_properties(0).multi_processor_count
-    sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
-    for i in range(3):
-        K.kvattn_read_probe(pools[i % copies][0], pools[i % copies][1], sink, grid, stream)
-    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
-    for i in range(n_ev):
-        pev[i][0].record(stream)
-        K.kvattn_read_probe(pools[i % copies][0], pools[i % copies][1], sink, grid, stream)
-        pev[i][1].record(stream)
-    torch.cuda.synchronize()
-    us = float(np.median([e[0].elapsed_time(e[1]) for e in pev])) * 1e3
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(2 * cus * 1024, dtype=torch.int32, device="cuda")
     nbytes = pools[0][0].numel() * 2 + pools[0][1].numel() * 2
-    return {"GB/s": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": int(nbytes), "us": round(us, 2), "grid": grid,
-            "what": "kvattn_read_probe: one contiguous share per workgroup of the K and V pools, "
-                    "median of HIP-event timed launches"}
+    best = None
+    for per_cu, depth, threads in PROBE_CONFIGS:
+        grid = per_cu * cus
+        for i in range(3):
+            K.kvattn_read_probe(pools[i % copies][0], pools[i % copies][1], sink, grid, stream, depth, threads)
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
+        for i in range(n_ev):
+            pev[i][0].record(stream)
+            K.kvattn_read_probe(pools[i % copies][0], pools[i % copies][1], sink, grid, stream, depth, threads)
+            pev[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.median([e[0].elapsed_time(e[1]) for e in pev])) * 1e3
+        r = {"GB/s": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": int(nbytes), "us": round(us, 2), "grid": grid,
+             "threads": threads, "loads_in_flight": depth}
+        if best is None or r["GB/s"] > best["GB/s"]:
+            best = r
+    best["what"] = ("kvattn_read_probe: one contiguous share per workgroup of the K and V pools, median of HIP-event "
+                    "timed launches, best of %d launch shapes" % len(PROBE_CONFIGS))
+    return best
 
 
 # ---- rocprofv3 summaries (profiles/) -------------------------------------------------------------

@@ -166,7 +166,7 @@ int launch_forward(const DevPlan& p, const Dims& d, int valu_rows, int mfma_tile
                    const uint16_t* q, const uint16_t* k, const uint16_t* v, float* out, void* stream);
 int launch_merge(const DevPlan& p, const Dims& d, int q_count, float* out, void* stream);
 int launch_read_probe(const void* a, size_t a_bytes, const void* b, size_t b_bytes, uint32_t* sink, int grid,
-                      void* stream);
+                      int depth, int threads, void* stream);
 int launch_merge_append(const DevPlan& p, const Dims& d, int q_count, const NewTokens& nt, float* out, void* stream);
 
 // kvattn_decode_noalloc: bytes of the static per-device scratch that holds a

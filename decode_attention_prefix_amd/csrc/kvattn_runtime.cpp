@@ -244,17 +244,22 @@ kvattn_status kvattn_decode_noalloc(const void* q, const void* k_cache, const vo
 }
 
 kvattn_status kvattn_read_probe(const void* a, size_t a_bytes, const void* b, size_t b_bytes, void* sink,
-                                size_t sink_bytes, int32_t grid, void* stream) {
+                                size_t sink_bytes, int32_t grid, int32_t loads_in_flight, int32_t threads,
+                                void* stream) {
     using namespace kvattn;
     clear_error();
     if (!a || !b || !sink) return set_error(KVATTN_EINVAL, "a, b or sink is NULL");
     if (!aligned16(a) || !aligned16(b) || !aligned16(sink) || (a_bytes & 15u) || (b_bytes & 15u))
         return set_error(KVATTN_EINVAL, "buffers must be 16-byte aligned and multiples of 16 bytes");
     if (grid < 1) return set_error(KVATTN_EINVAL, "grid must be >= 1");
-    if (sink_bytes < size_t(grid) * 256 * 4)
+    if ((loads_in_flight != 2 && loads_in_flight != 4 && loads_in_flight != 8) ||
+        (threads != 256 && threads != 512 && threads != 1024))
+        return set_error(KVATTN_EINVAL, "loads_in_flight must be 2, 4 or 8 and threads 256, 512 or 1024");
+    if (sink_bytes < size_t(grid) * size_t(threads) * 4)
         return set_error(KVATTN_EINVAL, "sink holds " + std::to_string(sink_bytes) + " bytes, the probe writes " +
-                                            std::to_string(size_t(grid) * 256 * 4));
-    const int rc = launch_read_probe(a, a_bytes, b, b_bytes, static_cast<uint32_t*>(sink), grid, stream);
+                                            std::to_string(size_t(grid) * size_t(threads) * 4));
+    const int rc = launch_read_probe(a, a_bytes, b, b_bytes, static_cast<uint32_t*>(sink), grid, loads_in_flight,
+                                     threads, stream);
     if (rc != 0) return set_error(KVATTN_EHIP, std::string("probe launch failed: ") + hipGetErrorString(hipError_t(rc)));
     return KVATTN_OK;
 }

@@ -97,7 +97,7 @@ def _load():
     lib.kvattn_decode_streams.restype = ctypes.c_int
     lib.kvattn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
     lib.kvattn_decode_append.restype = ctypes.c_int
-    lib.kvattn_read_probe.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp, ctypes.c_size_t, i32, vp]
+    lib.kvattn_read_probe.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp, ctypes.c_size_t, i32, i32, i32, vp]
     lib.kvattn_read_probe.restype = ctypes.c_int
     lib.kvattn_merge.argtypes = [vp, vp, vp]
     lib.kvattn_merge.restype = ctypes.c_int
@@ -260,10 +260,11 @@ def kvattn_decode_append(q, k_new, v_new, k_cache, v_cache, plan: Plan, out, str
                                      _ptr(out), _stream(stream)), "kvattn_decode_append")
 
 
-def kvattn_read_probe(a, b, sink, grid, stream=None):
+def kvattn_read_probe(a, b, sink, grid, stream=None, loads_in_flight=4, threads=256):
     """Plain streaming read of tensors a and b (measurement helper; see kvattn.h)."""
     _check(_lib.kvattn_read_probe(_ptr(a), a.numel() * a.element_size(), _ptr(b), b.numel() * b.element_size(),
-                                  _ptr(sink), sink.numel() * sink.element_size(), int(grid), _stream(stream)),
+                                  _ptr(sink), sink.numel() * sink.element_size(), int(grid), int(loads_in_flight),
+                                  int(threads), _stream(stream)),
            "kvattn_read_probe")
 
 

@@ -371,14 +371,18 @@ def test_read_probe_reads_every_word():
     a = rng.integers(0, 2 ** 31, size=(1000 * 4 + 4,), dtype=np.int64).astype(np.int32)
     b = rng.integers(0, 2 ** 31, size=(777 * 4,), dtype=np.int64).astype(np.int32)
     grid = 7
-    sink = torch.zeros(grid * 256, dtype=torch.int32, device="cuda")
-    k.kvattn_read_probe(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), sink, grid)
-    torch.cuda.synchronize()
-    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     want = np.bitwise_xor.reduce(np.concatenate([a, b]).view(np.uint32))
-    assert got == want
+    for depth in (2, 4, 8):
+        for threads in (256, 512, 1024):
+            sink = torch.zeros(grid * threads, dtype=torch.int32, device="cuda")
+            k.kvattn_read_probe(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), sink, grid, None, depth,
+                                threads)
+            torch.cuda.synchronize()
+            assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == want, (depth, threads)
     with pytest.raises(k.KvattnError):
         k.kvattn_read_probe(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), sink[:10], grid)
+    with pytest.raises(k.KvattnError):
+        k.kvattn_read_probe(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), sink, grid, None, 16, 256)
 
 
 def test_two_plans_in_flight_on_two_streams():
