@@ -414,7 +414,8 @@ def measure(c, args, torch, K, W, steps, warmup, extras_on):
     wl = W.WORKLOADS[c]().materialize()
     log("bench: %s generated in %.1f s; unique KV %.1f MB" % (wl.name, time.perf_counter() - t_gen,
                                                               wl.unique_kv_bytes / 1e6))
-    opts = K.make_options(pack_mode=args.pack_mode, split_tokens=args.split_tokens, fused_merge=args.fused_merge)
+    opts = K.make_options(pack_mode=args.pack_mode, split_tokens=args.split_tokens, fused_merge=args.fused_merge,
+                          force_variant=args.force_variant, num_cus=args.num_cus)
     # the device is initialised before this point: plan_upload_ms covers planning,
     # the workspace allocation and the upload copy only
     torch.cuda.synchronize()
@@ -461,20 +462,35 @@ def measure(c, args, torch, K, W, steps, warmup, extras_on):
     torch.cuda.synchronize()
 
     # one HIP graph per KV copy: a replay is one decode call (forward + merge launches)
-    graphs = []
+    # HIP graphs of consecutive decode calls, rotating over the KV copies: a model's
+    # decode step runs its layers' attention calls back to back inside one graph,
+    # so the timed region replays one graph holding exactly `steps` calls
+    # ("graph"); "graph-per-call" replays a one-call graph per step instead.
+    graphs, per_call = [], []
+    timing = "eager launches"
     if not args.no_graph:
         for i in range(copies):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 K.kvattn_decode(q, pools[i][0], pools[i][1], dec.plan, outs[i])
-            graphs.append(g)
+            per_call.append(g)
         for i in range(warmup):
-            graphs[i % copies].replay()
+            per_call[i % copies].replay()
         torch.cuda.synchronize()
+        if args.timing == "graph":
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(steps):
+                    K.kvattn_decode(q, pools[i % copies][0], pools[i % copies][1], dec.plan, outs[i % copies])
+            graphs.append(g)
+            timing = "one HIP graph of %d consecutive calls (rotating over %d KV copies), replayed once" % (steps,
+                                                                                                         copies)
+        else:
+            timing = "HIP graph replay per call"
 
     def step(i):
-        if graphs:
-            graphs[i % copies].replay()
+        if per_call:
+            per_call[i % copies].replay()
         else:
             eager_step(i)
 
@@ -490,30 +506,72 @@ def measure(c, args, torch, K, W, steps, warmup, extras_on):
         torch.cuda.synchronize()
     for i in range(warmup):
         step(i)
+    if graphs:
+        graphs[0].replay()   # the timed graph itself, once untimed
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps, synchronised on both sides
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        step(i)
+    if graphs:
+        graphs[0].replay()
+    else:
+        for i in range(steps):
+            step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / steps * 1e3
 
-    # per-stage GPU time with HIP events on the launch stream
+    # Per-stage GPU time with HIP events on the launch stream.  With graphs: one
+    # graph of n_ev consecutive forward launches and one of n_ev merge launches
+    # (over the partials the last forward wrote), each replay bracketed by events:
+    # the average duration of each kernel as it runs back to back, without launch
+    # latency.  Eagerly: an event pair around each launch.
     n_ev = min(max(steps, 30), 100)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
-    for i in range(n_ev):
-        kk, vv = pools[i % copies]
-        evs[i][0].record(stream)
-        K.kvattn_forward(q, kk, vv, dec.plan, outs[i % copies], stream)
-        evs[i][1].record(stream)
-        K.kvattn_merge(dec.plan, outs[i % copies], stream)
-        evs[i][2].record(stream)
-    torch.cuda.synchronize()
-    fwd_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(n_ev)])
-    mrg_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(n_ev)])
+    if graphs:
+        merges = st["num_merge_rows"] > 0   # one-launch plans have no merge launch
+        gf, gm = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gf):
+            for i in range(n_ev):
+                kk, vv = pools[i % copies]
+                K.kvattn_forward(q, kk, vv, dec.plan, outs[i % copies])
+        if merges:
+            with torch.cuda.graph(gm):
+                for i in range(n_ev):
+                    K.kvattn_merge(dec.plan, outs[(n_ev - 1) % copies])
+        gf.replay()
+        if merges:
+            gm.replay()
+        torch.cuda.synchronize()
+        fwd_ms, mrg_ms = [], []
+        for _ in range(3):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record(stream)
+            gf.replay()
+            ev[1].record(stream)
+            if merges:
+                gm.replay()
+            ev[2].record(stream)
+            torch.cuda.synchronize()
+            fwd_ms.append(ev[0].elapsed_time(ev[1]) / n_ev)
+            mrg_ms.append(ev[1].elapsed_time(ev[2]) / n_ev)
+        fwd_ms, mrg_ms = np.array(fwd_ms), np.array(mrg_ms)
+        stage_timing = "graphs of %d consecutive forward launches, then %d merge launches, events around each" % (
+            n_ev, n_ev)
+        del gf, gm
+    else:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+        for i in range(n_ev):
+            kk, vv = pools[i % copies]
+            evs[i][0].record(stream)
+            K.kvattn_forward(q, kk, vv, dec.plan, outs[i % copies], stream)
+            evs[i][1].record(stream)
+            K.kvattn_merge(dec.plan, outs[i % copies], stream)
+            evs[i][2].record(stream)
+        torch.cuda.synchronize()
+        fwd_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(n_ev)])
+        mrg_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(n_ev)])
+        stage_timing = "an event pair around each eager launch"
     call_ms = fwd_ms + mrg_ms
 
     plain = plain_read(K, torch, pools, stream, n_ev)
@@ -535,6 +593,7 @@ def measure(c, args, torch, K, W, steps, warmup, extras_on):
                                                                                  st["num_items_valu"]),
                 "algorithmic_bytes_per_launch": int(uniq),
                 "avg_forward_us": round(fwd_avg * 1e3, 2), "avg_merge_us": round(float(mrg_ms.mean()) * 1e3, 2),
+                "stage_timing": stage_timing,
                 "plain_read": dict(plain, forward_over_plain_read=round(achieved / plain["GB/s"], 4))}
     rec = {
         "value": round(value, 1), "unit": "GB/s", "steps": steps, "warmup": warmup,
@@ -554,7 +613,7 @@ def measure(c, args, torch, K, W, steps, warmup, extras_on):
                                     "num_folded_leaves", "num_merge_rows", "num_launches", "split_tokens",
                                     "planned_kv_bytes", "partial_bytes")},
         "kv_copies_rotated": copies,
-        "timing": "HIP graph replay per call" if graphs else "eager launches",
+        "timing": timing,
         "roofline": roofline,
     }
     desc = describe(c, wl)
@@ -564,7 +623,7 @@ def measure(c, args, torch, K, W, steps, warmup, extras_on):
         if c in SINGLE_CORE_CONFIGS:
             rec["cpu_baseline_single_core"] = cpu_baseline(wl, args.cpu_budget_s / 2, threads=1)
             log("bench: cpu baseline, one core %s" % json.dumps(rec["cpu_baseline_single_core"]))
-    del dec, graphs, pools, outs, q, k0, v0
+    del dec, graphs, per_call, pools, outs, q, k0, v0
     wl.release_values()
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -579,6 +638,10 @@ def main():
     ap.add_argument("--config", default="all", choices=["all", "1", "2", "3", "4", "5"])
     ap.add_argument("--pack-mode", type=int, default=0)
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--num-cus", type=int, default=0,
+                    help="plan option num_cus (0: a whole MI355X); more than the device's CUs leaves lists to run-time claims")
+    ap.add_argument("--force-variant", type=int, default=-1, choices=[-1, 0, 1, 2],
+                    help="plan option force_variant: -1 auto, 0 VALU, 1 MFMA, 2 VALU_SPLIT tile for every item")
     ap.add_argument("--fused-merge", type=int, default=-1, choices=[-1, 0, 1],
                     help="plan option fused_merge: -1 auto, 0 merge launch, 1 merge inside the forward launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -587,6 +650,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0)
     ap.add_argument("--copy-calibration", type=int, default=0)
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--timing", default="graph", choices=["graph", "graph-per-call"],
+                    help="graph: one HIP graph of the timed steps' consecutive calls; graph-per-call: one replay per call")
     ap.add_argument("--prewarm-s", type=float, default=0.2,
                     help="seconds of untimed calls before the counted warm-up steps (GPU clocks settle)")
     ap.add_argument("--no-extras", action="store_true",
