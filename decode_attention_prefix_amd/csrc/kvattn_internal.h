@@ -154,6 +154,9 @@ struct DevPlan {
     int32_t* arrive;
     uint32_t part_ml_bytes;     // bytes of part_ml and part_acc (< 4 GiB when fused)
     uint32_t part_acc_bytes;
+    // 1 when both partial arrays fit 32-bit byte offsets (always when fused): the
+    // kernels then store partials written through the L2 (sc1); 0: plain stores
+    int32_t part_wt;
 };
 
 struct Dims {

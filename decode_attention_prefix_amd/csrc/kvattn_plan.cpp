@@ -1081,7 +1081,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     // or with concurrent multi-stream launches; the kernels address the partials
     // with 32-bit byte offsets.
     {
-        bool split_items = false;   // VALU_SPLIT tasks write their partials with plain stores
+        bool split_items = false;   // VALU_SPLIT tasks count no arrivals
         for (const Item& it : P.items) split_items |= it.kind == KVATTN_VARIANT_VALU_SPLIT;
         const bool eligible = !o.new_token && !o.multi_stream && !P.merge_query.empty() && !split_items &&
                               uint64_t(slots_used) * uint64_t(D) * 4 < (uint64_t(1) << 32);
