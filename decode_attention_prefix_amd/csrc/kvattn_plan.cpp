@@ -854,7 +854,10 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         if (one_launch) {
             // Each range whole (up to the item cap); its tasks -- one per KV head on the
             // VALU_SPLIT tile, one per four heads on the VALU tile -- placed longest
-            // first on the least-loaded list, in block-times of one wave.
+            // first on the least-loaded list, in block-times of one wave.  A task of KV
+            // head (or head quad) k prefers a list of XCD k mod 8, so the queries that
+            // share a range read its blocks through one L2: they run at the same time,
+            // and the L2 fetches each block from HBM once for all of them.
             struct T {
                 size_t piece;
                 int slot;
@@ -886,15 +889,23 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             }
             std::stable_sort(tl.begin(), tl.end(), [](const T& a, const T& b) { return a.cost > b.cost; });
             using LE = std::pair<double, int>;
-            std::priority_queue<LE, std::vector<LE>, std::greater<LE>> heap;
+            using Heap = std::priority_queue<LE, std::vector<LE>, std::greater<LE>>;
+            std::vector<Heap> heap_x(kXcds);   // keys are times: load / rate
             std::vector<double> lload(static_cast<size_t>(n_lists), 0.0);
-            for (int w = 0; w < n_lists; ++w) heap.push({0.0, w});
+            for (int w = 0; w < n_lists; ++w) heap_x[size_t(w % kXcds)].push({0.0, w});
             for (const T& t : tl) {
-                const int w = heap.top().second;
-                heap.pop();
+                int xb = -1;
+                for (int x = 0; x < kXcds; ++x)
+                    if (!heap_x[size_t(x)].empty() && (xb < 0 || heap_x[size_t(x)].top() < heap_x[size_t(xb)].top())) xb = x;
+                const int xp = t.slot % kXcds;
+                int x = xb;
+                if (!heap_x[size_t(xp)].empty() && heap_x[size_t(xp)].top().first <= heap_x[size_t(xb)].top().first + 0.25 * t.cost)
+                    x = xp;
+                const int w = heap_x[size_t(x)].top().second;
+                heap_x[size_t(x)].pop();
                 best.pieces[t.piece].head_list[size_t(t.slot)] = w;
                 lload[size_t(w)] += t.cost + kValuTaskCost / kBlock;
-                heap.push({lload[size_t(w)] / list_rate(w), w});
+                heap_x[size_t(x)].push({lload[size_t(w)] / list_rate(w), w});
             }
             (void)first_piece;
         } else if (o.split_tokens > 0) {
