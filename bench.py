@@ -340,8 +340,8 @@ def _csv_rows(directory, suffix):
 
 
 def _short(name):
-    name = name.replace("void kvattn::(anonymous namespace)::", "")
-    return name[:60]
+    name = name.replace("void kvattn::(anonymous namespace)::", "").replace("kvattn::(anonymous namespace)::", "")
+    return name.split("(")[0][:60]
 
 
 def trace_summary(directory, c, command):
@@ -592,7 +592,9 @@ def measure(c, args, torch, K, W, steps, warmup, extras_on):
                 "kernel": "fwd_kernel (persistent; %d MFMA + %d VALU items)" % (st["num_items_mfma"],
                                                                                  st["num_items_valu"]),
                 "algorithmic_bytes_per_launch": int(uniq),
-                "avg_forward_us": round(fwd_avg * 1e3, 2), "avg_merge_us": round(float(mrg_ms.mean()) * 1e3, 2),
+                "avg_forward_us": round(fwd_avg * 1e3, 2),
+                # plans without merge rows (one-launch plans) have no merge launch
+                "avg_merge_us": round(float(mrg_ms.mean()) * 1e3, 2) if st["num_merge_rows"] > 0 else None,
                 "stage_timing": stage_timing,
                 "plain_read": dict(plain, forward_over_plain_read=round(achieved / plain["GB/s"], 4))}
     rec = {
