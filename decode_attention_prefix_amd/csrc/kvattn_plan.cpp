@@ -285,10 +285,14 @@ constexpr int64_t kMfmaChunkCapTokens = int64_t(kMfmaMaxItemBlocks) * kBlock - k
 // rate (measured on MI355X: ~45 ns against ~180-280 ns per head-token under
 // load) after a pipeline fill of ~7 us; wider row groups add matrix work per
 // token.  A VALU task adds a small boundary cost to its wave streams
-// (epilogue, q rows).
+// (epilogue, q rows); a fit of per-task traces (workgroup end times against
+// blocks and tasks per list) put it near 1.5 block-times, and 24 units beat 8
+// on the Llama-3-8B-shaped layer (49.1 against 49.8 us per call, two rounds;
+// the other workloads within noise), while a larger MFMA task cost (100) was
+// slower on both shared workloads.
 constexpr double kMfmaTokenCost = 0.2;
 constexpr double kMfmaTaskCost = 40.0;
-constexpr double kValuTaskCost = 8.0;
+constexpr double kValuTaskCost = 24.0;
 // Partial triples are written into a saturated HBM read stream; on MI355X a
 // VALU wave's small partial stores cost about twenty read bytes per byte
 // (measured), which is why the VALU work is cut at most once per stripe.  An
