@@ -232,28 +232,30 @@ def append_timing(K, torch, W, wl, dec, pools, q, outs, steps, warmup):
 
 
 def graph_best_us(torch, fns, copies, steps, warmup):
-    """HIP-graph replays of each step function (one graph per KV copy), timed in two
-    alternating rounds; the best round of each.  Launch-bound sizes are sensitive to
-    what ran just before, hence the alternation."""
+    """Each step function captured as one HIP graph of `steps` consecutive calls
+    (call i on KV copy i mod copies, as the main timing does), replayed once per
+    round between HIP events after warm-up replays, in two alternating rounds;
+    the best round of each.  Launch-bound sizes are sensitive to what ran just before, hence the
+    alternation."""
     graphs = {}
     for name, fn in fns.items():
-        graphs[name] = []
-        for i in range(copies):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
                 fn(i)
-            graphs[name].append(g)
+        graphs[name] = g
     best = {}
     for _ in range(2):
-        for name, gs in graphs.items():
-            for i in range(warmup):
-                gs[i % copies].replay()
+        for name, g in graphs.items():
+            for _ in range(max(1, warmup // 5)):
+                g.replay()
             torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for i in range(steps):
-                gs[i % copies].replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
             torch.cuda.synchronize()
-            us = (time.perf_counter() - t0) / steps * 1e6
+            us = e0.elapsed_time(e1) / steps * 1e3
             best[name] = min(best.get(name, us), us)
     return {name: round(us, 2) for name, us in best.items()}
 
