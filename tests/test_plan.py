@@ -490,3 +490,21 @@ def test_tile_selector_by_kv_length():
     for kind, n in zip(ex["items"]["kind"], ex["items"]["n_tokens"]):
         want = K.KVATTN_VARIANT_VALU_SPLIT if (n + 15) // 16 >= 4 else K.KVATTN_VARIANT_VALU
         assert kind == want, (kind, n)
+
+
+def test_one_launch_places_each_kv_head_on_one_xcd():
+    """In a one-launch plan every task of KV head k sits on a list of XCD k mod 8 (list w runs on
+    XCD w mod 8), so the queries that share a prefix read it through one L2."""
+    wl = W.config1()
+    ex = K.kvattn_plan_export(plan_of(wl))
+    lp = np.asarray(ex["list_ptr"]).reshape(-1, 3)
+    desc = np.asarray(ex["desc"])
+    seen = 0
+    for w in range(ex["num_lists"]):
+        off, end = lp[w][1], lp[w][2]
+        while off < end:
+            head = int(desc[off + 2])
+            assert head % 8 == w % 8, (w, head)
+            seen += 1
+            off += int(desc[off + 8])
+    assert seen == wl.num_queries * wl.num_kv_heads
