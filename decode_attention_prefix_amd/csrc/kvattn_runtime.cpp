@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <cstdint>
 #include <mutex>
 #include <string>
@@ -31,11 +32,15 @@ DevPlan resolve(const kvattn_plan_s& P, int launch, void* ws) {
     d.part_acc = reinterpret_cast<float*>(base + h.off_part_acc);
     d.arrive = P.fused_merge ? reinterpret_cast<int32_t*>(base + h.off_arrive) : nullptr;
     // < 4 GiB whenever the plan fuses its merge (the planner checks); larger arrays
-    // are written with plain stores and 64-bit addresses (part_wt 0)
+    // are written with plain stores and 64-bit addresses (part_wt 0).  The
+    // environment variable KVATTN_PLAIN_PARTIALS=1 takes that path at any size
+    // (plans without a fused merge), so tests can check it on small batches.
     const uint64_t acc_bytes = uint64_t(P.n_slots) * uint64_t(h.head_dim) * 4;
     d.part_ml_bytes = uint32_t(std::min<uint64_t>(uint64_t(P.n_slots) * 8, 0xFFFFFFF0u));
     d.part_acc_bytes = uint32_t(std::min<uint64_t>(acc_bytes, 0xFFFFFFF0u));
-    d.part_wt = acc_bytes <= 0xFFFFFFF0u ? 1 : 0;
+    const char* plain = std::getenv("KVATTN_PLAIN_PARTIALS");
+    const bool force_plain = plain && plain[0] == '1' && !P.fused_merge;
+    d.part_wt = acc_bytes <= 0xFFFFFFF0u && !force_plain ? 1 : 0;
     return d;
 }
 

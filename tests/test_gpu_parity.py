@@ -325,6 +325,28 @@ def test_forward_then_merge_equals_decode():
     assert torch.equal(a, c)
 
 
+@pytest.mark.parametrize("c", [2, 3, 4, 5])
+def test_plain_partial_stores_match_write_through(c, monkeypatch):
+    """Partials are stored written through the L2 when the partial arrays fit 32-bit offsets,
+    with plain stores otherwise; KVATTN_PLAIN_PARTIALS=1 takes the plain path on a small batch:
+    bit-identical outputs, within tolerance of the oracle."""
+    k = K()
+    wl = small(c)
+    dec = k.Decoder(wl.shape_tuple(), wl.block_tables, wl.seq_lens)
+    assert k.kvattn_plan_stats(dec.plan)["num_partial_slots"] > 0
+    q, kc, vc = device_inputs(wl)
+    a = torch.zeros((wl.num_queries, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+    b = torch.zeros_like(a)
+    k.kvattn_decode(q, kc, vc, dec.plan, a)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("KVATTN_PLAIN_PARTIALS", "1")
+    k.kvattn_decode(q, kc, vc, dec.plan, b)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("KVATTN_PLAIN_PARTIALS")
+    assert torch.equal(a, b)
+    assert_close(b.cpu().numpy(), oracle_out(wl), "plain partial stores, config %d" % c)
+
+
 @pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
 def test_parity_full_size(c):
     """Full-size configs in the launch configuration the bench times (default plan), every
