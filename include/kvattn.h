@@ -365,6 +365,10 @@ kvattn_status kvattn_plan_upload(kvattn_plan_t plan, void* dev_workspace, size_t
  * The bound workspace holds the partial triples, so at most one decode per
  * workspace may be in flight.  One plan serves any number of calls (e.g. every
  * layer of a decode step) with different q / caches of the same shape.
+ * Partial triples are stored written through the L2 while the partial arrays
+ * fit 32-bit byte offsets, with plain stores beyond; the environment variable
+ * KVATTN_PLAIN_PARTIALS=1 selects the plain stores at any size (for tests;
+ * plans with a fused merge always write through).
  * Errors: EINVAL (NULL, plan made with new_token: use kvattn_decode_append),
  * ESTATE (no workspace bound), EHIP (launch failed).
  */
