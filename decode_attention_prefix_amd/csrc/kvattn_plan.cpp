@@ -471,10 +471,14 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     // VALU_SPLIT tile, then finishes sooner than the usual plan's share plus the
     // merge launch's fixed cost, the plan reads each query's own range once per
     // KV head, in one launch, with no packs, cuts or partials.  Times are in
-    // block-times of one wave.
+    // block-times of one wave.  New-token plans take the same decision for their
+    // forward; their merge launch (which adds the new tokens) follows either way,
+    // and on such batches the usual plan's many small pieces cost about a launch
+    // more than its model time (measured on MI355X: the tiny batch's fused append
+    // takes 9.3 us with this forward against 13.0 us with the usual one).
     bool one_launch = false;
     if (o.pack_mode == KVATTN_PACK_AUTO && o.force_variant == KVATTN_VARIANT_AUTO && o.split_tokens == 0 &&
-        !o.new_token && !o.multi_stream && G <= valu_max_rows(D)) {
+        !o.multi_stream && G <= valu_max_rows(D)) {
         const double waves = double(num_cus) * 2.0 * kWaves;
         double t_one = 0.0, all = 0.0;
         int max_nb = 0;

@@ -200,7 +200,9 @@ typedef struct {
     uint64_t blob_bytes;             /* schedule bytes uploaded by kvattn_plan_upload            */
     uint64_t workspace_bytes;        /* = kvattn_plan_device_bytes                               */
     int32_t num_items_valu_split;    /* items on the VALU_SPLIT tile (counted in num_items_valu) */
-    int32_t one_launch;              /* 1: a small batch planned as one launch without partials */
+    int32_t one_launch;              /* 1: a small batch's forward planned as one launch without packs
+                                        or cuts (no partials and no merge launch, except that
+                                        new-token plans merge every row)                          */
 } kvattn_stats;
 
 /* One forward work item, as exported for inspection and coverage checks. */

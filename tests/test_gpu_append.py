@@ -87,6 +87,18 @@ def test_append_parity_small_configs(c, opts):
     assert_close(got, ref, "append %s %s" % (wl.name, opts))
 
 
+def test_append_one_launch_forward_tiny_batch():
+    """The tiny batch's new-token plan reads every query's cached range whole (no packs, no
+    cuts: the one-launch forward), then the merge adds the new tokens: parity and bit-exact
+    caches at full size."""
+    wl = W.config1().materialize()
+    got, ref, dec = run_append(wl, 77)
+    st = dec.stats()
+    assert st["one_launch"] == 1 and st["num_packed_nodes"] == 0 and st["num_launches"] == 2
+    assert st["num_merge_rows"] == wl.num_queries * wl.num_q_heads
+    assert_close(got, ref, "append one-launch tiny batch")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_append_edge_lengths(D):
     """seq_len 1 (the new token alone), new tokens opening a block, and ragged tails, in one batch."""
