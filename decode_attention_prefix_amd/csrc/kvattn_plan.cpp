@@ -299,10 +299,14 @@ constexpr double kValuTaskCost = 24.0;
 // MFMA task writes its partials as one burst of up to 128 rows, which costs
 // far less per byte.
 constexpr double kPartialWriteCostMfma = 2.0;
-// Measured on MI355X (per-task traces): workgroups on odd XCDs stream ~10 %
-// slower than on even ones, whatever the KV heads they read; VALU stripes on
-// odd XCDs are filled to 0.9 of the common level.
-constexpr double kOddXcdRate = 0.9;
+// Relative streaming rate of lists on odd XCDs (list w runs on XCD w mod 8).
+// Per-task traces of earlier builds, whose partial stores stayed in the L2,
+// showed odd XCDs ~10 % slower, and 0.9 paid then.  With write-through partial
+// stores they no longer lag: the traces show them ending first, and on two
+// boxes 1.0 beat 0.9 (C3 233 against 240 us, the no-sharing batch 1509 against
+// 1548 us, the Llama-3-8B-shaped layer 48.5 against 49.4 us per call; 0.95 in
+// between).  The rate stays a parameter of the placement.
+constexpr double kOddXcdRate = 1.0;
 // A list that runs MFMA tasks starts its VALU stream late and from cold: the
 // descriptor window, the q rows and the first blocks each take a round trip
 // under full load (per-task traces on MI355X: a 16-token VALU remainder after
