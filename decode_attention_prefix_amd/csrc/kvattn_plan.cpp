@@ -300,12 +300,13 @@ constexpr double kValuTaskCost = 24.0;
 // far less per byte.
 constexpr double kPartialWriteCostMfma = 2.0;
 // Relative streaming rate of lists on odd XCDs (list w runs on XCD w mod 8).
-// Per-task traces of earlier builds, whose partial stores stayed in the L2,
-// showed odd XCDs ~10 % slower, and 0.9 paid then.  With write-through partial
-// stores they no longer lag: the traces show them ending first, and on two
-// boxes 1.0 beat 0.9 (C3 233 against 240 us, the no-sharing batch 1509 against
-// 1548 us, the Llama-3-8B-shaped layer 48.5 against 49.4 us per call; 0.95 in
-// between).  The rate stays a parameter of the placement.
+// Traces of single launches show odd XCDs 8-15 % slower while every workgroup
+// streams, and a 0.9 fill paid in earlier builds.  With write-through partial
+// stores, back-to-back calls run faster without it, on three boxes: the
+// two-level tree 232.9 against 239.6 us, the no-sharing batch 1510.6 against
+// 1549.3 us, the Llama-3-8B-shaped layer 48.6 against 49.1 us per call (0.95
+// in between; the equal MFMA chunks of the streaming sessions never used it).
+// The rate stays a parameter of the placement.
 constexpr double kOddXcdRate = 1.0;
 // A list that runs MFMA tasks starts its VALU stream late and from cold: the
 // descriptor window, the q rows and the first blocks each take a round trip
