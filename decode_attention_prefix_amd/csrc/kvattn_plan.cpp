@@ -308,6 +308,14 @@ constexpr double kPartialWriteCostMfma = 2.0;
 // in between; the equal MFMA chunks of the streaming sessions never used it).
 // The rate stays a parameter of the placement.
 constexpr double kOddXcdRate = 1.0;
+// Relative streaming rate of the second workgroup of each CU (lists n_lists/2
+// and up run on the same CUs as lists 0 and up, dispatched after them).
+// Per-task traces show it 11-15 % slower per block for the whole launch.  A 0.9
+// fill measured, over two boxes and two rounds each, 47.35-47.55 against
+// 48.1-48.26 us per call on the Llama-3-8B-shaped layer and 231.0 against
+// 233.4 us on the two-level tree; the no-sharing batch and the streaming
+// sessions within noise (0.85: no better).
+constexpr double kSecondSlotRate = 0.9;
 // A list that runs MFMA tasks starts its VALU stream late and from cold: the
 // descriptor window, the q rows and the first blocks each take a round trip
 // under full load (per-task traces on MI355X: a 16-token VALU remainder after
@@ -698,8 +706,8 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     auto stripe_list = [&](int s, int q) {
         return xcd_stripes ? (s / kXcds) * kXcds * quads + s % kXcds + kXcds * q : s * quads + q;
     };
-    // relative streaming rate of list w (odd XCDs are slower)
-    auto list_rate = [&](int w) { return (w % kXcds) % 2 ? kOddXcdRate : 1.0; };
+    // relative streaming rate of list w (XCD parity and workgroup slot)
+    auto list_rate = [&](int w) { return ((w % kXcds) % 2 ? kOddXcdRate : 1.0) * (w >= n_lists / 2 ? kSecondSlotRate : 1.0); };
     auto stripe_rate = [&](int s) { return list_rate(stripe_list(s, 0)); };
     const double pu_mfma = (kPartialWriteCostMfma + 1.0) * double(partial_row_bytes) / double(2 * D * 2);
     auto mfma_cost = [&](const Group& g, int64_t tok) { return double(tok) * g.w + kMfmaTaskCost; };
@@ -812,9 +820,12 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         // the level at which the stripes, each filled from its base, hold `work`
         auto fill_level = [&](const std::vector<double>& base, double work) {
             double lo = *std::min_element(base.begin(), base.end());
-            double hi = 0.0;
-            for (int s = 0; s < n_stripes; ++s) hi = std::max(hi, base[size_t(s)] / stripe_rate(s));
-            hi += work / (n_stripes * kOddXcdRate) + 1.0;
+            double hi = 0.0, rmin = 1.0;
+            for (int s = 0; s < n_stripes; ++s) {
+                hi = std::max(hi, base[size_t(s)] / stripe_rate(s));
+                rmin = std::min(rmin, stripe_rate(s));
+            }
+            hi += work / (n_stripes * rmin) + 1.0;   // every stripe then holds >= work / n_stripes
             for (int it = 0; it < 60; ++it) {
                 const double mid = 0.5 * (lo + hi);
                 double cap = 0.0;
