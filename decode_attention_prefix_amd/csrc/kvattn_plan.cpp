@@ -299,15 +299,23 @@ constexpr double kValuTaskCost = 24.0;
 // MFMA task writes its partials as one burst of up to 128 rows, which costs
 // far less per byte.
 constexpr double kPartialWriteCostMfma = 2.0;
-// Relative streaming rate of lists on odd XCDs (list w runs on XCD w mod 8).
-// Traces of single launches show odd XCDs 8-15 % slower while every workgroup
-// streams, and a 0.9 fill paid in earlier builds.  With write-through partial
-// stores, back-to-back calls run faster without it, on three boxes: the
-// two-level tree 232.9 against 239.6 us, the no-sharing batch 1510.6 against
-// 1549.3 us, the Llama-3-8B-shaped layer 48.6 against 49.1 us per call (0.95
-// in between; the equal MFMA chunks of the streaming sessions never used it).
-// The rate stays a parameter of the placement.
-constexpr double kOddXcdRate = 1.0;
+// Relative streaming rate of lists on odd XCDs (list w runs on XCD w mod 8),
+// for launches whose lists hold at least kOddRateMinLoad units (32 blocks per
+// wave); shorter lists keep 1.0, since a block is already ~10 % of them.
+// Traces show odd XCDs streaming 8-12 % slower than even ones while every
+// workgroup streams, yet on this GPU every way of giving them less work
+// measured slower with back-to-back calls (a 0.9 fill: the two-level tree
+// 239.6 against 232.9 us, the no-sharing batch 1549 against 1511 us), and
+// giving them more measured faster: 1.1 took the no-sharing batch from
+// 1506.1 to 1462.8-1468.9 us and the two-level tree from 232.6-233.2 to
+// 228.8-229.5 us per call on two boxes (1.05 and 1.2 in between), while the
+// Llama-3-8B-shaped layer, whose lists hold ~11 blocks, lost 2 % (hence the
+// threshold).  MFMA-only launches take it through chunk lengths (odd-XCD
+// chunks 1.1 as long): the streaming sessions went from 1506-1510 to
+// 1482-1489 us per call.  The rate is empirical: it models the XCDs' shares of
+// the memory system under full load, which is not a per-XCD speed.
+constexpr double kOddXcdRate = 1.1;
+constexpr double kOddRateMinLoad = 512.0;
 // Relative streaming rate of the second workgroup of each CU (lists n_lists/2
 // and up run on the same CUs as lists 0 and up, dispatched after them).
 // Per-task traces show it 11-15 % slower per block for the whole launch.  A 0.9
@@ -706,8 +714,10 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     auto stripe_list = [&](int s, int q) {
         return xcd_stripes ? (s / kXcds) * kXcds * quads + s % kXcds + kXcds * q : s * quads + q;
     };
-    // relative streaming rate of list w (XCD parity and workgroup slot)
-    auto list_rate = [&](int w) { return ((w % kXcds) % 2 ? kOddXcdRate : 1.0) * (w >= n_lists / 2 ? kSecondSlotRate : 1.0); };
+    // relative streaming rate of list w (XCD parity and workgroup slot); the
+    // odd-XCD rate is set per launch
+    double odd_rate = 1.0;
+    auto list_rate = [&](int w) { return ((w % kXcds) % 2 ? odd_rate : 1.0) * (w >= n_lists / 2 ? kSecondSlotRate : 1.0); };
     auto stripe_rate = [&](int s) { return list_rate(stripe_list(s, 0)); };
     const double pu_mfma = (kPartialWriteCostMfma + 1.0) * double(partial_row_bytes) / double(2 * D * 2);
     auto mfma_cost = [&](const Group& g, int64_t tok) { return double(tok) * g.w + kMfmaTaskCost; };
@@ -735,6 +745,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         for (int gi : vg) w_valu += double(unit_tokens(groups[gi])) * quads;
         for (int gi : mg) w_mfma += double(unit_tokens(groups[gi])) * groups[gi].w * Hkv;
         const double mean0 = std::max(64.0, (w_valu + w_mfma) / n_lists);
+        odd_rate = mean0 >= kOddRateMinLoad ? kOddXcdRate : 1.0;
 
         // chunks of MFMA group g at a target task cost `target`
         auto mfma_chunks = [&](const Group& g, double target) {
@@ -753,32 +764,49 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             std::vector<double> load;
             double extra = 0.0;
         };
-        auto place_mfma = [&](double target) {
+        // chunk lengths of group g at `target`: (even, odd) chunk length.  With
+        // `parity` the chunks alternate between lists of even and of odd XCDs,
+        // the odd ones odd_rate times as long, so that the two halves of the GPU
+        // end together although every chunk of a group serves all its KV heads
+        // (an MFMA-only launch has no VALU work to even them out).
+        auto mfma_lens = [&](const Group& g, double target, bool parity) {
+            const int64_t tokens = unit_tokens(g);
+            const int64_t nch = mfma_chunks(g, target);
+            const int64_t len = ceil16((tokens + nch - 1) / nch);
+            if (!parity) return std::make_pair(len, len);
+            const int64_t n_e = (nch + 1) / 2, n_o = nch / 2;
+            const int64_t le = ceil16(int64_t(std::ceil(double(tokens) / (double(n_e) + odd_rate * double(n_o)))));
+            const int64_t lo = ceil16((std::max<int64_t>(0, tokens - n_e * le) + n_o - 1) / n_o);
+            return std::make_pair(le, lo);
+        };
+        auto place_mfma = [&](double target, bool parity) {
             MfmaPlan mp;
             mp.load.assign(size_t(n_lists), 0.0);
             struct T {
                 int piece, head;
                 double cost;
+                int cls;   // parity plans: XCD parity of the task's list; else -1
             };
             std::vector<T> tasks;
             for (int gi : mg) {
                 const Group& g = groups[size_t(gi)];
                 const int64_t tokens = unit_tokens(g);
                 const int64_t nch = mfma_chunks(g, target);
-                const int64_t len = ceil16((tokens + nch - 1) / nch);
+                const auto lens = mfma_lens(g, target, parity);
                 mp.extra += double(nch - 1) * g.rows * Hkv * pu_mfma;
-                for (int64_t c = 0; c < nch; ++c) {
-                    const int64_t tok0 = c * len;
-                    if (tok0 >= tokens) break;
+                int64_t tok0 = 0;
+                for (int64_t c = 0; c < nch && tok0 < tokens; ++c) {
+                    const int cls = parity ? int(c % 2) : -1;
                     Piece pc;
                     pc.group = gi;
                     pc.tok0 = tok0;
-                    pc.ntok = std::min(len, tokens - tok0);
+                    pc.ntok = std::min(cls == 1 ? lens.second : lens.first, tokens - tok0);
                     pc.last = tok0 + pc.ntok == tokens;
                     pc.head_list.assign(size_t(Hkv), 0);
                     const int64_t with_fold = pc.ntok + (pc.last ? units[g.unit].fold_tokens : 0);
                     for (int h = 0; h < Hkv; ++h)
-                        tasks.push_back({int(mp.pieces.size()), h, mfma_cost(g, with_fold)});
+                        tasks.push_back({int(mp.pieces.size()), h, mfma_cost(g, with_fold), cls});
+                    tok0 += pc.ntok;
                     mp.pieces.push_back(std::move(pc));
                 }
             }
@@ -793,8 +821,10 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             for (const T& t : tasks) {
                 int xb = -1;
                 for (int x = 0; x < kXcds; ++x)
-                    if (!heap_x[size_t(x)].empty() && (xb < 0 || heap_x[size_t(x)].top() < heap_x[size_t(xb)].top())) xb = x;
-                const int xp = t.head % kXcds;
+                    if ((t.cls < 0 || x % 2 == t.cls) && !heap_x[size_t(x)].empty() &&
+                        (xb < 0 || heap_x[size_t(x)].top() < heap_x[size_t(xb)].top()))
+                        xb = x;
+                const int xp = t.cls < 0 ? t.head % kXcds : ((t.head % kXcds) & ~1) | t.cls;
                 int x = xb;
                 if (!heap_x[size_t(xp)].empty() && heap_x[size_t(xp)].top().first <= heap_x[size_t(xb)].top().first + 0.25 * t.cost)
                     x = xp;
@@ -858,16 +888,25 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             // more than 16 MFMA tasks per list never pays for its partials
             if (have && n_tasks > 16 * int64_t(n_lists)) continue;
             if (!tried.insert(key).second) continue;
-            MfmaPlan mp = place_mfma(target);
-            const std::vector<double> base = stripe_base(mp.load);
-            double makespan = 0.0;
-            for (int w = 0; w < n_lists; ++w) makespan = std::max(makespan, mp.load[size_t(w)] / list_rate(w));
-            if (!vg.empty()) makespan = std::max(makespan, fill_level(base, valu_work));
-            const double score = makespan + mp.extra / (double(n_lists) * kWaves);
-            if (!have || score < best_score * 0.995) {
-                best = std::move(mp);
-                best_score = score;
-                have = true;
+            // parity chunking: MFMA-only launches with an odd-XCD rate, every group in 2+ chunks
+            bool parity_ok = vg.empty() && odd_rate != 1.0 && o.split_tokens <= 0 && n_lists % kXcds == 0;
+            for (int gi : mg) {
+                const Group& g = groups[size_t(gi)];
+                parity_ok = parity_ok && mfma_chunks(g, target) >= 2 &&
+                            std::max(mfma_lens(g, target, true).first, mfma_lens(g, target, true).second) <= kMfmaChunkCapTokens;
+            }
+            for (int par = 0; par < (parity_ok ? 2 : 1); ++par) {
+                MfmaPlan mp = place_mfma(target, par == 1);
+                const std::vector<double> base = stripe_base(mp.load);
+                double makespan = 0.0;
+                for (int w = 0; w < n_lists; ++w) makespan = std::max(makespan, mp.load[size_t(w)] / list_rate(w));
+                if (!vg.empty()) makespan = std::max(makespan, fill_level(base, valu_work));
+                const double score = makespan + mp.extra / (double(n_lists) * kWaves);
+                if (!have || score < best_score * 0.995) {
+                    best = std::move(mp);
+                    best_score = score;
+                    have = true;
+                }
             }
         }
         for (const Piece& pc : best.pieces) C = std::max(C, pc.ntok < unit_tokens(groups[size_t(pc.group)]) ? pc.ntok : 0);
