@@ -312,7 +312,8 @@ constexpr double kPartialWriteCostMfma = 2.0;
 // Llama-3-8B-shaped layer, whose lists hold ~11 blocks, lost 2 % (hence the
 // threshold).  MFMA-only launches take it through chunk lengths (odd-XCD
 // chunks 1.1 as long): the streaming sessions went from 1506-1510 to
-// 1482-1489 us per call.  The rate is empirical: it models the XCDs' shares of
+// 1482-1489 us per call, and with the second-slot rate as well (four chunk
+// classes) from 1490-1503 to 1480-1486 us (four rounds).  The rate is empirical: it models the XCDs' shares of
 // the memory system under full load, which is not a per-XCD speed.
 constexpr double kOddXcdRate = 1.1;
 constexpr double kOddRateMinLoad = 512.0;
@@ -764,75 +765,98 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             std::vector<double> load;
             double extra = 0.0;
         };
-        // chunk lengths of group g at `target`: (even, odd) chunk length.  With
-        // `parity` the chunks alternate between lists of even and of odd XCDs,
-        // the odd ones odd_rate times as long, so that the two halves of the GPU
-        // end together although every chunk of a group serves all its KV heads
-        // (an MFMA-only launch has no VALU work to even them out).
-        auto mfma_lens = [&](const Group& g, double target, bool parity) {
+        // Rate classes of MFMA chunks.  An MFMA-only launch has no VALU work to
+        // fill by rate, and a group's chunk serves all its KV heads at once, so
+        // the rates enter through chunk lengths: with ncls = 2 a group's chunks
+        // alternate between even- and odd-XCD lists, with ncls = 4 also between
+        // first- and second-slot lists, each as long as its class's rate.
+        auto class_rate = [&](int cls) {
+            return (cls & 1 ? odd_rate : 1.0) * (cls >> 1 ? kSecondSlotRate : 1.0);
+        };
+        // chunk lengths of group g at `target` (ncls 1: equal chunks)
+        auto chunk_lens = [&](const Group& g, double target, int ncls) {
             const int64_t tokens = unit_tokens(g);
             const int64_t nch = mfma_chunks(g, target);
-            const int64_t len = ceil16((tokens + nch - 1) / nch);
-            if (!parity) return std::make_pair(len, len);
-            const int64_t n_e = (nch + 1) / 2, n_o = nch / 2;
-            const int64_t le = ceil16(int64_t(std::ceil(double(tokens) / (double(n_e) + odd_rate * double(n_o)))));
-            const int64_t lo = ceil16((std::max<int64_t>(0, tokens - n_e * le) + n_o - 1) / n_o);
-            return std::make_pair(le, lo);
+            std::vector<int64_t> lens;
+            if (ncls == 1) {
+                const int64_t len = ceil16((tokens + nch - 1) / nch);
+                for (int64_t t0 = 0; t0 < tokens; t0 += len) lens.push_back(std::min(len, tokens - t0));
+                return lens;
+            }
+            double sum = 0.0;
+            for (int64_t c = 0; c < nch; ++c) sum += class_rate(int(c % ncls));
+            int64_t t0 = 0;
+            for (int64_t c = 0; c < nch && t0 < tokens; ++c) {
+                const int64_t len = c == nch - 1 ? tokens - t0
+                                                 : ceil16(int64_t(std::ceil(double(tokens) * class_rate(int(c % ncls)) / sum)));
+                lens.push_back(std::min(len, tokens - t0));
+                t0 += lens.back();
+            }
+            return lens;
         };
-        auto place_mfma = [&](double target, bool parity) {
+        auto place_mfma = [&](double target, int ncls) {
             MfmaPlan mp;
             mp.load.assign(size_t(n_lists), 0.0);
             struct T {
                 int piece, head;
                 double cost;
-                int cls;   // parity plans: XCD parity of the task's list; else -1
+                int cls;   // rate class of the task's list (ncls > 1); else -1
             };
             std::vector<T> tasks;
             for (int gi : mg) {
                 const Group& g = groups[size_t(gi)];
                 const int64_t tokens = unit_tokens(g);
-                const int64_t nch = mfma_chunks(g, target);
-                const auto lens = mfma_lens(g, target, parity);
-                mp.extra += double(nch - 1) * g.rows * Hkv * pu_mfma;
+                const std::vector<int64_t> lens = chunk_lens(g, target, ncls);
+                mp.extra += double(lens.size() - 1) * g.rows * Hkv * pu_mfma;
                 int64_t tok0 = 0;
-                for (int64_t c = 0; c < nch && tok0 < tokens; ++c) {
-                    const int cls = parity ? int(c % 2) : -1;
+                for (size_t c = 0; c < lens.size(); ++c) {
                     Piece pc;
                     pc.group = gi;
                     pc.tok0 = tok0;
-                    pc.ntok = std::min(cls == 1 ? lens.second : lens.first, tokens - tok0);
+                    pc.ntok = lens[c];
                     pc.last = tok0 + pc.ntok == tokens;
                     pc.head_list.assign(size_t(Hkv), 0);
                     const int64_t with_fold = pc.ntok + (pc.last ? units[g.unit].fold_tokens : 0);
                     for (int h = 0; h < Hkv; ++h)
-                        tasks.push_back({int(mp.pieces.size()), h, mfma_cost(g, with_fold), cls});
+                        tasks.push_back({int(mp.pieces.size()), h, mfma_cost(g, with_fold), ncls > 1 ? int(c % size_t(ncls)) : -1});
                     tok0 += pc.ntok;
                     mp.pieces.push_back(std::move(pc));
                 }
             }
             std::stable_sort(tasks.begin(), tasks.end(), [](const T& a, const T& b) { return a.cost > b.cost; });
-            // one min-heap of (load, list) per XCD; the least-loaded list overall is
-            // the least of the XCD minima
+            // one min-heap of (load, list) per XCD and workgroup slot; the least-loaded
+            // list overall is the least of the heap minima
             using LE = std::pair<double, int>;
             using Heap = std::priority_queue<LE, std::vector<LE>, std::greater<LE>>;
             // keys are times: a list's load divided by its rate
-            std::vector<Heap> heap_x(kXcds);
-            for (int w = 0; w < n_lists; ++w) heap_x[size_t(w % kXcds)].push({0.0, w});
+            std::vector<Heap> heap_xs(2 * kXcds);
+            auto hidx = [&](int w) { return w % kXcds + (w >= n_lists / 2 ? kXcds : 0); };
+            for (int w = 0; w < n_lists; ++w) heap_xs[size_t(hidx(w))].push({0.0, w});
+            auto allowed = [&](const T& t, int h) {
+                if (t.cls < 0) return true;
+                if ((h % kXcds) % 2 != (t.cls & 1)) return false;
+                return ncls < 4 || (h >= kXcds) == ((t.cls >> 1) != 0);
+            };
             for (const T& t : tasks) {
-                int xb = -1;
-                for (int x = 0; x < kXcds; ++x)
-                    if ((t.cls < 0 || x % 2 == t.cls) && !heap_x[size_t(x)].empty() &&
-                        (xb < 0 || heap_x[size_t(x)].top() < heap_x[size_t(xb)].top()))
-                        xb = x;
-                const int xp = t.cls < 0 ? t.head % kXcds : ((t.head % kXcds) & ~1) | t.cls;
-                int x = xb;
-                if (!heap_x[size_t(xp)].empty() && heap_x[size_t(xp)].top().first <= heap_x[size_t(xb)].top().first + 0.25 * t.cost)
-                    x = xp;
-                const int w = heap_x[size_t(x)].top().second;
-                heap_x[size_t(x)].pop();
+                int hb = -1;
+                for (int h = 0; h < 2 * kXcds; ++h)
+                    if (allowed(t, h) && !heap_xs[size_t(h)].empty() &&
+                        (hb < 0 || heap_xs[size_t(h)].top() < heap_xs[size_t(hb)].top()))
+                        hb = h;
+                // preferred: a list of the XCD of the task's KV head (of the class's parity)
+                const int xp = t.cls < 0 ? t.head % kXcds : ((t.head % kXcds) & ~1) | (t.cls & 1);
+                int hp = -1;
+                for (int h : {xp, xp + kXcds})
+                    if (allowed(t, h) && !heap_xs[size_t(h)].empty() &&
+                        (hp < 0 || heap_xs[size_t(h)].top() < heap_xs[size_t(hp)].top()))
+                        hp = h;
+                int h = hb;
+                if (hp >= 0 && heap_xs[size_t(hp)].top().first <= heap_xs[size_t(hb)].top().first + 0.25 * t.cost) h = hp;
+                const int w = heap_xs[size_t(h)].top().second;
+                heap_xs[size_t(h)].pop();
                 mp.pieces[size_t(t.piece)].head_list[size_t(t.head)] = w;
                 mp.load[size_t(w)] += t.cost;
-                heap_x[size_t(x)].push({mp.load[size_t(w)] / list_rate(w), w});
+                heap_xs[size_t(h)].push({mp.load[size_t(w)] / list_rate(w), w});
             }
             return mp;
         };
@@ -888,15 +912,23 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             // more than 16 MFMA tasks per list never pays for its partials
             if (have && n_tasks > 16 * int64_t(n_lists)) continue;
             if (!tried.insert(key).second) continue;
-            // parity chunking: MFMA-only launches with an odd-XCD rate, every group in 2+ chunks
-            bool parity_ok = vg.empty() && odd_rate != 1.0 && o.split_tokens <= 0 && n_lists % kXcds == 0;
-            for (int gi : mg) {
-                const Group& g = groups[size_t(gi)];
-                parity_ok = parity_ok && mfma_chunks(g, target) >= 2 &&
-                            std::max(mfma_lens(g, target, true).first, mfma_lens(g, target, true).second) <= kMfmaChunkCapTokens;
+            // rate-class chunking (MFMA-only launches): 2 classes with an odd-XCD
+            // rate, 4 with a second-slot rate too; every group's chunk count a
+            // multiple of the class count, no chunk over the cap
+            std::vector<int> classes{1};
+            for (int ncls : {2, 4}) {
+                bool ok = vg.empty() && odd_rate != 1.0 && (ncls == 2 || kSecondSlotRate != 1.0) && o.split_tokens <= 0 &&
+                          n_lists % (2 * kXcds) == 0;
+                for (int gi : mg) {
+                    const Group& g = groups[size_t(gi)];
+                    const int64_t nch = mfma_chunks(g, target);
+                    if (!ok || nch < ncls || nch % ncls != 0) { ok = false; break; }
+                    for (int64_t l : chunk_lens(g, target, ncls)) ok = ok && l <= kMfmaChunkCapTokens;
+                }
+                if (ok) classes.push_back(ncls);
             }
-            for (int par = 0; par < (parity_ok ? 2 : 1); ++par) {
-                MfmaPlan mp = place_mfma(target, par == 1);
+            for (int ncls : classes) {
+                MfmaPlan mp = place_mfma(target, ncls);
                 const std::vector<double> base = stripe_base(mp.load);
                 double makespan = 0.0;
                 for (int w = 0; w < n_lists; ++w) makespan = std::max(makespan, mp.load[size_t(w)] / list_rate(w));
