@@ -508,3 +508,30 @@ def test_one_launch_places_each_kv_head_on_one_xcd():
             seen += 1
             off += int(desc[off + 8])
     assert seen == wl.num_queries * wl.num_kv_heads
+
+
+def test_mfma_only_chunks_follow_list_rate_classes():
+    """A launch of MFMA tasks only (the streaming sessions) cuts each group's range into chunks
+    whose lengths follow the rate of the lists they go to: four classes by XCD parity and
+    workgroup slot, every list holding chunks of one length class, odd-XCD chunks longer than
+    even ones, second-slot chunks shorter than first-slot ones; coverage as always."""
+    wl = W.WORKLOADS[4]()
+    ex = K.kvattn_plan_export(plan_of(wl))
+    check_coverage(wl.block_tables, wl.seq_lens, wl.num_q_heads, wl.num_kv_heads, ex)
+    n = ex["num_lists"]
+    lp = np.asarray(ex["list_ptr"]).reshape(-1, 3)
+    desc = np.asarray(ex["desc"])
+    by_class = {}
+    for w in range(n):
+        off, end = lp[w][0], lp[w][1]
+        while off < end:
+            by_class.setdefault(((w % 8) % 2, w >= n // 2), []).append(int(desc[off + 3]))
+            off += int(desc[off + 8])
+    mean = {k: np.mean(v) for k, v in by_class.items()}
+    assert set(mean) == {(0, False), (0, True), (1, False), (1, True)}
+    for slot in (False, True):
+        assert mean[(1, slot)] > 1.05 * mean[(0, slot)]   # odd XCDs: longer chunks
+    for par in (0, 1):
+        assert mean[(par, True)] < 0.95 * mean[(par, False)]   # second slot: shorter chunks
+    # equal task counts per list: two chunks each
+    assert all(len(v) == n // 4 * 2 for v in by_class.values())
