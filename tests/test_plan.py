@@ -535,3 +535,30 @@ def test_mfma_only_chunks_follow_list_rate_classes():
         assert mean[(par, True)] < 0.95 * mean[(par, False)]   # second slot: shorter chunks
     # equal task counts per list: two chunks each
     assert all(len(v) == n // 4 * 2 for v in by_class.values())
+
+
+def test_valu_stripes_follow_list_rates():
+    """VALU stripes fill to the level times their lists' rate: second-slot lists (n/2 and up)
+    0.9, odd-XCD lists 1.1 when the launch's lists are long (the no-sharing batch, ~520 blocks
+    per wave) and 1.0 when they are short (the Llama-3-8B-shaped layer, ~11 blocks)."""
+    def blocks(c):
+        ex = K.kvattn_plan_export(plan_of(W.WORKLOADS[c]()))
+        n = ex["num_lists"]
+        lp = np.asarray(ex["list_ptr"]).reshape(-1, 3)
+        desc = np.asarray(ex["desc"])
+        vb = np.zeros(n)
+        for w in range(n):
+            off, end = lp[w][1], lp[w][2]
+            while off < end:
+                vb[w] += desc[off + 6]
+                off += int(desc[off + 8])
+        w = np.arange(n)
+        odd, second = (w % 8) % 2 == 1, w >= n // 2
+        return {(o, s): vb[(odd == o) & (second == s)].mean() for o in (False, True) for s in (False, True)}
+    b5 = blocks(5)
+    for o in (False, True):
+        assert 0.85 < b5[(o, True)] / b5[(o, False)] < 0.95
+    for s in (False, True):
+        assert 1.05 < b5[(True, s)] / b5[(False, s)] < 1.15
+    b2 = blocks(2)
+    assert 0.93 < b2[(True, False)] / b2[(False, False)] < 1.07   # short lists: no odd-XCD rate
