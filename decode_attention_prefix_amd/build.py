@@ -4,6 +4,11 @@ Usage: python -m decode_attention_prefix_amd.build [--sanitize]   (or build() fr
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
 selection turned off (-Xclang -target-feature -Xclang -packed-fp32-ops).
 
+build() also makes _build/trace/libkvattn.so, a diagnostic variant whose
+forward kernel writes per-task trace records (compiled with
+-DKVATTN_TASK_TRACE; task_trace.py loads it).  The library itself carries no
+trace code: without the macro the kernels compile to the same instructions.
+
 build(sanitize=True) makes a checking variant for host tests only,
 _build/san/libkvattn.so: the host planner (the part that indexes caller
 tables, trees and lengths) is compiled by g++ with AddressSanitizer and
@@ -36,6 +41,8 @@ def _run(cmd):
     subprocess.check_call(cmd)
 
 
+TRACE_DIR = os.path.join(BUILD, "trace")
+TRACE_LIB = os.path.join(TRACE_DIR, "libkvattn.so")
 SAN_DIR = os.path.join(BUILD, "san")
 SAN_LIB = os.path.join(SAN_DIR, "libkvattn.so")
 SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
@@ -61,7 +68,21 @@ def build_sanitized() -> str:
     return SAN_LIB
 
 
-def build(verbose_isa: bool = False, sanitize: bool = False) -> str:
+def build_trace() -> str:
+    """The per-task trace variant: kernels with -DKVATTN_TASK_TRACE, linked with the regular
+    planner and runtime objects (built by build())."""
+    os.makedirs(TRACE_DIR, exist_ok=True)
+    k_o = os.path.join(TRACE_DIR, "kvattn_kernels_trace.o")
+    _run([HIPCC, "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-DKVATTN_TASK_TRACE", "-I", INCLUDE,
+          *NO_PACKED_FP32, "-c", os.path.join(CSRC, "kvattn_kernels.hip"), "-o", k_o])
+    tmp = TRACE_LIB + ".tmp%d" % os.getpid()
+    _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, os.path.join(BUILD, "kvattn_plan.o"),
+          os.path.join(BUILD, "kvattn_runtime.o"), k_o, "-o", tmp])
+    os.replace(tmp, TRACE_LIB)
+    return TRACE_LIB
+
+
+def build(verbose_isa: bool = False, sanitize: bool = False, trace: bool = True) -> str:
     if sanitize:
         return build_sanitized()
     os.makedirs(BUILD, exist_ok=True)
@@ -84,6 +105,8 @@ def build(verbose_isa: bool = False, sanitize: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    if trace:
+        build_trace()
     return LIB
 
 

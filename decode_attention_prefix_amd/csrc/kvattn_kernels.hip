@@ -37,7 +37,36 @@
 #include "kvattn_internal.h"
 
 namespace kvattn {
+
+// Per-task trace (a diagnostic build only: compiled with -DKVATTN_TASK_TRACE,
+// see build.py; the library itself has none of it).  Each workgroup slot of the
+// forward launch owns kTraceEvents records of 4 words in a caller buffer set
+// with kvattn_trace_set: (type | XCC id << 8, s_memrealtime low word (100 MHz),
+// HW_ID register, extra).  Types: 0 list start (extra: list), 1 MFMA task start
+// (tokens | rows << 20), 2 MFMA task end, 3 VALU window ready (words), 4 a
+// wave's VALU stream end (at record 40 + wave; extra: its blocks), 5 VALU end.
+// Records past kTraceEvents are dropped; each launch overwrites its slots.
+#ifdef KVATTN_TASK_TRACE
+__device__ uint32_t* g_trace;
+#endif
+
 namespace {
+#ifdef KVATTN_TASK_TRACE
+constexpr int kTraceEvents = 64;
+__device__ __forceinline__ void trace_ev(int slot_wg, int idx, uint32_t type, uint32_t extra) {
+    if (!g_trace || idx >= kTraceEvents) return;
+    uint32_t* e = g_trace + (size_t(slot_wg) * kTraceEvents + idx) * 4;
+    const uint64_t t = __builtin_amdgcn_s_memrealtime();
+    const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);     // HW_ID
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);   // XCC_ID
+    *reinterpret_cast<uint4*>(e) = make_uint4(type | (xcc << 8), uint32_t(t), hw, extra);
+}
+#define KV_TRACE(...) trace_ev(__VA_ARGS__)
+#define KV_TRACE_ON 1
+#else
+#define KV_TRACE(...) ((void)0)
+#define KV_TRACE_ON 0
+#endif
 
 constexpr float kRescaleLog2 = 8.0f;
 // VALU load ring depth in 16-token blocks.  Two (one block in flight while
@@ -767,6 +796,10 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
         }
     }
     flush();
+    if constexpr (KV_TRACE_ON && !SPLIT) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
+        if (lane == 0) KV_TRACE(blockIdx.x, 40 + wave, 4, uint32_t(total));
+    }
 
     // Fused merge: the stream's partial stores are complete (sc1: performed at
     // agent scope) before its arrivals; the task completing a (query, KV head)
@@ -1199,6 +1232,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     __shared__ int s_next[2];
     const bool claims = p.n_lists > int(gridDim.x);
     int w = blockIdx.x;
+    [[maybe_unused]] int nev = 0;   // trace records of this workgroup slot
+    if (threadIdx.x == 0) KV_TRACE(blockIdx.x, nev++, 0, uint32_t(w));
     for (int round = 0; w < p.n_lists; ++round) {
         int ticket = 0;
         if (claims && threadIdx.x == 0) ticket = atomicAdd(p.claim + opaque_zero(), 1);
@@ -1218,8 +1253,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
                 const int noff = off + words;
                 if (noff < v0) fetch_desc(p.desc + noff, next_words, s_desc[buf ^ 1]);
                 const TaskView it = view_of(d);
+                if (threadIdx.x == 0) KV_TRACE(blockIdx.x, nev++, 1, uint32_t(it.n_tokens) | (uint32_t(it.n_rows) << 20));
                 mfma_task<D, TPW>(p, dm, it, it.head, q, kc, vc, out, s_kv);
                 wait_all_and_sync();   // the prefetched descriptor landed; this task's LDS is free
+                if (threadIdx.x == 0) KV_TRACE(blockIdx.x, nev++, 2, 0u);
                 if (p.arrive) mfma_arrivals<D>(p, dm, it, out, s_last, s_last + kMaxItemQueries);
                 if (noff >= v0) break;
                 off = noff;
@@ -1232,12 +1269,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             int32_t* win = reinterpret_cast<int32_t*>(s_kv);
             fetch_desc(p.desc + v0, e0 - v0, win);
             wait_all_and_sync();
+            if (threadIdx.x == 0) KV_TRACE(blockIdx.x, nev++, 3, uint32_t(e0 - v0));
             uint16_t* qs = s_kv + 2 * WIN + wave * 4 * R * D;
             float* cbuf = reinterpret_cast<float*>(&s_desc[0][0]);   // the descriptor buffers are idle here
             valu_stream<D, R, false>(p, dm, win, e0 - v0, qs, cbuf, q, kc, vc, out);
             wait_all_and_sync();
             valu_stream<D, R, true>(p, dm, win, e0 - v0, qs, cbuf, q, kc, vc, out);
             wait_all_and_sync();   // the window is free for the next list
+            if (threadIdx.x == 0) KV_TRACE(blockIdx.x, nev++, 5, 0u);
         }
         if (!claims) break;
         if (threadIdx.x == 0) {
@@ -1386,6 +1425,13 @@ int scratch_device_pointer(void** ptr) {
     *ptr = addr[dev];
     return int(hipSuccess);
 }
+
+#ifdef KVATTN_TASK_TRACE
+// Trace builds only: the device buffer that receives the records (NULL: off).
+extern "C" int kvattn_trace_set(void* p) {
+    return int(hipMemcpyToSymbol(HIP_SYMBOL(g_trace), &p, sizeof(p)));
+}
+#endif
 
 int launch_read_probe(const void* a, size_t a_bytes, const void* b, size_t b_bytes, uint32_t* sink, int grid,
                       int depth, int threads, void* stream) {

@@ -54,3 +54,18 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
                        env=env)
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "libkvattn.so is not built" in r.stderr
+
+
+def test_trace_hook_only_in_the_trace_build():
+    """The per-task trace hook exists in the diagnostic build (_build/trace) and not in the library."""
+    from decode_attention_prefix_amd import build as B
+
+    def exported(path):
+        out = subprocess.check_output(["nm", "-D", "--defined-only", path]).decode()
+        return set(line.split()[-1] for line in out.splitlines() if line.strip())
+
+    if not os.path.exists(B.LIB):
+        pytest.skip("library not built")
+    assert "kvattn_trace_set" not in exported(B.LIB)
+    if os.path.exists(B.TRACE_LIB):
+        assert "kvattn_trace_set" in exported(B.TRACE_LIB)
