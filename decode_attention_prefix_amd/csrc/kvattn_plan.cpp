@@ -325,6 +325,16 @@ constexpr double kOddRateMinLoad = 512.0;
 // 233.4 us on the two-level tree; the no-sharing batch and the streaming
 // sessions within noise (0.85: no better).
 constexpr double kSecondSlotRate = 0.9;
+// The same for the chunk classes of MFMA-only launches, where the second slot
+// lags more: its first chunks end ~5 % after the first slot's at 0.9.  0.85
+// measured 1461.7-1470.7 against 1483.4-1488.3 us per call on the streaming
+// sessions (four rounds; 0.8: 1496-1502 us).
+constexpr double kMfmaSecondSlotRate = 0.85;
+// And the odd-XCD rate of those chunk classes (used only where the launch's
+// odd-XCD rate applies): 1.15 measured 1467.9-1471.9 against 1475.7-1477.8 us
+// per call (four rounds, 0.85 second slot) and 1476-1483 against 1483-1488 us
+// with a 0.9 second slot.
+constexpr double kMfmaOddXcdRate = 1.15;
 // A list that runs MFMA tasks starts its VALU stream late and from cold: the
 // descriptor window, the q rows and the first blocks each take a round trip
 // under full load (per-task traces on MI355X: a 16-token VALU remainder after
@@ -771,7 +781,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         // alternate between even- and odd-XCD lists, with ncls = 4 also between
         // first- and second-slot lists, each as long as its class's rate.
         auto class_rate = [&](int cls) {
-            return (cls & 1 ? odd_rate : 1.0) * (cls >> 1 ? kSecondSlotRate : 1.0);
+            return (cls & 1 ? kMfmaOddXcdRate : 1.0) * (cls >> 1 ? kMfmaSecondSlotRate : 1.0);
         };
         // chunk lengths of group g at `target` (ncls 1: equal chunks)
         auto chunk_lens = [&](const Group& g, double target, int ncls) {
@@ -917,7 +927,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             // multiple of the class count, no chunk over the cap
             std::vector<int> classes{1};
             for (int ncls : {2, 4}) {
-                bool ok = vg.empty() && odd_rate != 1.0 && (ncls == 2 || kSecondSlotRate != 1.0) && o.split_tokens <= 0 &&
+                bool ok = vg.empty() && odd_rate != 1.0 && (ncls == 2 || kMfmaSecondSlotRate != 1.0) && o.split_tokens <= 0 &&
                           n_lists % (2 * kXcds) == 0;
                 for (int gi : mg) {
                     const Group& g = groups[size_t(gi)];
