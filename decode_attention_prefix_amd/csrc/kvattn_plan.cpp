@@ -310,11 +310,10 @@ constexpr double kPartialWriteCostMfma = 2.0;
 // 1506.1 to 1462.8-1468.9 us and the two-level tree from 232.6-233.2 to
 // 228.8-229.5 us per call on two boxes (1.05 and 1.2 in between), while the
 // Llama-3-8B-shaped layer, whose lists hold ~11 blocks, lost 2 % (hence the
-// threshold).  MFMA-only launches take it through chunk lengths (odd-XCD
-// chunks 1.1 as long): the streaming sessions went from 1506-1510 to
-// 1482-1489 us per call, and with the second-slot rate as well (four chunk
-// classes) from 1490-1503 to 1480-1486 us (four rounds).  The rate is empirical: it models the XCDs' shares of
-// the memory system under full load, which is not a per-XCD speed.
+// threshold).  MFMA-only launches take their rates through chunk lengths
+// (kMfmaOddXcdRate, kMfmaSecondSlotRate below).  The rate is empirical: it
+// models the XCDs' shares of the memory system under full load, which is not
+// a per-XCD speed.
 constexpr double kOddXcdRate = 1.1;
 constexpr double kOddRateMinLoad = 512.0;
 // Relative streaming rate of the second workgroup of each CU (lists n_lists/2
@@ -325,10 +324,12 @@ constexpr double kOddRateMinLoad = 512.0;
 // 233.4 us on the two-level tree; the no-sharing batch and the streaming
 // sessions within noise (0.85: no better).
 constexpr double kSecondSlotRate = 0.9;
-// The same for the chunk classes of MFMA-only launches, where the second slot
-// lags more: its first chunks end ~5 % after the first slot's at 0.9.  0.85
-// measured 1461.7-1470.7 against 1483.4-1488.3 us per call on the streaming
-// sessions (four rounds; 0.8: 1496-1502 us).
+// The same for the chunk classes of MFMA-only launches (four classes: XCD
+// parity x workgroup slot, each chunk as long as its class's rate), where the
+// second slot lags more: its chunks end ~5 % after the first slot's at 0.9.
+// On the streaming sessions: equal chunks 1506-1510 us per call, parity
+// classes at 1.1 1490-1503 us, four classes with 0.9 1476-1488 us, with 0.85
+// 1461.7-1470.7 us (four rounds; 0.8: 1496-1502 us).
 constexpr double kMfmaSecondSlotRate = 0.85;
 // And the odd-XCD rate of those chunk classes (used only where the launch's
 // odd-XCD rate applies): 1.15 measured 1467.9-1471.9 against 1475.7-1477.8 us
