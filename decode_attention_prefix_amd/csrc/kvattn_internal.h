@@ -157,6 +157,9 @@ struct DevPlan {
     // 1 when both partial arrays fit 32-bit byte offsets (always when fused): the
     // kernels then store partials written through the L2 (sc1); 0: plain stores
     int32_t part_wt;
+    // 1 when some task of the plan runs on the VALU_SPLIT tile; 0: the forward
+    // skips the second pass over each list's VALU descriptors
+    int32_t has_split;
 };
 
 struct Dims {

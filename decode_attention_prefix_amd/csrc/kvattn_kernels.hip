@@ -467,11 +467,6 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
         }
     };
     l_enter();
-    int total = 0;   // blocks of this wave's stream
-    for (int off = l_off; off < n_words; off = skip(off + hdr(off, kDescWords))) {
-        const int nb = hdr(off, kDescBlocks);
-        total += range_hi(nb) - range_lo(nb);
-    }
 
     // A block's K and V slices of KV head l_g are read through buffer resources
     // whose size covers the block's valid tokens only: the hardware returns
@@ -513,8 +508,10 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
         }
     };
 
-    // ---- process side
-    int p_off = skip(0);
+    // ---- process side: the stream ends when the last task's last block is
+    // processed (p_off past the window); no load waits on a count of blocks
+    int p_off = l_off;
+    [[maybe_unused]] int n_done = 0;   // blocks processed (trace records only)
     int p_blk = -1, p_slot = 0, p_hi = 0;   // p_blk < 0: the next block starts a task
     int limit[R];
     float m[R], l[R], acc[R][NE];
@@ -759,6 +756,7 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
     auto proc_block = [&](const uint4 (&kb)[2][NPC], const uint4 (&vb)[2][NPC]) {
         if (p_blk < 0) begin_task();
         process(p_blk, kb, vb);
+        if constexpr (KV_TRACE_ON) ++n_done;
         if (++p_blk == p_hi) {
             end_task();
             if constexpr (SPLIT) {
@@ -784,10 +782,10 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
     uint4 kr[NR][2][NPC], vr[NR][2][NPC];
 #pragma unroll
     for (int u = 0; u < NR; ++u) load_block(kr[u], vr[u]);
-    for (int j = 0; j < total; j += NR) {
+    while (p_off < n_words) {
 #pragma unroll
         for (int u = 0; u < NR; ++u) {
-            if (j + u < total) proc_block(kr[u], vr[u]);
+            if (p_off < n_words) proc_block(kr[u], vr[u]);
             __builtin_amdgcn_sched_barrier(0);
             load_block(kr[u], vr[u]);
             __builtin_amdgcn_sched_barrier(0);
@@ -798,7 +796,7 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
     flush();
     if constexpr (KV_TRACE_ON && !SPLIT) {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
-        if (lane == 0) KV_TRACE(blockIdx.x, 40 + wave, 4, uint32_t(total));
+        if (lane == 0) KV_TRACE(blockIdx.x, 40 + wave, 4, uint32_t(n_done));
     }
 
     // Fused merge: the stream's partial stores are complete (sc1: performed at
@@ -1273,9 +1271,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
             uint16_t* qs = s_kv + 2 * WIN + wave * 4 * R * D;
             float* cbuf = reinterpret_cast<float*>(&s_desc[0][0]);   // the descriptor buffers are idle here
             valu_stream<D, R, false>(p, dm, win, e0 - v0, qs, cbuf, q, kc, vc, out);
-            wait_all_and_sync();
-            valu_stream<D, R, true>(p, dm, win, e0 - v0, qs, cbuf, q, kc, vc, out);
-            wait_all_and_sync();   // the window is free for the next list
+            wait_all_and_sync();   // the window is free for the next list ...
+            if (p.has_split) {     // ... after the VALU_SPLIT tasks, if the plan has any
+                valu_stream<D, R, true>(p, dm, win, e0 - v0, qs, cbuf, q, kc, vc, out);
+                wait_all_and_sync();
+            }
             if (threadIdx.x == 0) KV_TRACE(blockIdx.x, nev++, 5, 0u);
         }
         if (!claims) break;

@@ -426,6 +426,8 @@ bool serialize_lists(kvattn_plan_s& P) {
 // Header and arrays of the device blob (the part kvattn_plan_upload copies);
 // the partial triples follow it in the workspace.
 void serialize_blob(kvattn_plan_s& P) {
+    P.has_split = false;
+    for (const Item& it : P.items) P.has_split |= it.kind == KVATTN_VARIANT_VALU_SPLIT;
     BlobHeader& h = P.header;
     std::memset(&h, 0, sizeof(h));
     h.magic = kBlobMagic;

@@ -18,6 +18,7 @@ struct kvattn_plan_s {
     std::vector<int32_t> merge_rec;                            // device: (b, slot base, partials, new-token slot) per merged query
     std::vector<int32_t> rec_of_query;                         // [B] index of the query's merge record, -1 if none
     bool fused_merge = false;                                  // the forward launch merges (no merge launch)
+    bool has_split = false;                                    // some task runs on the VALU_SPLIT tile
     int32_t n_slots = 0;
     std::vector<kvattn::Task> tasks;
     std::vector<int32_t> list_ptr;          // [launch][n_lists + 1] task ranges of the static lists

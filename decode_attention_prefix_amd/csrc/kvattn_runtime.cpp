@@ -41,6 +41,7 @@ DevPlan resolve(const kvattn_plan_s& P, int launch, void* ws) {
     const char* plain = std::getenv("KVATTN_PLAIN_PARTIALS");
     const bool force_plain = plain && plain[0] == '1' && !P.fused_merge;
     d.part_wt = acc_bytes <= 0xFFFFFFF0u && !force_plain ? 1 : 0;
+    d.has_split = P.has_split ? 1 : 0;
     return d;
 }
 
