@@ -1084,31 +1084,102 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
         }
     };
 
-    // ---- NS-stage pipeline: tiles i+1 .. i+NS-1 stream in while tile i is computed ----
-// Unrolled by NS so that every stage offset is a constant: LDS reads then
-    // take it in their offset field instead of a vector add per address.
-    static_assert(NS == 4, "the wait counts below assume at most two younger tiles");
+    if constexpr (TPW == 1) {
+        // ---- Register-staged pipeline (16 rows per wave): tile i + RT is loaded into
+        // VGPRs while tile i is computed, and each tile is written to LDS by the
+        // workgroup just before its barrier.  Measured streaming these 32-token
+        // tiles alone (2 workgroups per CU, 8 GiB): three 16 KB tiles in registers
+        // 6.30-6.40 TB/s, where buffer->LDS copies with three tiles in flight reach
+        // 5.79-5.84 TB/s.  The tiles take 16 LPT VGPRs each, which fits next to one
+        // sixteen-row tile per wave but not two.  The LDS layout is the DMA path's:
+        // thread c of a copy holds chunk c of the stage, read from the permuted
+        // global offset.
+        constexpr int RT = 3;                   // tiles in flight (and LDS stages used)
+        static_assert(RT <= NS, "register-staged tiles use the MFMA stage buffer");
+        static_assert(TCH % NT == 0, "every thread holds LPT chunks of each tile");
+        struct RegTile {
+            u32x4 k[LPT], v[LPT];
+        };
+        // loads of tile i; past the task's last tile the resources are empty, so the
+        // loads read nothing from memory and return zeros (the loop stays branch-free)
+        auto load_tile = [&](int i, RegTile& t) {
+            const bool live = i < ntiles;      // wave-uniform
+            const int kb = live ? 2 * i : 0;
+            const int blk0 = __builtin_amdgcn_readfirstlane(s_blk[kb]);
+            const int blk1 = __builtin_amdgcn_readfirstlane(kb + 1 < nblk ? s_blk[kb + 1] : blk0);
+            const int rem = live ? n_tok - kb * kBlock : 0;
+            const uint32_t bytes0 = uint32_t(min(rem, kBlock)) * D * 2;
+            const uint32_t bytes1 = uint32_t(max(0, min(rem - kBlock, kBlock))) * D * 2;
 #pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
-        if (i < ntiles) issue_tile(i, i);
-    for (int i0 = 0; i0 < ntiles; i0 += NS) {
+            for (int u = 0; u < LPT; ++u) {
+                const bool second = (u * NT + wave * 64) / CPR >= kBlock;   // wave-uniform
+                const size_t ob = size_t(second ? blk1 : blk0) * blk_elems;
+                const int nb = int(second ? bytes1 : bytes0);
+                const __amdgpu_buffer_rsrc_t rk =
+                    __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kh + ob), 0, nb, kBufferWord3);
+                const __amdgpu_buffer_rsrc_t rv =
+                    __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vh + ob), 0, nb, kBufferWord3);
+                t.k[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_k, 0, 0);
+                t.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v, 0, 0);
+            }
+        };
+        auto write_tile = [&](const RegTile& t, int stage) {
+            uint16_t* sb = s_kv + stage * STAGE;
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-            const int i = i0 + st;
-            if (i < ntiles) {
-                // this thread's DMA for tile i is complete once at most the loads of the
-                // (up to NS - 2) younger tiles remain outstanding
-                const int younger = min(ntiles - 1 - i, NS - 2);
-                if (younger >= 2) {
-                    __builtin_amdgcn_s_waitcnt(waitcnt_vm<4 * LPT>());
-                } else if (younger == 1) {
-                    __builtin_amdgcn_s_waitcnt(waitcnt_vm<2 * LPT>());
-                } else {
-                    __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
+            for (int u = 0; u < LPT; ++u) {
+                *reinterpret_cast<u32x4*>(sb + (u * NT + tid) * 8) = t.k[u];
+                *reinterpret_cast<u32x4*>(sb + TT * D + (u * NT + tid) * 8) = t.v[u];
+            }
+        };
+        // One step: tile i (held in t) is written to LDS stage st, and t takes the
+        // loads of tile i + RT.  Stage st last held tile i - RT, which every wave
+        // finished before it passed the previous step's barrier; after this step's
+        // barrier every wave's part of tile i is in LDS.
+        auto step = [&](RegTile& t, int i, int st) {
+            write_tile(t, st);
+            load_tile(i + RT, t);
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            if (i < ntiles) compute(i, s_kv + st * STAGE);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        RegTile t0, t1, t2;
+        load_tile(0, t0);
+        load_tile(1, t1);
+        load_tile(2, t2);
+        for (int i0 = 0; i0 < ntiles; i0 += RT) {
+            step(t0, i0, 0);
+            step(t1, i0 + 1, 1);
+            step(t2, i0 + 2, 2);
+        }
+    } else {
+        // ---- NS-stage pipeline: tiles i+1 .. i+NS-1 stream in while tile i is computed ----
+    // Unrolled by NS so that every stage offset is a constant: LDS reads then
+        // take it in their offset field instead of a vector add per address.
+        static_assert(NS == 4, "the wait counts below assume at most two younger tiles");
+    #pragma unroll
+        for (int i = 0; i < NS - 1; ++i)
+            if (i < ntiles) issue_tile(i, i);
+        for (int i0 = 0; i0 < ntiles; i0 += NS) {
+    #pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                const int i = i0 + st;
+                if (i < ntiles) {
+                    // this thread's DMA for tile i is complete once at most the loads of the
+                    // (up to NS - 2) younger tiles remain outstanding
+                    const int younger = min(ntiles - 1 - i, NS - 2);
+                    if (younger >= 2) {
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm<4 * LPT>());
+                    } else if (younger == 1) {
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm<2 * LPT>());
+                    } else {
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm<0>());
+                    }
+                    __builtin_amdgcn_s_barrier();   // every wave's DMA for tile i landed; tile i-1 is consumed
+                    if (i + NS - 1 < ntiles) issue_tile(i + NS - 1, (st + NS - 1) % NS);
+                    compute(i, s_kv + st * STAGE);
                 }
-                __builtin_amdgcn_s_barrier();   // every wave's DMA for tile i landed; tile i-1 is consumed
-                if (i + NS - 1 < ntiles) issue_tile(i + NS - 1, (st + NS - 1) % NS);
-                compute(i, s_kv + st * STAGE);
             }
         }
     }
