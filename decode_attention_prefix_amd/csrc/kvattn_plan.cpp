@@ -299,21 +299,23 @@ constexpr double kValuTaskCost = 24.0;
 // MFMA task writes its partials as one burst of up to 128 rows, which costs
 // far less per byte.
 constexpr double kPartialWriteCostMfma = 2.0;
-// Relative streaming rate of lists on odd XCDs (list w runs on XCD w mod 8),
-// for launches whose lists hold at least kOddRateMinLoad units (32 blocks per
-// wave); shorter lists keep 1.0, since a block is already ~10 % of them.
-// Traces show odd XCDs streaming 8-12 % slower than even ones while every
-// workgroup streams, yet on this GPU every way of giving them less work
-// measured slower with back-to-back calls (a 0.9 fill: the two-level tree
-// 239.6 against 232.9 us, the no-sharing batch 1549 against 1511 us), and
-// giving them more measured faster: 1.1 took the no-sharing batch from
-// 1506.1 to 1462.8-1468.9 us and the two-level tree from 232.6-233.2 to
-// 228.8-229.5 us per call on two boxes (1.05 and 1.2 in between), while the
-// Llama-3-8B-shaped layer, whose lists hold ~11 blocks, lost 2 % (hence the
-// threshold).  MFMA-only launches take their rates through chunk lengths
-// (kMfmaOddXcdRate, kMfmaSecondSlotRate below).  The rate is empirical: it
-// models the XCDs' shares of the memory system under full load, which is not
-// a per-XCD speed.
+// Relative streaming rate of the lists with an odd index, for launches whose
+// lists hold at least kOddRateMinLoad units (32 blocks per wave); shorter
+// lists keep 1.0, since a block is already ~10 % of them.  Lists w and w + 8
+// share an XCD (and its L2); which XCD is up to the dispatcher, and per-task
+// traces (the XCC_ID register, eager and graph launches, two GPUs) put
+// workgroup w of the forward launch on XCC (w + 7) mod 8, so the odd lists run
+// on the even-numbered XCCs.  The same traces show the odd-numbered XCCs
+// streaming 8-12 % slower while every workgroup streams.  Measured with
+// back-to-back calls: 1.1 took the no-sharing batch from 1506.1 to
+// 1462.8-1468.9 us and the two-level tree from 232.6-233.2 to 228.8-229.5 us
+// per call on two boxes (1.05 and 1.2 in between; 0.9, i.e. more work on the
+// slower XCCs, cost 2.8 % and 2.5 %), while the Llama-3-8B-shaped layer,
+// whose lists hold ~11 blocks, lost 2 % (hence the threshold).  MFMA-only
+// launches take their rates through chunk lengths (kMfmaOddXcdRate,
+// kMfmaSecondSlotRate below).  The rate is tied to that placement: on a GPU
+// that placed workgroups otherwise the balance would be worse, the results
+// the same.
 constexpr double kOddXcdRate = 1.1;
 constexpr double kOddRateMinLoad = 512.0;
 // Relative streaming rate of the second workgroup of each CU (lists n_lists/2
@@ -331,8 +333,8 @@ constexpr double kSecondSlotRate = 0.9;
 // classes at 1.1 1490-1503 us, four classes with 0.9 1476-1488 us, with 0.85
 // 1461.7-1470.7 us (four rounds; 0.8: 1496-1502 us).
 constexpr double kMfmaSecondSlotRate = 0.85;
-// And the odd-XCD rate of those chunk classes (used only where the launch's
-// odd-XCD rate applies): 1.15 measured 1467.9-1471.9 against 1475.7-1477.8 us
+// And the odd-list rate of those chunk classes (used only where the launch's
+// odd-list rate applies): 1.15 measured 1467.9-1471.9 against 1475.7-1477.8 us
 // per call (four rounds, 0.85 second slot) and 1476-1483 against 1483-1488 us
 // with a 0.9 second slot.
 constexpr double kMfmaOddXcdRate = 1.15;
@@ -706,9 +708,9 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     //  * MFMA items (packed groups) run one task per KV head on a whole
     //    workgroup.  Their chunk length is chosen from a few candidates; for
     //    each, the tasks are placed longest first on the least-loaded list (an
-    //    MFMA task of KV head g prefers a list of XCD g mod 8 -- workgroup w runs
-    //    on XCD w mod 8 -- so the row groups and chunks reading one head's shared
-    //    range meet in one L2).
+    //    MFMA task of KV head g prefers a list w = g mod 8 (mod 8) -- workgroups
+    //    w and w + 8 run on one XCD -- so the row groups and chunks reading one
+    //    head's shared range meet in one L2).
     //  * VALU items run one task per four KV heads, one wave per head, as part
     //    of continuous per-wave streams.  The lists are taken in groups of
     //    ceil(Hkv / 4) lists on one XCD ("stripes", all KV heads of an item);
@@ -722,15 +724,16 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
     const int n_lists = num_cus * 2;
     const int quads = (Hkv + kWaves - 1) / kWaves;
     const int n_stripes = std::max(1, n_lists / quads);
-    // A stripe's lists sit on one XCD (list w runs on XCD w mod 8): members
-    // w, w + 8, ... when the lists split evenly, so they stream at one rate.
+    // A stripe's lists sit on one XCD (workgroups w and w + 8 share one):
+    // members w, w + 8, ... when the lists split evenly, so they stream at one rate.
     const bool xcd_stripes = n_lists % (kXcds * quads) == 0;
     auto stripe_list = [&](int s, int q) {
         return xcd_stripes ? (s / kXcds) * kXcds * quads + s % kXcds + kXcds * q : s * quads + q;
     };
     // relative streaming rate of list w (XCD parity and workgroup slot); the
-    // odd-XCD rate is set per launch
+    // odd-list rate is set per launch
     double odd_rate = 1.0;
+    // odd lists run on the faster (even-numbered) XCCs; second-slot lists share CUs with the first slot's
     auto list_rate = [&](int w) { return ((w % kXcds) % 2 ? odd_rate : 1.0) * (w >= n_lists / 2 ? kSecondSlotRate : 1.0); };
     auto stripe_rate = [&](int s) { return list_rate(stripe_list(s, 0)); };
     const double pu_mfma = (kPartialWriteCostMfma + 1.0) * double(partial_row_bytes) / double(2 * D * 2);
@@ -781,7 +784,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
         // Rate classes of MFMA chunks.  An MFMA-only launch has no VALU work to
         // fill by rate, and a group's chunk serves all its KV heads at once, so
         // the rates enter through chunk lengths: with ncls = 2 a group's chunks
-        // alternate between even- and odd-XCD lists, with ncls = 4 also between
+        // alternate between even and odd lists (XCD parity), with ncls = 4 also between
         // first- and second-slot lists, each as long as its class's rate.
         auto class_rate = [&](int cls) {
             return (cls & 1 ? kMfmaOddXcdRate : 1.0) * (cls >> 1 ? kMfmaSecondSlotRate : 1.0);
@@ -925,7 +928,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             // more than 16 MFMA tasks per list never pays for its partials
             if (have && n_tasks > 16 * int64_t(n_lists)) continue;
             if (!tried.insert(key).second) continue;
-            // rate-class chunking (MFMA-only launches): 2 classes with an odd-XCD
+            // rate-class chunking (MFMA-only launches): 2 classes with an odd-list
             // rate, 4 with a second-slot rate too; every group's chunk count a
             // multiple of the class count, no chunk over the cap
             std::vector<int> classes{1};
@@ -963,7 +966,7 @@ kvattn_status build_plan(const kvattn_shape& s, const int32_t* block_tables, con
             // Each range whole (up to the item cap); its tasks -- one per KV head on the
             // VALU_SPLIT tile, one per four heads on the VALU tile -- placed longest
             // first on the least-loaded list, in block-times of one wave.  A task of KV
-            // head (or head quad) k prefers a list of XCD k mod 8, so the queries that
+            // head (or head quad) k prefers a list w = k (mod 8), one XCD, so the queries that
             // share a range read its blocks through one L2: they run at the same time,
             // and the L2 fetches each block from HBM once for all of them.
             struct T {
