@@ -106,6 +106,23 @@ __device__ __forceinline__ float octet_sum(float x) {
     return x;
 }
 
+// Cross-lane exchanges without LDS.  lane_x8: the value of lane l ^ 8 (DPP
+// row_ror:8 within each 16-lane row).  swap16 / swap32 (gfx950
+// v_permlane16_swap / v_permlane32_swap) pair lane l with lane l ^ 16 (l ^ 32)
+// and return, on the lane of the pair whose bit is clear, {own x, partner's
+// x}, and on the lane whose bit is set, {partner's y, own y}.  So .x + .y sums
+// the pair's x on the lower lane and the pair's y on the upper lane (a
+// reduce-scatter step), and with x = y both lanes get {own, partner}.
+__device__ __forceinline__ float lane_x8(float x) { return dpp<0x128>(x); }
+__device__ __forceinline__ float2 swap16(float x, float y) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float2 swap32(float x, float y) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // v_max3_f32 without the NaN-quieting canonicalisations fmaxf adds for values
@@ -612,40 +629,44 @@ __device__ __forceinline__ void valu_stream(const DevPlan& p, const Dims& dm, co
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             float M = m[r];
-            M = fmaxf(M, __shfl_xor(M, 8));
-            M = fmaxf(M, __shfl_xor(M, 16));
-            M = fmaxf(M, __shfl_xor(M, 32));
+            M = fmaxf(M, lane_x8(M));
+            float2 s = swap16(M, M);
+            M = fmaxf(s.x, s.y);
+            s = swap32(M, M);
+            M = fmaxf(s.x, s.y);
             const float f = fast_exp2(m[r] - M);
             float lr = l[r] * f;
-            lr += __shfl_xor(lr, 8);
-            lr += __shfl_xor(lr, 16);
-            lr += __shfl_xor(lr, 32);
+            lr += lane_x8(lr);
+            s = swap16(lr, lr);
+            lr = s.x + s.y;
+            s = swap32(lr, lr);
+            lr = s.x + s.y;
             ltot[r] = lr;
             mrow[r] = M;
 #pragma unroll
             for (int e = 0; e < NE; ++e) acc[r][e] *= f;
         }
-        // reduce-scatter over t: after three halving exchanges each lane owns NE/8 elements
-        const bool u32 = (lane & 32) != 0, u16 = (lane & 16) != 0, u8 = (lane & 8) != 0;
+        // reduce-scatter over t: after three halving exchanges each lane owns NE/8
+        // elements (lanes with bit 32 set keep the upper half of acc, and so on);
+        // the first two exchanges are lane swaps, the last a DPP read
+        const bool u8 = (lane & 8) != 0;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
 #pragma unroll
             for (int i = 0; i < NE / 2; ++i) {
-                const float send = u32 ? acc[r][i] : acc[r][NE / 2 + i];
-                const float keep = u32 ? acc[r][NE / 2 + i] : acc[r][i];
-                acc[r][i] = keep + __shfl_xor(send, 32);
+                const float2 s = swap32(acc[r][i], acc[r][NE / 2 + i]);
+                acc[r][i] = s.x + s.y;
             }
 #pragma unroll
             for (int i = 0; i < NE / 4; ++i) {
-                const float send = u16 ? acc[r][i] : acc[r][NE / 4 + i];
-                const float keep = u16 ? acc[r][NE / 4 + i] : acc[r][i];
-                acc[r][i] = keep + __shfl_xor(send, 16);
+                const float2 s = swap16(acc[r][i], acc[r][NE / 4 + i]);
+                acc[r][i] = s.x + s.y;
             }
 #pragma unroll
             for (int i = 0; i < NE / 8; ++i) {
                 const float send = u8 ? acc[r][i] : acc[r][NE / 8 + i];
                 const float keep = u8 ? acc[r][NE / 8 + i] : acc[r][i];
-                acc[r][i] = keep + __shfl_xor(send, 8);
+                acc[r][i] = keep + lane_x8(send);
             }
         }
     };
@@ -1037,8 +1058,10 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
 #pragma unroll
             for (int rt = 0; rt < TPW; ++rt) {
                 float rm = tmax[rt];
-                rm = fmaxf(rm, __shfl_xor(rm, 16));
-                rm = fmaxf(rm, __shfl_xor(rm, 32));
+                float2 s = swap16(rm, rm);
+                rm = fmaxf(s.x, s.y);
+                s = swap32(rm, rm);
+                rm = fmaxf(s.x, s.y);
                 const float mn = fmaxf(mref[rt], rm);
                 const float alpha = fast_exp2(mref[rt] - mn);
                 lsum[rt] *= alpha;
@@ -1189,8 +1212,10 @@ __device__ __forceinline__ void mfma_task(const DevPlan& p, const Dims& dm, cons
     for (int rt = 0; rt < TPW; ++rt) {
         if (!active) continue;
         float lt = lsum[rt];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
+        float2 s = swap16(lt, lt);
+        lt = s.x + s.y;
+        s = swap32(lt, lt);
+        lt = s.x + s.y;
         const int r = row0 + rt * 16 + lr;
         if (r >= it.n_rows) continue;
         const Entry e = entry_of(it, r / G);
