@@ -289,10 +289,13 @@ constexpr int64_t kMfmaChunkCapTokens = int64_t(kMfmaMaxItemBlocks) * kBlock - k
 // blocks and tasks per list) put it near 1.5 block-times, and 24 units beat 8
 // on the Llama-3-8B-shaped layer (49.1 against 49.8 us per call, two rounds;
 // the other workloads within noise), while a larger MFMA task cost (100) was
-// slower on both shared workloads.
+// slower on both shared workloads.  With the task end's cross-lane reductions
+// done by lane swaps instead of LDS permutes, 20 measured 43.4-44.0 against
+// 44.0-44.5 us per call there (four rounds, two boxes; 12, 16 and 28 no better,
+// the two-level tree and the no-sharing batch within noise).
 constexpr double kMfmaTokenCost = 0.2;
 constexpr double kMfmaTaskCost = 40.0;
-constexpr double kValuTaskCost = 24.0;
+constexpr double kValuTaskCost = 20.0;
 // Partial triples are written into a saturated HBM read stream; on MI355X a
 // VALU wave's small partial stores cost about twenty read bytes per byte
 // (measured), which is why the VALU work is cut at most once per stripe.  An
